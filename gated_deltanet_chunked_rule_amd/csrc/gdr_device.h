@@ -1,0 +1,158 @@
+// gdr_device.h -- device helpers for the gfx950 chunked gated-delta-rule kernels.
+//
+// Workgroups are 256 threads = 4 wave64.  Chunk GEMMs run on the CDNA4 matrix
+// cores: bf16 operands use V_MFMA_F32_16X16X32_BF16, fp32 operands use
+// V_MFMA_F32_16X16X4_F32; both accumulate in fp32.  Operand tiles live in LDS.
+//
+// MFMA lane layouts (wave64, checked on the device):
+//   A fragment (16 x KSTEP): lane l holds row l%16, k = 8*(l/16)+j (bf16, j<8)
+//                                                  k = l/16         (fp32)
+//   B fragment (KSTEP x 16): lane l holds col l%16, same k as A
+//   C/D 16 x 16 fp32:        lane l holds rows 4*(l/16)+j (j<4), col l%16
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;      // chunk length (tokens)
+constexpr int NTHR = 256;   // threads per workgroup
+constexpr int NWAVE = 4;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Orders LDS traffic between the lanes of one wave (no workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x) { return static_cast<T>(x); }
+
+// LDS row pitch (elements) for a row of D elements: +16 bytes keeps 16-byte
+// alignment and shifts consecutive rows by four banks.
+template <typename T, int D> struct Pitch { static constexpr int value = D + 16 / (int)sizeof(T); };
+
+// ---------------------------------------------------------------- MFMA --
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int KSTEP = 32;
+  typedef bf16x8 frag;
+  __device__ static __forceinline__ f32x4 op(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // Element (i, kk) of a fragment source, i = l%16 (stride RS), kk along K (stride KS).
+  template <int RS, int KS>
+  __device__ static __forceinline__ frag load(const bf16* p) {
+    const int l = lane_id();
+    const bf16* q = p + (l & 15) * RS + ((l >> 4) * 8) * KS;
+    if constexpr (KS == 1) {
+      return *reinterpret_cast<const frag*>(q);
+    } else {
+      frag f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = q[j * KS];
+      return f;
+    }
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KSTEP = 4;
+  typedef float frag;
+  __device__ static __forceinline__ f32x4 op(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  template <int RS, int KS>
+  __device__ static __forceinline__ frag load(const float* p) {
+    const int l = lane_id();
+    return p[(l & 15) * RS + (l >> 4) * KS];
+  }
+};
+
+// acc[j] += A[16 x KD] * B[KD x 16 (column tile j)], for NT column tiles.
+//   A(m, k) = a[m*ARS + k*ACS]          (a points at the tile's (0, 0))
+//   B(k, n) = b[k*BRS + (16*j + n)*BCS] (b points at column 0)
+// Contraction steps with k0 >= kend are skipped (kend is wave-uniform; the
+// skipped part of A must be zero for the result to be exact).
+template <typename T, int KD, int NT, int ARS, int ACS, int BRS, int BCS>
+__device__ __forceinline__ void mma_row(f32x4 (&acc)[NT], const T* a, const T* b, int kend = KD) {
+  constexpr int KS = Mma<T>::KSTEP;
+  static_assert(KD % KS == 0, "contraction length must be a multiple of the MFMA K step");
+#pragma unroll
+  for (int k0 = 0; k0 < KD; k0 += KS) {
+    if (k0 < kend) {
+      const auto fa = Mma<T>::template load<ARS, ACS>(a + k0 * ACS);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const auto fb = Mma<T>::template load<BCS, BRS>(b + k0 * BRS + 16 * j * BCS);
+        acc[j] = Mma<T>::op(fa, fb, acc[j]);
+      }
+    }
+  }
+}
+
+// Single 16x16 output tile.
+template <typename T, int KD, int ARS, int ACS, int BRS, int BCS>
+__device__ __forceinline__ void mma_tile(f32x4& acc, const T* a, const T* b, int kend = KD) {
+  f32x4 t[1] = {acc};
+  mma_row<T, KD, 1, ARS, ACS, BRS, BCS>(t, a, b, kend);
+  acc = t[0];
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row / column of accumulator element j held by this lane (within a tile).
+__device__ __forceinline__ int acc_row(int j) { return 4 * (lane_id() >> 4) + j; }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+// ------------------------------------------------------------- staging --
+// Copies rows [0, nrows) of an R x D tile from global memory (row stride
+// `gstride` elements) to LDS (row pitch P); rows >= nrows are zero-filled.
+// 16-byte vector accesses; D * sizeof(T) must be a multiple of 16.
+template <typename T, int R, int D, int P>
+__device__ __forceinline__ void stage_rows(T* lds, const T* g, long gstride, int nrows) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int VPR = D / VEC;
+  static_assert(D % VEC == 0, "row length must be a multiple of 16 bytes");
+  static_assert((P * sizeof(T)) % 16 == 0, "LDS pitch must keep 16-byte alignment");
+  for (int i = threadIdx.x; i < R * VPR; i += NTHR) {
+    const int r = i / VPR, c = (i % VPR) * VEC;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (r < nrows) val = *reinterpret_cast<const uint4*>(g + (long)r * gstride + c);
+    *reinterpret_cast<uint4*>(lds + r * P + c) = val;
+  }
+}
+
+// Finds the sequence n with off[n] <= c < off[n + 1] (off non-decreasing,
+// length N + 1); returns the last such n among empty sequences.
+__device__ __forceinline__ int find_seq(const int32_t* off, int N, int c) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Inclusive prefix sum across a wave64 (lane i gets x_0 + ... + x_i).
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_up(x, d, 64);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+
+}  // namespace gdr

@@ -1,0 +1,527 @@
+// gdr_fwd.hip -- forward kernels of the chunked gated delta rule on gfx950.
+//
+// Chunk form (derived from the recurrence S_t = e^{g_t}(I - b_t k_t k_t^T)S_{t-1}
+// + b_t k_t v_t^T, o_t = s S_t^T q_t; the pages name the WY intermediates
+// W, U and the per-chunk state S that the forward writes and re-reads:
+// FlashQLA curated summary, section "GDN Chunked Prefill的效率問題").  For a
+// chunk of n <= 64 tokens entering with state h:
+//   gamma = cumsum(g),  Gamma = e^gamma,  D_ij = e^{gamma_i - gamma_j}
+//   L = strict_lower(diag(b) (D * K K^T)),  A = (I + L)^{-1}
+//   W = A diag(b Gamma) K,   U = A diag(b) V,   Vnew = U - W h
+//   O = s (diag(Gamma) Q h + lower(D * Q K^T) Vnew)
+//   h' = Gamma_n h + (diag(e^{gamma_n - gamma}) K)^T Vnew
+//
+// Kernels, in launch order:
+//   k_plan    token/chunk/segment offset tables (one workgroup)
+//   k_intra   per (chunk, value head): gate cumsum, K K^T, blocked fp32
+//             triangular inverse, W and U on MFMA            [fully parallel]
+//   k_state   per (sequence, value head, V block, CP segment): the serial
+//             chunk recurrence with h in fp32 registers        [serial part]
+//   k_output  per (chunk, value head): O                       [fully parallel]
+// The split of the serial state pass into context-parallel segments rebuilt
+// by a gate-decay warmup follows the pages' automatic single-card CP (FlashQLA
+// curated summary, section "平衡解決方案：雙核心融合與自動CP"; Tongyi page,
+// section "FlashQLAの主な利点").
+#include <math.h>
+#include <type_traits>
+
+#include "gdr_device.h"
+#include "gdr_kernels.h"
+
+namespace gdr {
+
+// ---------------------------------------------------------------- k_plan --
+// cu[n] (copied or n*T), chunk_off[n] = sum_{m<n} ceil(len_m / 64),
+// seg_off[n] = sum_{m<n} max(1, ceil(chunks_m / seg_chunks)).
+__global__ __launch_bounds__(1024) void k_plan(PlanParams p) {
+  __shared__ int32_t sc[2][1024], ss[2][1024];
+  const int tid = threadIdx.x, N = p.N;
+  const int per = (N + 1023) / 1024;
+  const int b = min(tid * per, N), e = min(b + per, N);
+  auto cu_at = [&](int n) -> int32_t { return p.cu_in ? p.cu_in[n] : n * p.T; };
+  int c_sum = 0, s_sum = 0;
+  for (int n = b; n < e; ++n) {
+    const int len = max(cu_at(n + 1) - cu_at(n), 0);
+    const int ch = (len + CH - 1) / CH;
+    c_sum += ch;
+    s_sum += max(1, (ch + p.seg_chunks - 1) / p.seg_chunks);
+  }
+  int buf = 0;
+  sc[0][tid] = c_sum;
+  ss[0][tid] = s_sum;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
+    const int a = sc[buf][tid] + (tid >= d ? sc[buf][tid - d] : 0);
+    const int s2 = ss[buf][tid] + (tid >= d ? ss[buf][tid - d] : 0);
+    buf ^= 1;
+    sc[buf][tid] = a;
+    ss[buf][tid] = s2;
+    __syncthreads();
+  }
+  int c_run = sc[buf][tid] - c_sum, s_run = ss[buf][tid] - s_sum;  // exclusive
+  for (int n = b; n < e; ++n) {
+    const int len = max(cu_at(n + 1) - cu_at(n), 0);
+    const int ch = (len + CH - 1) / CH;
+    p.cu[n] = cu_at(n);
+    p.chunk_off[n] = c_run;
+    p.seg_off[n] = s_run;
+    c_run += ch;
+    s_run += max(1, (ch + p.seg_chunks - 1) / p.seg_chunks);
+  }
+  if (tid == 1023) {
+    p.cu[N] = cu_at(N);
+    p.chunk_off[N] = sc[buf][1023];
+    p.seg_off[N] = ss[buf][1023];
+  }
+}
+
+// Locates chunk c: sequence n, first token t0 and valid length; false if the
+// device tables disagree with the grid (then the workgroup writes nothing).
+__device__ __forceinline__ bool locate_chunk(const SeqTables& s, int c, int& n, int& t0, int& len) {
+  if (c >= s.NTtot) return false;
+  n = find_seq(s.chunk_off, s.N, c);
+  t0 = s.cu[n] + (c - s.chunk_off[n]) * CH;
+  len = min(CH, s.cu[n + 1] - t0);
+  return len > 0 && t0 >= 0 && (long)t0 + len <= s.Ttot;
+}
+
+// --------------------------------------------------------------- k_intra --
+template <typename T, int KD>
+__global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
+  constexpr bool F32 = std::is_same<T, float>::value;
+  constexpr int VD = KD;
+  constexpr int PK = Pitch<T, KD>::value;
+  constexpr int PV = Pitch<T, VD>::value;
+  constexpr int PL = 68;                        // fp32 64-wide rows
+  constexpr int PAT = Pitch<T, CH>::value;
+  constexpr int PX = 20;
+  __shared__ __align__(16) T sK[CH * PK];
+  __shared__ __align__(16) T sV[CH * PV];
+  __shared__ __align__(16) float sL[CH * PL];
+  __shared__ __align__(16) float sA[CH * PL];
+  __shared__ __align__(16) T sAt[F32 ? 4 : CH * PAT];
+  __shared__ __align__(16) float sX[NWAVE][16 * PX];
+  __shared__ float sG[CH], sB[CH];
+
+  const SeqTables& s = p.s;
+  const int c = blockIdx.x, h = blockIdx.y;
+  int n, t0, len;
+  if (!locate_chunk(s, c, n, t0, len)) return;
+  const int hk = h / (p.Hv / p.Hq);
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+
+  if (w == 0) {
+    const float gv = (l < len) ? p.g[(long)(t0 + l) * p.Hv + h] : 0.f;
+    const float bv = (l < len) ? p.beta[(long)(t0 + l) * p.Hv + h] : 0.f;
+    const float gc = wave_inclusive_scan(gv);
+    sG[l] = gc;
+    sB[l] = bv;
+    if (l < len) {
+      p.gcum[(long)h * s.Ttot + t0 + l] = gc;
+      if (p.g_cum_out) p.g_cum_out[(long)(t0 + l) * p.Hv + h] = gc;
+    }
+  }
+  stage_rows<T, CH, KD, PK>(sK, (const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+  stage_rows<T, CH, VD, PV>(sV, (const T*)p.v + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, len);
+  __syncthreads();
+
+  // L = strict_lower(diag(b) (D * K K^T)); the diagonal of K K^T certifies
+  // 0 <= b |k|^2 <= 2 (non-expansive steps) for the CP warmup bound.
+  int bad = 0;
+  for (int jt = 0; jt < 4; ++jt) {
+    f32x4 a = zero4();
+    if (jt <= w) mma_tile<T, KD, PK, 1, 1, PK>(a, sK + 16 * w * PK, sK + 16 * jt * PK);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + acc_row(e), cc = 16 * jt + acc_col();
+      float lv = 0.f;
+      if (r > cc) lv = sB[r] * __expf(sG[r] - sG[cc]) * a[e];
+      if (r == cc && r < len) {
+        const float bn = sB[r] * a[e];
+        if (!(bn >= 0.f && bn <= 2.f)) bad = 1;
+      }
+      sL[r * PL + cc] = lv;
+    }
+  }
+  const int any_bad = __syncthreads_or(bad);
+  if (tid == 0) p.cert[(long)h * s.NTtot + c] = any_bad ? INFINITY : sG[len - 1];
+
+  if (p.A_in) {
+    // A supplied by the caller (rows of valid tokens; identity beyond).
+    for (int i = tid; i < CH * CH; i += NTHR) {
+      const int r = i / CH, cc = i % CH;
+      float a = (r == cc) ? 1.f : 0.f;
+      if (r < len) a = (cc < len) ? p.A_in[((long)(t0 + r) * p.Hv + h) * CH + cc] : 0.f;
+      sA[r * PL + cc] = a;
+    }
+    __syncthreads();
+  } else {
+    // Blocked inverse of the unit lower triangular I + L in fp32:
+    // diagonal 16x16 blocks by forward substitution (one wave each) ...
+    if (l < 16) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = (r == l) ? 1.f : 0.f;
+        const float* Lr = sL + (16 * w + r) * PL + 16 * w;
+#pragma unroll
+        for (int jj = 0; jj < r; ++jj) acc -= Lr[jj] * x[jj];
+        x[r] = acc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sA[(16 * w + r) * PL + 16 * w + l] = x[r];
+    }
+    for (int i = tid; i < CH * CH; i += NTHR) {
+      const int r = i / CH, cc = i % CH;
+      if ((cc >> 4) > (r >> 4)) sA[r * PL + cc] = 0.f;
+    }
+    __syncthreads();
+    // ... then the off-diagonal blocks by distance from the diagonal:
+    // A_ij = -A_ii * sum_{j <= m < i} L_im A_mj.
+    for (int d = 1; d < 4; ++d) {
+      if (w + d < 4) {
+        const int i = w + d, j = w;
+        f32x4 xacc = zero4();
+        for (int m = j; m < i; ++m)
+          mma_tile<float, 16, PL, 1, PL, 1>(xacc, sL + 16 * i * PL + 16 * m, sA + 16 * m * PL + 16 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sX[w][acc_row(e) * PX + acc_col()] = xacc[e];
+        wave_sync();
+        f32x4 yacc = zero4();
+        mma_tile<float, 16, PL, 1, PX, 1>(yacc, sA + 16 * i * PL + 16 * i, sX[w]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sA[(16 * i + acc_row(e)) * PL + 16 * j + acc_col()] = -yacc[e];
+      }
+      __syncthreads();
+    }
+  }
+
+  // Export A, fold the row scales into K and V, round A for the MFMA.
+  if (p.A_ws || p.A_out) {
+    for (int i = tid; i < len * CH; i += NTHR) {
+      const int r = i / CH, cc = i % CH;
+      const float a = sA[r * PL + cc];
+      if (p.A_ws) p.A_ws[((long)h * s.Ttot + t0 + r) * CH + cc] = a;
+      if (p.A_out) p.A_out[((long)(t0 + r) * p.Hv + h) * CH + cc] = a;
+    }
+  }
+  for (int i = tid; i < CH * KD; i += NTHR) {
+    const int r = i / KD, cc = i % KD;
+    sK[r * PK + cc] = from_f<T>(to_f(sK[r * PK + cc]) * (sB[r] * __expf(sG[r])));
+  }
+  for (int i = tid; i < CH * VD; i += NTHR) {
+    const int r = i / VD, cc = i % VD;
+    sV[r * PV + cc] = from_f<T>(to_f(sV[r * PV + cc]) * sB[r]);
+  }
+  if constexpr (!F32) {
+    for (int i = tid; i < CH * CH; i += NTHR) {
+      const int r = i / CH, cc = i % CH;
+      sAt[r * PAT + cc] = from_f<T>(sA[r * PL + cc]);
+    }
+  }
+  __syncthreads();
+
+  constexpr int PA = F32 ? PL : PAT;
+  const T* Ap = F32 ? reinterpret_cast<const T*>(sA) : sAt;
+  {
+    f32x4 acc[KD / 16];
+#pragma unroll
+    for (int j = 0; j < KD / 16; ++j) acc[j] = zero4();
+    mma_row<T, CH, KD / 16, PA, 1, PK, 1>(acc, Ap + 16 * w * PA, sK, 16 * (w + 1));
+    T* Wg = (T*)p.W + ((long)h * s.Ttot + t0) * KD;
+#pragma unroll
+    for (int j = 0; j < KD / 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + acc_row(e);
+        if (r < len) Wg[(long)r * KD + 16 * j + acc_col()] = from_f<T>(acc[j][e]);
+      }
+  }
+  {
+    f32x4 acc[VD / 16];
+#pragma unroll
+    for (int j = 0; j < VD / 16; ++j) acc[j] = zero4();
+    mma_row<T, CH, VD / 16, PA, 1, PV, 1>(acc, Ap + 16 * w * PA, sV, 16 * (w + 1));
+    T* Ug = (T*)p.U + ((long)h * s.Ttot + t0) * VD;
+#pragma unroll
+    for (int j = 0; j < VD / 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + acc_row(e);
+        if (r < len) Ug[(long)r * VD + 16 * j + acc_col()] = from_f<T>(acc[j][e]);
+      }
+  }
+}
+
+// --------------------------------------------------------------- k_state --
+template <typename T, int KD, int BV>
+__global__ __launch_bounds__(NTHR) void k_state(StateParams p) {
+  constexpr int VD = KD;
+  constexpr int PK = Pitch<T, KD>::value;
+  constexpr int PU = Pitch<T, BV>::value;
+  constexpr int PVT = Pitch<T, CH>::value;
+  constexpr int NCB = BV / 16;
+  constexpr int NTILE = (KD / 16) * NCB;
+  constexpr int TPW = NTILE / NWAVE;
+  static_assert(NTILE % NWAVE == 0, "state tiles must split evenly over the waves");
+  __shared__ __align__(16) T sW[CH * PK];
+  __shared__ __align__(16) T sK[CH * PK];
+  __shared__ __align__(16) T sU[CH * PU];
+  __shared__ __align__(16) T shT[BV * PK];
+  __shared__ __align__(16) T sVt[BV * PVT];
+  __shared__ float sDec[CH];
+
+  const SeqTables& s = p.s;
+  const int h = blockIdx.y / p.nvb, vb = blockIdx.y % p.nvb;
+  const int item = blockIdx.x;
+  const int n = find_seq(s.seg_off, s.N, item);
+  const int pseg = item - s.seg_off[n];
+  const int nseg = s.seg_off[n + 1] - s.seg_off[n];
+  const int c0 = s.chunk_off[n];
+  const int nch = s.chunk_off[n + 1] - c0;
+  if (pseg < 0 || pseg >= nseg || c0 < 0 || c0 + nch > s.NTtot) return;
+  const int L = p.seg_chunks;
+  const int hk = h / (p.Hv / p.Hq);
+  const int w = wave_id();
+
+  // A head is certified when every warmup window's gate mass is small enough
+  // (all segments of the head evaluate the same test, so they agree).
+  int ok = 1;
+  for (int q = 1 + (int)threadIdx.x; q < nseg; q += NTHR) {
+    const int ws = q * L - p.warmup;
+    if (ws > 0) {
+      float sum = 0.f;
+      for (int cc = ws; cc < q * L; ++cc) sum += p.cert[(long)h * s.NTtot + c0 + cc];
+      if (!(sum <= p.log_eps)) ok = 0;
+    }
+  }
+  const bool certified = !__syncthreads_or(!ok);
+  int cstart, cbeg, cend;
+  bool write_final;
+  if (!certified) {
+    if (pseg != 0) return;             // segment 0 runs the whole head serially
+    cstart = 0; cbeg = 0; cend = nch; write_final = true;
+  } else {
+    cbeg = pseg * L;
+    cend = min(cbeg + L, nch);
+    cstart = (pseg == 0) ? 0 : max(0, cbeg - p.warmup);
+    write_final = (pseg == nseg - 1);
+  }
+
+  f32x4 hacc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 16 * rb + acc_row(e), v = vb * BV + 16 * cb + acc_col();
+      hacc[i][e] = (cstart == 0 && p.h0) ? p.h0[(((long)n * p.Hv + h) * KD + d) * VD + v] : 0.f;
+    }
+  }
+
+  for (int jc = cstart; jc < cend; ++jc) {
+    const int gc = c0 + jc;
+    const int t0 = s.cu[n] + jc * CH;
+    const int len = min(CH, s.cu[n + 1] - t0);
+    if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) break;
+    const bool warm = jc < cbeg;
+    stage_rows<T, CH, KD, PK>(sW, (const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
+    stage_rows<T, CH, KD, PK>(sK, (const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    stage_rows<T, CH, BV, PU>(sU, (const T*)p.U + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, len);
+    const float glast = p.gcum[(long)h * s.Ttot + t0 + len - 1];
+    if (threadIdx.x < CH) {
+      const int r = threadIdx.x;
+      sDec[r] = (r < len) ? __expf(glast - p.gcum[(long)h * s.Ttot + t0 + r]) : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * rb + acc_row(e), vl = 16 * cb + acc_col();
+        const T hv = from_f<T>(hacc[i][e]);
+        shT[vl * PK + d] = hv;
+        if (!warm && p.hbuf)
+          ((T*)p.hbuf)[(((long)h * s.NTtot + gc) * VD + vb * BV + vl) * KD + d] = hv;
+      }
+    }
+    __syncthreads();
+
+    {  // Vnew = U - W h ; stage diag(e^{gamma_n - gamma}) Vnew transposed
+      f32x4 acc[NCB];
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) acc[j] = zero4();
+      mma_row<T, KD, NCB, PK, 1, 1, PK>(acc, sW + 16 * w * PK, shT);
+#pragma unroll
+      for (int j = 0; j < NCB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * w + acc_row(e), vl = 16 * j + acc_col();
+          const float vn = to_f(sU[r * PU + vl]) - acc[j][e];
+          if (!warm && r < len)
+            ((T*)p.vnew)[((long)h * s.Ttot + t0 + r) * VD + vb * BV + vl] = from_f<T>(vn);
+          sVt[vl * PVT + r] = from_f<T>(vn * sDec[r]);
+        }
+    }
+    __syncthreads();
+
+    const float dlast = __expf(glast);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
+      hacc[i] *= dlast;
+      mma_tile<T, CH, 1, PK, 1, PVT>(hacc[i], sK + 16 * rb, sVt + 16 * cb * PVT);
+    }
+    __syncthreads();
+  }
+
+  if (write_final && p.ht) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * rb + acc_row(e), v = vb * BV + 16 * cb + acc_col();
+        p.ht[(((long)n * p.Hv + h) * KD + d) * VD + v] = hacc[i][e];
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------- k_output --
+template <typename T, int KD>
+__global__ __launch_bounds__(NTHR) void k_output(OutputParams p) {
+  constexpr int VD = KD;
+  constexpr int PK = Pitch<T, KD>::value;
+  constexpr int PV = Pitch<T, VD>::value;
+  constexpr int PP = Pitch<T, CH>::value;
+  __shared__ __align__(16) T sQ[CH * PK];
+  __shared__ __align__(16) T sK[CH * PK];
+  __shared__ __align__(16) T shT[VD * PK];
+  __shared__ __align__(16) T sVn[CH * PV];
+  __shared__ __align__(16) T sP[CH * PP];
+  __shared__ float sG[CH];
+
+  const SeqTables& s = p.s;
+  const int c = blockIdx.x, h = blockIdx.y;
+  int n, t0, len;
+  if (!locate_chunk(s, c, n, t0, len)) return;
+  const int hk = h / (p.Hv / p.Hq);
+  const int w = wave_id();
+
+  stage_rows<T, CH, KD, PK>(sQ, (const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+  stage_rows<T, CH, KD, PK>(sK, (const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+  stage_rows<T, VD, KD, PK>(shT, (const T*)p.hbuf + ((long)h * s.NTtot + c) * VD * KD, KD, VD);
+  stage_rows<T, CH, VD, PV>(sVn, (const T*)p.vnew + ((long)h * s.Ttot + t0) * VD, VD, len);
+  if (threadIdx.x < CH) sG[threadIdx.x] = p.gcum[(long)h * s.Ttot + t0 + min((int)threadIdx.x, len - 1)];
+  __syncthreads();
+
+  for (int jt = 0; jt < 4; ++jt) {  // P = lower(D * Q K^T), diagonal included
+    f32x4 a = zero4();
+    if (jt <= w) mma_tile<T, KD, PK, 1, 1, PK>(a, sQ + 16 * w * PK, sK + 16 * jt * PK);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + acc_row(e), cc = 16 * jt + acc_col();
+      const float pv = (r >= cc) ? __expf(sG[r] - sG[cc]) * a[e] : 0.f;
+      sP[r * PP + cc] = from_f<T>(pv);
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[VD / 16];
+#pragma unroll
+  for (int j = 0; j < VD / 16; ++j) acc[j] = zero4();
+  mma_row<T, KD, VD / 16, PK, 1, 1, PK>(acc, sQ + 16 * w * PK, shT);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float gm = __expf(sG[16 * w + acc_row(e)]);
+#pragma unroll
+    for (int j = 0; j < VD / 16; ++j) acc[j][e] *= gm;
+  }
+  mma_row<T, CH, VD / 16, PP, 1, PV, 1>(acc, sP + 16 * w * PP, sVn, 16 * (w + 1));
+  T* og = (T*)p.o;
+#pragma unroll
+  for (int j = 0; j < VD / 16; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * w + acc_row(e);
+      if (r < len) og[((long)(t0 + r) * p.Hv + h) * VD + 16 * j + acc_col()] = from_f<T>(p.scale * acc[j][e]);
+    }
+}
+
+// ------------------------------------------------------------- launchers --
+#define GDR_LAUNCH(name, kern, grid, st, ...)        \
+  do {                                               \
+    timing_before(name, st);                         \
+    hipLaunchKernelGGL(kern, grid, dim3(NTHR), 0, st, __VA_ARGS__); \
+    err = hipGetLastError();                         \
+    timing_after(st);                                \
+  } while (0)
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t st) {
+  timing_before("plan", st);
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, p);
+  hipError_t err = hipGetLastError();
+  timing_after(st);
+  return err;
+}
+
+template <typename T, int KD>
+static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
+  hipError_t err;
+  GDR_LAUNCH("intra_wy", (k_intra<T, KD>), dim3(p.s.NTtot, p.Hv), st, p);
+  return err;
+}
+
+template <typename T, int KD, int BV>
+static hipError_t state_impl(const StateParams& p, int total_segs, hipStream_t st) {
+  hipError_t err;
+  GDR_LAUNCH("chunk_state", (k_state<T, KD, BV>), dim3(total_segs, p.Hv * p.nvb), st, p);
+  return err;
+}
+
+template <typename T, int KD>
+static hipError_t output_impl(const OutputParams& p, hipStream_t st) {
+  hipError_t err;
+  GDR_LAUNCH("chunk_output", (k_output<T, KD>), dim3(p.s.NTtot, p.Hv), st, p);
+  return err;
+}
+
+hipError_t launch_intra(DType dt, int KD, const IntraParams& p, hipStream_t st) {
+  if (dt == DType::BF16) {
+    if (KD == 32) return intra_impl<bf16, 32>(p, st);
+    if (KD == 64) return intra_impl<bf16, 64>(p, st);
+    if (KD == 128) return intra_impl<bf16, 128>(p, st);
+  } else {
+    if (KD == 32) return intra_impl<float, 32>(p, st);
+    if (KD == 64) return intra_impl<float, 64>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int total_segs, hipStream_t st) {
+  if (dt == DType::BF16) {
+    if (KD == 32 && BV == 32) return state_impl<bf16, 32, 32>(p, total_segs, st);
+    if (KD == 64 && BV == 32) return state_impl<bf16, 64, 32>(p, total_segs, st);
+    if (KD == 128 && BV == 32) return state_impl<bf16, 128, 32>(p, total_segs, st);
+    if (KD == 128 && BV == 64) return state_impl<bf16, 128, 64>(p, total_segs, st);
+  } else {
+    if (KD == 32 && BV == 32) return state_impl<float, 32, 32>(p, total_segs, st);
+    if (KD == 64 && BV == 32) return state_impl<float, 64, 32>(p, total_segs, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_output(DType dt, int KD, const OutputParams& p, hipStream_t st) {
+  if (dt == DType::BF16) {
+    if (KD == 32) return output_impl<bf16, 32>(p, st);
+    if (KD == 64) return output_impl<bf16, 64>(p, st);
+    if (KD == 128) return output_impl<bf16, 128>(p, st);
+  } else {
+    if (KD == 32) return output_impl<float, 32>(p, st);
+    if (KD == 64) return output_impl<float, 64>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

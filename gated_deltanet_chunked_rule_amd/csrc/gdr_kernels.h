@@ -1,0 +1,109 @@
+// gdr_kernels.h -- parameter blocks and launchers of the gfx950 kernels
+// (internal to libgdr; the public C ABI is include/gdr.h).
+//
+// Workspace layouts (head-major so that one chunk of one head is contiguous):
+//   gcum  fp32 [Hv][Ttot]          chunk-local inclusive cumsum of g
+//   cert  fp32 [Hv][NTtot]         chunk gate sum, +inf if some beta|k|^2 is outside [0, 2]
+//   W, U  T    [Hv][Ttot][K|V]     W = A diag(beta*Gamma) K,  U = A diag(beta) V
+//   vnew  T    [Hv][Ttot][V]       Vnew = U - W h (the chunk's corrected values)
+//   hbuf  T    [Hv][NTtot][V][K]   state entering each chunk, stored transposed
+//   A     fp32 [Hv][Ttot][64]      rows of the chunk's A (backward only)
+//   dhbuf T    [Hv][NTtot][V][K]   state gradient leaving each chunk (transposed)
+//   dvn   T    [Hv][Ttot][V]       gradient of Vnew
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+enum class DType { BF16 = 0, F32 = 1 };
+
+struct SeqTables {
+  const int32_t* cu;         // [N+1] token offsets
+  const int32_t* chunk_off;  // [N+1] first global chunk of each sequence
+  const int32_t* seg_off;    // [N+1] first state work item of each sequence
+  int N;
+  long Ttot;                 // tokens in the packed batch
+  int NTtot;                 // chunks (host count; device tables must agree)
+};
+
+struct PlanParams {
+  const int32_t* cu_in;      // nullable: uniform rows of T tokens
+  int N, T, seg_chunks;
+  int32_t *cu, *chunk_off, *seg_off;
+};
+
+struct IntraParams {
+  SeqTables s;
+  const void *k, *v;
+  const float *g, *beta;
+  int Hq, Hv;
+  float* gcum;
+  float* g_cum_out;          // nullable, [Ttot][Hv]
+  float* cert;
+  void *W, *U;
+  float* A_ws;               // nullable, [Hv][Ttot][64]
+  float* A_out;              // nullable, [Ttot][Hv][64]
+  const float* A_in;         // nullable: use this A ([Ttot][Hv][64]) instead of inverting
+};
+
+struct StateParams {
+  SeqTables s;
+  const void *k, *W, *U;
+  const float *gcum, *cert;
+  const float* h0;           // nullable [N][Hv][K][V]
+  float* ht;                 // nullable [N][Hv][K][V]
+  void* hbuf;                // nullable
+  void* vnew;
+  int Hq, Hv;
+  int seg_chunks, warmup;
+  float log_eps;
+  int nvb;                   // V blocks per head
+};
+
+struct OutputParams {
+  SeqTables s;
+  const void *q, *k, *hbuf, *vnew;
+  const float* gcum;
+  void* o;                   // [Ttot][Hv][V]
+  int Hq, Hv;
+  float scale;
+};
+
+struct DStateParams {        // reverse state pass
+  SeqTables s;
+  const void *q, *k, *W, *d_o;
+  const float* gcum;
+  const float* dht;          // nullable
+  float* dh0;                // nullable
+  void* dhbuf;
+  void* dvn;
+  int Hq, Hv;
+  float scale;
+  int nvb;
+};
+
+struct GradParams {          // per-chunk gradients
+  SeqTables s;
+  const void *q, *k, *v, *d_o, *hbuf, *vnew, *dhbuf, *dvn;
+  const float *gcum, *beta, *A_ws;
+  void *dq, *dk, *dv;
+  float *dbeta, *dg;
+  int Hq, Hv;
+  float scale;
+};
+
+// Kernel launchers; each returns hipGetLastError() of its launch.
+hipError_t launch_plan(const PlanParams& p, hipStream_t st);
+hipError_t launch_intra(DType dt, int KD, const IntraParams& p, hipStream_t st);
+hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int total_segs, hipStream_t st);
+hipError_t launch_output(DType dt, int KD, const OutputParams& p, hipStream_t st);
+hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, hipStream_t st);
+hipError_t launch_grads(DType dt, int KD, const GradParams& p, hipStream_t st);
+
+// Kernel timing hooks (gdr_timing.cpp).
+void timing_before(const char* name, hipStream_t st);
+void timing_after(hipStream_t st);
+
+}  // namespace gdr
