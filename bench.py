@@ -1,0 +1,151 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked gated-delta-rule forward on one MI355X.
+
+Workload: the long-context configuration B=1, T=65536, Hq=4, Hv=8, K=V=128,
+bf16 q/k/v with fp32 g/beta, 64-token chunks, no initial state, automatic
+context-parallel split.  One step = one full forward pass (plan, intra-chunk
+WY, serial state, output) through the C ABI on resident device buffers.
+
+Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant
+kernel (its HIP-event duration on the launch stream, against the algorithmic
+bytes or flops per launch) and the fp64 CPU oracle's throughput on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 MFMA
+METRIC = "GDN chunked-prefill fwd tokens/s (B=1,T=64K,Hv=8) + % MFMA/HBM roofline"
+
+
+def per_kernel_work(w, G):
+    """Algorithmic bytes and flops per token x value head for each kernel of
+    the forward (each input read once, each output written once; bf16 = 2 B).
+    Returns {kernel: (bytes, flops)} per token*value-head."""
+    K, V, C, e = w.K, w.V, 64, 2
+    return {
+        # k, v, g, beta in; W, U, g_cum out; K K^T, A W-solve, A U-solve (+inverse)
+        "intra_wy": (K * e / G + V * e + 8 + (K + V) * e + 4,
+                     2 * C * K + 2 * C * K + 2 * C * V + C * C // 3),
+        # W, U, k, g_cum in; Vnew and the chunk entry state out
+        "chunk_state": (K * e + V * e + K * e / G + 4 + V * e + K * V * e / C,
+                        4 * K * V),
+        # q, k, chunk state, Vnew, g_cum in; o out
+        "chunk_output": (2 * K * e / G + K * V * e / C + V * e + 4 + V * e,
+                         2 * C * K + 2 * K * V + 2 * C * V),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "the path is a single-GPU kernel and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_chunked_rule_amd as gdr
+    import gdr_inputs as gi
+
+    w = gi.WORKLOADS["long_context"]
+    inp = gi.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    g, beta = inp["g"].to(dev), inp["beta"].to(dev)
+    scale = inp["scale"]
+    G = w.Hv // w.Hq
+    plan = gdr.gdr_chunk_fwd_plan(q, v)
+    # workspace allocated once, outside the timed region
+    o, ht, _, _ = gdr.gdr_chunk_fwd(q, k, v, g, beta, scale)
+    ws = torch.empty(gdr.fwd_workspace_bytes(q, v), device=dev, dtype=torch.uint8)
+
+    def step():
+        gdr.gdr_chunk_fwd(q, k, v, g, beta, scale, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gdr.timing.reset()
+    gdr.timing.enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gdr.timing.enable(False)
+    kern = gdr.timing.collect()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens = w.B * w.T
+    value = tokens / (ms_per_step * 1e-3)
+
+    if args.calib_copy_mb > 0:
+        nbytes = args.calib_copy_mb << 20
+        src = torch.empty(nbytes // 4, device=dev, dtype=torch.float32).uniform_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # roofline of the dominant kernel
+    work = per_kernel_work(w, G)
+    tv = w.B * w.T * w.Hv
+    dom = max((n for n in kern if n in work), key=lambda n: kern[n][0])
+    avg_ms = kern[dom][0] / kern[dom][1]
+    bytes_tv, flops_tv = work[dom]
+    t_hbm = bytes_tv * tv / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops_tv * tv / (MFMA_BF16_PEAK_TFS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": bytes_tv * tv / (avg_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops_tv * tv / (avg_ms * 1e-3) / 1e12,
+                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["kernel_avg_us"] = avg_ms * 1e3
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = max(1, min(16, os.cpu_count() or 1))
+        t_sample = w.T
+        f = lambda x: x.to(torch.float64).numpy()
+        c0 = time.perf_counter()
+        oracle.gdr_fwd(f(inp["q"][:, :t_sample]), f(inp["k"][:, :t_sample]), f(inp["v"][:, :t_sample]),
+                       f(inp["g"][:, :t_sample]), f(inp["beta"][:, :t_sample]), scale, threads=threads)
+        c1 = time.perf_counter()
+        cpu = {"value": t_sample / (c1 - c0), "unit": "tokens/s", "cores": min(threads, w.Hv),
+               "kind": "oracle",
+               "sample": f"fp64 token recurrence over the whole workload ({t_sample} tokens x {w.Hv} "
+                         f"value heads), one thread per head"}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "long_context", "B": w.B, "T": w.T, "Hq": w.Hq, "Hv": w.Hv, "K": w.K,
+                   "V": w.V, "chunk": 64, "cp_segment_chunks": plan["segment_chunks"],
+                   "cp_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"]},
+        "kernels_us": {n: 1e3 * t / c for n, (t, c) in kern.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -32,7 +32,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_fwd_plan", "chunk_gated_delta_rule",
+__all__ = ["gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_fwd_plan", "fwd_workspace_bytes",
+           "bwd_workspace_bytes", "chunk_gated_delta_rule",
            "chunk_gated_delta_rule_fwd", "chunk_gated_delta_rule_bwd", "Options", "lib_path",
            "load_library", "GdrError", "timing"]
 
@@ -177,6 +178,32 @@ def gdr_chunk_fwd_plan(q, v, cu_seqlens=None, options=None):
     _check(lib.gdr_chunk_fwd_plan(ctypes.byref(sh), None if o is None else ctypes.byref(o),
                                   _host_ptr(cu_host), ctypes.byref(info)))
     return {n: getattr(info, n) for n, _ in _PlanInfo._fields_}
+
+
+def fwd_workspace_bytes(q, v, cu_seqlens=None, options=None) -> int:
+    """Workspace bytes gdr_chunk_fwd needs (to allocate it once, ahead of time)."""
+    lib = load_library()
+    _, cu_host = _cu_pair(cu_seqlens, "cpu") if cu_seqlens is not None else (None, None)
+    sh, _ = _shape(q, v, cu_host)
+    o = _opts(options)
+    n = lib.gdr_chunk_fwd_workspace_size(ctypes.byref(sh), None if o is None else ctypes.byref(o),
+                                         _host_ptr(cu_host))
+    if n == 0:
+        _check(-1)
+    return n
+
+
+def bwd_workspace_bytes(q, v, cu_seqlens=None, options=None) -> int:
+    """Workspace bytes gdr_chunk_bwd needs."""
+    lib = load_library()
+    _, cu_host = _cu_pair(cu_seqlens, "cpu") if cu_seqlens is not None else (None, None)
+    sh, _ = _shape(q, v, cu_host)
+    o = _opts(options)
+    n = lib.gdr_chunk_bwd_workspace_size(ctypes.byref(sh), None if o is None else ctypes.byref(o),
+                                         _host_ptr(cu_host))
+    if n == 0:
+        _check(-1)
+    return n
 
 
 def gdr_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, *,

@@ -62,8 +62,7 @@ int choose_segment(const Problem& P) {
   const long slots = (long)kCUs * kStateWgPerCU;
   const long units = (long)P.Hv * P.nvb;
   const int NTmax = std::max(P.NTmax, 1);
-  long base = 0;
-  for (int c : P.chunks) base += units * 1;
+  const long base = units * (long)P.N;
   if (base >= slots || NTmax <= 2 * W + 1) return NTmax;
   auto cost = [&](int L) {
     double total = 0.0;
@@ -178,7 +177,7 @@ Layout layout(const Problem& P, bool bwd) {
   Lo.cert = take(hv * nt * 4);
   Lo.W = take(hv * tt * P.K * P.esize);
   Lo.U = take(hv * tt * P.V * P.esize);
-  Lo.vnew = take(hv * tt * P.V * P.esize);
+  Lo.vnew = take(hv * nt * P.V * kChunk * P.esize);
   Lo.hbuf = take(hv * nt * P.V * P.K * P.esize);
   if (bwd) {
     Lo.A = take(hv * tt * kChunk * 4);

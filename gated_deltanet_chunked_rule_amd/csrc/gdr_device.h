@@ -133,6 +133,91 @@ __device__ __forceinline__ void stage_rows(T* lds, const T* g, long gstride, int
   }
 }
 
+// Global rows -> registers -> LDS.  load() issues every 16-byte global read of
+// an R x D tile (rows >= nrows read as zero) before anything is written, so a
+// tile's reads overlap; store() writes the rows to LDS (pitch P) and
+// store_t() writes the transpose (LDS element (c, r) = scale(r) * tile(r, c)).
+template <typename T, int R, int D>
+struct TileRegs {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int VPR = D / VEC;
+  static constexpr int NV = (R * VPR + NTHR - 1) / NTHR;
+  static_assert(D % VEC == 0, "row length must be a multiple of 16 bytes");
+  uint4 v[NV];
+  __device__ __forceinline__ void load(const T* g, long gstride, int nrows) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (int)threadIdx.x + i * NTHR;
+      const int r = idx / VPR, c = (idx % VPR) * VEC;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (idx < R * VPR && r < nrows) v[i] = *reinterpret_cast<const uint4*>(g + (long)r * gstride + c);
+    }
+  }
+  __device__ __forceinline__ int row(int i) const { return ((int)threadIdx.x + i * NTHR) / VPR; }
+  template <int P>
+  __device__ __forceinline__ void store(T* lds) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (int)threadIdx.x + i * NTHR;
+      const int r = idx / VPR, c = (idx % VPR) * VEC;
+      if (idx < R * VPR) *reinterpret_cast<uint4*>(lds + r * P + c) = v[i];
+    }
+  }
+  template <int PT, typename F>
+  __device__ __forceinline__ void store_t(T* lds, F scale) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = (int)threadIdx.x + i * NTHR;
+      const int r = idx / VPR, c = (idx % VPR) * VEC;
+      if (idx < R * VPR) {
+        const float s = scale(r);
+        const T* e = reinterpret_cast<const T*>(&v[i]);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) lds[(c + j) * PT + r] = from_f<T>(to_f(e[j]) * s);
+      }
+    }
+  }
+};
+
+// LDS rows [0, nrows) of an R x D tile (pitch P) -> global (row stride gstride),
+// 16-byte accesses.
+template <typename T, int R, int D, int P>
+__device__ __forceinline__ void store_rows(T* g, long gstride, const T* lds, int nrows) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int VPR = D / VEC;
+  for (int i = threadIdx.x; i < R * VPR; i += NTHR) {
+    const int r = i / VPR, c = (i % VPR) * VEC;
+    if (r < nrows) *reinterpret_cast<uint4*>(g + (long)r * gstride + c) = *reinterpret_cast<const uint4*>(lds + r * P + c);
+  }
+}
+
+// Accumulator tile -> LDS, transposed: element (row, col) of the tile goes to
+// lds[(col0 + col) * P + row0 + row]; a lane's four rows are contiguous, so
+// this is one 8-byte (bf16) or 16-byte (fp32) write.
+template <typename T, int P>
+__device__ __forceinline__ void acc_store_t(T* lds, int row0, int col0, const f32x4& a, float s = 1.f) {
+  T* dst = lds + (col0 + acc_col()) * P + row0 + acc_row(0);
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = from_f<T>(a[e] * s);
+    *reinterpret_cast<bf16x4*>(dst) = pk;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = from_f<T>(a[e] * s);
+  }
+}
+
+// Hardware workgroup id -> logical work index such that each of the 8 XCDs
+// (workgroups are dispatched round-robin over them) receives one contiguous
+// range of logical indices, run in increasing order: neighbouring work items
+// that read the same tiles then share that XCD's L2.  The grid is padded to a
+// multiple of 8; indices >= total must exit.
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int per = (total + 7) >> 3;
+  return (id & 7) * per + (id >> 3);
+}
+
 // Finds the sequence n with off[n] <= c < off[n + 1] (off non-decreasing,
 // length N + 1); returns the last such n among empty sequences.
 __device__ __forceinline__ int find_seq(const int32_t* off, int N, int c) {

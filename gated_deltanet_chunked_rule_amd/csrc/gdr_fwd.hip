@@ -86,30 +86,45 @@ __device__ __forceinline__ bool locate_chunk(const SeqTables& s, int c, int& n, 
 }
 
 // --------------------------------------------------------------- k_intra --
+// One workgroup per (chunk, value head).  LDS regions are reused across the
+// phases (A: K rows -> (b Gamma K)^T -> W staging; B: inverse scratch ->
+// (b V)^T -> U staging; C: L -> A in the working dtype; D: A in fp32).
 template <typename T, int KD>
 __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
-  constexpr int PK = Pitch<T, KD>::value;
-  constexpr int PV = Pitch<T, VD>::value;
-  constexpr int PL = 68;                        // fp32 64-wide rows
-  constexpr int PAT = Pitch<T, CH>::value;
+  constexpr int PK = Pitch<T, KD>::value;     // row-major K / W / U rows
+  constexpr int PT = Pitch<T, CH>::value;     // transposed tiles (64 tokens wide)
+  constexpr int PL = 68;                      // fp32 64-wide rows
   constexpr int PX = 20;
-  __shared__ __align__(16) T sK[CH * PK];
-  __shared__ __align__(16) T sV[CH * PV];
-  __shared__ __align__(16) float sL[CH * PL];
-  __shared__ __align__(16) float sA[CH * PL];
-  __shared__ __align__(16) T sAt[F32 ? 4 : CH * PAT];
-  __shared__ __align__(16) float sX[NWAVE][16 * PX];
+  constexpr int SZ_A = (CH * PK > KD * PT ? CH * PK : KD * PT) * (int)sizeof(T);
+  constexpr int SZ_B = (CH * PK > KD * PT ? CH * PK : KD * PT) * (int)sizeof(T);
+  constexpr int SZ_C = CH * PL * 4;
+  constexpr int SZ_D = CH * PL * 4;
+  static_assert(NWAVE * 16 * PX * 4 <= SZ_B, "inverse scratch must fit region B");
+  static_assert(CH * PT * (int)sizeof(T) <= SZ_C, "A tile must fit region C");
+  __shared__ __align__(16) char smem[SZ_A + SZ_B + SZ_C + SZ_D];
   __shared__ float sG[CH], sB[CH];
+  T* rA = reinterpret_cast<T*>(smem);
+  T* rB = reinterpret_cast<T*>(smem + SZ_A);
+  float* sL = reinterpret_cast<float*>(smem + SZ_A + SZ_B);
+  float* sA = reinterpret_cast<float*>(smem + SZ_A + SZ_B + SZ_C);
+  T* sAt = reinterpret_cast<T*>(smem + SZ_A + SZ_B);  // over L once the inverse is done
+  float* sX = reinterpret_cast<float*>(rB);
 
   const SeqTables& s = p.s;
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int u = xcd_remap(blockIdx.x, s.NTtot * p.Hv);
+  if (u >= s.NTtot * p.Hv) return;
+  const int c = u / p.Hv, h = u % p.Hv;
   int n, t0, len;
   if (!locate_chunk(s, c, n, t0, len)) return;
   const int hk = h / (p.Hv / p.Hq);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
 
+  TileRegs<T, CH, KD> rk;
+  TileRegs<T, CH, VD> rv;
+  rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+  rv.load((const T*)p.v + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, len);
   if (w == 0) {
     const float gv = (l < len) ? p.g[(long)(t0 + l) * p.Hv + h] : 0.f;
     const float bv = (l < len) ? p.beta[(long)(t0 + l) * p.Hv + h] : 0.f;
@@ -121,16 +136,15 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
       if (p.g_cum_out) p.g_cum_out[(long)(t0 + l) * p.Hv + h] = gc;
     }
   }
-  stage_rows<T, CH, KD, PK>(sK, (const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-  stage_rows<T, CH, VD, PV>(sV, (const T*)p.v + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, len);
+  rk.template store<PK>(rA);
   __syncthreads();
 
   // L = strict_lower(diag(b) (D * K K^T)); the diagonal of K K^T certifies
-  // 0 <= b |k|^2 <= 2 (non-expansive steps) for the CP warmup bound.
+  // 0 <= b |k|^2 <= 2 (non-expansive steps) for the context-parallel warmup.
   int bad = 0;
   for (int jt = 0; jt < 4; ++jt) {
     f32x4 a = zero4();
-    if (jt <= w) mma_tile<T, KD, PK, 1, 1, PK>(a, sK + 16 * w * PK, sK + 16 * jt * PK);
+    if (jt <= w) mma_tile<T, KD, PK, 1, 1, PK>(a, rA + 16 * w * PK, rA + 16 * jt * PK);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * w + acc_row(e), cc = 16 * jt + acc_col();
@@ -147,7 +161,6 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
   if (tid == 0) p.cert[(long)h * s.NTtot + c] = any_bad ? INFINITY : sG[len - 1];
 
   if (p.A_in) {
-    // A supplied by the caller (rows of valid tokens; identity beyond).
     for (int i = tid; i < CH * CH; i += NTHR) {
       const int r = i / CH, cc = i % CH;
       float a = (r == cc) ? 1.f : 0.f;
@@ -156,8 +169,8 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
     }
     __syncthreads();
   } else {
-    // Blocked inverse of the unit lower triangular I + L in fp32:
-    // diagonal 16x16 blocks by forward substitution (one wave each) ...
+    // Blocked inverse of the unit lower triangular I + L in fp32: diagonal
+    // 16x16 blocks by forward substitution (one wave each) ...
     if (l < 16) {
       float x[16];
 #pragma unroll
@@ -181,14 +194,15 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
     for (int d = 1; d < 4; ++d) {
       if (w + d < 4) {
         const int i = w + d, j = w;
+        float* X = sX + w * 16 * PX;
         f32x4 xacc = zero4();
         for (int m = j; m < i; ++m)
           mma_tile<float, 16, PL, 1, PL, 1>(xacc, sL + 16 * i * PL + 16 * m, sA + 16 * m * PL + 16 * j);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sX[w][acc_row(e) * PX + acc_col()] = xacc[e];
+        for (int e = 0; e < 4; ++e) X[acc_row(e) * PX + acc_col()] = xacc[e];
         wave_sync();
         f32x4 yacc = zero4();
-        mma_tile<float, 16, PL, 1, PX, 1>(yacc, sA + 16 * i * PL + 16 * i, sX[w]);
+        mma_tile<float, 16, PL, 1, PX, 1>(yacc, sA + 16 * i * PL + 16 * i, X);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sA[(16 * i + acc_row(e)) * PL + 16 * j + acc_col()] = -yacc[e];
       }
@@ -196,84 +210,81 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
     }
   }
 
-  // Export A, fold the row scales into K and V, round A for the MFMA.
+  // Export A; stage (b Gamma K)^T, (b V)^T and A in the working dtype.
   if (p.A_ws || p.A_out) {
-    for (int i = tid; i < len * CH; i += NTHR) {
-      const int r = i / CH, cc = i % CH;
-      const float a = sA[r * PL + cc];
-      if (p.A_ws) p.A_ws[((long)h * s.Ttot + t0 + r) * CH + cc] = a;
-      if (p.A_out) p.A_out[((long)(t0 + r) * p.Hv + h) * CH + cc] = a;
+    for (int i = tid; i < len * (CH / 4); i += NTHR) {
+      const int r = i / (CH / 4), cc = (i % (CH / 4)) * 4;
+      const float4 a = *reinterpret_cast<const float4*>(sA + r * PL + cc);
+      if (p.A_ws) *reinterpret_cast<float4*>(p.A_ws + ((long)h * s.Ttot + t0 + r) * CH + cc) = a;
+      if (p.A_out) *reinterpret_cast<float4*>(p.A_out + ((long)(t0 + r) * p.Hv + h) * CH + cc) = a;
     }
   }
-  for (int i = tid; i < CH * KD; i += NTHR) {
-    const int r = i / KD, cc = i % KD;
-    sK[r * PK + cc] = from_f<T>(to_f(sK[r * PK + cc]) * (sB[r] * __expf(sG[r])));
-  }
-  for (int i = tid; i < CH * VD; i += NTHR) {
-    const int r = i / VD, cc = i % VD;
-    sV[r * PV + cc] = from_f<T>(to_f(sV[r * PV + cc]) * sB[r]);
-  }
-  if constexpr (!F32) {
-    for (int i = tid; i < CH * CH; i += NTHR) {
-      const int r = i / CH, cc = i % CH;
-      sAt[r * PAT + cc] = from_f<T>(sA[r * PL + cc]);
+  rk.template store_t<PT>(rA, [&](int r) { return sB[r] * __expf(sG[r]); });
+  rv.template store_t<PT>(rB, [&](int r) { return sB[r]; });
+  if constexpr (F32) {
+    for (int i = tid; i < CH * CH; i += NTHR) sAt[(i / CH) * PT + i % CH] = sA[(i / CH) * PL + i % CH];
+  } else {
+    for (int i = tid; i < CH * CH / 4; i += NTHR) {
+      const int r = i / (CH / 4), cc = (i % (CH / 4)) * 4;
+      const float4 a = *reinterpret_cast<const float4*>(sA + r * PL + cc);
+      bf16x4 pk;
+      pk[0] = from_f<T>(a.x); pk[1] = from_f<T>(a.y); pk[2] = from_f<T>(a.z); pk[3] = from_f<T>(a.w);
+      *reinterpret_cast<bf16x4*>(sAt + r * PT + cc) = pk;
     }
   }
   __syncthreads();
 
-  constexpr int PA = F32 ? PL : PAT;
-  const T* Ap = F32 ? reinterpret_cast<const T*>(sA) : sAt;
-  {
-    f32x4 acc[KD / 16];
+  // W^T = (b Gamma K)^T A^T and U^T = (b V)^T A^T; A is lower triangular, so
+  // output column block j only contracts over tokens < 16 (j + 1).
+  constexpr int TILES = (KD / 16) * 4;
+  constexpr int TPW = TILES / NWAVE;
+  f32x4 wacc[TPW], uacc[TPW];
 #pragma unroll
-    for (int j = 0; j < KD / 16; ++j) acc[j] = zero4();
-    mma_row<T, CH, KD / 16, PA, 1, PK, 1>(acc, Ap + 16 * w * PA, sK, 16 * (w + 1));
-    T* Wg = (T*)p.W + ((long)h * s.Ttot + t0) * KD;
-#pragma unroll
-    for (int j = 0; j < KD / 16; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + acc_row(e);
-        if (r < len) Wg[(long)r * KD + 16 * j + acc_col()] = from_f<T>(acc[j][e]);
-      }
+  for (int i = 0; i < TPW; ++i) {
+    const int ti = w * TPW + i, rb = ti / 4, cb = ti % 4;
+    wacc[i] = zero4();
+    uacc[i] = zero4();
+    mma_tile<T, CH, PT, 1, 1, PT>(wacc[i], rA + 16 * rb * PT, sAt + 16 * cb * PT, 16 * (cb + 1));
+    mma_tile<T, CH, PT, 1, 1, PT>(uacc[i], rB + 16 * rb * PT, sAt + 16 * cb * PT, 16 * (cb + 1));
   }
-  {
-    f32x4 acc[VD / 16];
+  __syncthreads();
 #pragma unroll
-    for (int j = 0; j < VD / 16; ++j) acc[j] = zero4();
-    mma_row<T, CH, VD / 16, PA, 1, PV, 1>(acc, Ap + 16 * w * PA, sV, 16 * (w + 1));
-    T* Ug = (T*)p.U + ((long)h * s.Ttot + t0) * VD;
-#pragma unroll
-    for (int j = 0; j < VD / 16; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + acc_row(e);
-        if (r < len) Ug[(long)r * VD + 16 * j + acc_col()] = from_f<T>(acc[j][e]);
-      }
+  for (int i = 0; i < TPW; ++i) {
+    const int ti = w * TPW + i, rb = ti / 4, cb = ti % 4;
+    acc_store_t<T, PK>(rA, 16 * rb, 16 * cb, wacc[i]);
+    acc_store_t<T, PK>(rB, 16 * rb, 16 * cb, uacc[i]);
   }
+  __syncthreads();
+  store_rows<T, CH, KD, PK>((T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, rA, len);
+  store_rows<T, CH, VD, PK>((T*)p.U + ((long)h * s.Ttot + t0) * VD, VD, rB, len);
 }
 
 // --------------------------------------------------------------- k_state --
+// One workgroup per (sequence, value head, V block, CP segment), serial over
+// the segment's chunks.  h (K x BV) stays in fp32 MFMA accumulators; the next
+// chunk's W, K, U rows are fetched into registers while the current one runs.
 template <typename T, int KD, int BV>
-__global__ __launch_bounds__(NTHR) void k_state(StateParams p) {
+__global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) {
   constexpr int VD = KD;
   constexpr int PK = Pitch<T, KD>::value;
   constexpr int PU = Pitch<T, BV>::value;
-  constexpr int PVT = Pitch<T, CH>::value;
+  constexpr int PT = Pitch<T, CH>::value;
   constexpr int NCB = BV / 16;
   constexpr int NTILE = (KD / 16) * NCB;
   constexpr int TPW = NTILE / NWAVE;
   static_assert(NTILE % NWAVE == 0, "state tiles must split evenly over the waves");
   __shared__ __align__(16) T sW[CH * PK];
-  __shared__ __align__(16) T sK[CH * PK];
+  __shared__ __align__(16) T sKdT[KD * PT];
   __shared__ __align__(16) T sU[CH * PU];
   __shared__ __align__(16) T shT[BV * PK];
-  __shared__ __align__(16) T sVt[BV * PVT];
-  __shared__ float sDec[CH];
+  __shared__ __align__(16) T sVt[BV * PT];
 
   const SeqTables& s = p.s;
-  const int h = blockIdx.y / p.nvb, vb = blockIdx.y % p.nvb;
-  const int item = blockIdx.x;
+  const int u = xcd_remap(blockIdx.x, total_items);
+  if (u >= total_items) return;
+  const int vb = u % p.nvb;
+  const int h = (u / p.nvb) % p.Hv;
+  const int item = u / (p.nvb * p.Hv);
   const int n = find_seq(s.seg_off, s.N, item);
   const int pseg = item - s.seg_off[n];
   const int nseg = s.seg_off[n + 1] - s.seg_off[n];
@@ -319,58 +330,80 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p) {
     }
   }
 
+  TileRegs<T, CH, KD> rw, rk;
+  TileRegs<T, CH, BV> ru;
+  float gam[TileRegs<T, CH, KD>::NV];
+  float glast_next = 0.f;
+  auto prefetch = [&](int jc) {
+    const int t0 = s.cu[n] + jc * CH;
+    const int len = min(CH, s.cu[n + 1] - t0);
+    rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
+    rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    ru.load((const T*)p.U + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, len);
+    const float* gc = p.gcum + (long)h * s.Ttot + t0;
+#pragma unroll
+    for (int i = 0; i < TileRegs<T, CH, KD>::NV; ++i) {
+      const int r = rk.row(i);
+      gam[i] = (r < len) ? gc[r] : 0.f;
+    }
+    glast_next = gc[len - 1];
+  };
+  if (cstart < cend) prefetch(cstart);
+
   for (int jc = cstart; jc < cend; ++jc) {
     const int gc = c0 + jc;
     const int t0 = s.cu[n] + jc * CH;
     const int len = min(CH, s.cu[n + 1] - t0);
-    if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) break;
     const bool warm = jc < cbeg;
-    stage_rows<T, CH, KD, PK>(sW, (const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
-    stage_rows<T, CH, KD, PK>(sK, (const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-    stage_rows<T, CH, BV, PU>(sU, (const T*)p.U + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, len);
-    const float glast = p.gcum[(long)h * s.Ttot + t0 + len - 1];
-    if (threadIdx.x < CH) {
-      const int r = threadIdx.x;
-      sDec[r] = (r < len) ? __expf(glast - p.gcum[(long)h * s.Ttot + t0 + r]) : 0.f;
+    const float glast = glast_next;
+    rw.template store<PK>(sW);
+    ru.template store<PU>(sU);
+    {
+      float dec[TileRegs<T, CH, KD>::NV];
+#pragma unroll
+      for (int i = 0; i < TileRegs<T, CH, KD>::NV; ++i) dec[i] = (rk.row(i) < len) ? __expf(glast - gam[i]) : 0.f;
+      // transposed, decayed K: sKdT[d][t] = e^{gamma_n - gamma_t} k_t[d]
+#pragma unroll
+      for (int i = 0; i < TileRegs<T, CH, KD>::NV; ++i) {
+        const int idx = (int)threadIdx.x + i * NTHR;
+        const int r = idx / TileRegs<T, CH, KD>::VPR, cc = (idx % TileRegs<T, CH, KD>::VPR) * TileRegs<T, CH, KD>::VEC;
+        const T* e = reinterpret_cast<const T*>(&rk.v[i]);
+#pragma unroll
+        for (int j = 0; j < TileRegs<T, CH, KD>::VEC; ++j) sKdT[(cc + j) * PT + r] = from_f<T>(to_f(e[j]) * dec[i]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 16 * rb + acc_row(e), vl = 16 * cb + acc_col();
-        const T hv = from_f<T>(hacc[i][e]);
-        shT[vl * PK + d] = hv;
-        if (!warm && p.hbuf)
-          ((T*)p.hbuf)[(((long)h * s.NTtot + gc) * VD + vb * BV + vl) * KD + d] = hv;
-      }
+      acc_store_t<T, PK>(shT, 16 * rb, 16 * cb, hacc[i]);
     }
     __syncthreads();
+    if (jc + 1 < cend) prefetch(jc + 1);
+    if (!warm && p.hbuf)
+      store_rows<T, BV, KD, PK>((T*)p.hbuf + (((long)h * s.NTtot + gc) * VD + vb * BV) * KD, KD, shT, BV);
 
-    {  // Vnew = U - W h ; stage diag(e^{gamma_n - gamma}) Vnew transposed
+    {  // Vnew = U - W h, staged transposed (tokens contiguous)
       f32x4 acc[NCB];
 #pragma unroll
       for (int j = 0; j < NCB; ++j) acc[j] = zero4();
       mma_row<T, KD, NCB, PK, 1, 1, PK>(acc, sW + 16 * w * PK, shT);
 #pragma unroll
-      for (int j = 0; j < NCB; ++j)
+      for (int j = 0; j < NCB; ++j) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * w + acc_row(e), vl = 16 * j + acc_col();
-          const float vn = to_f(sU[r * PU + vl]) - acc[j][e];
-          if (!warm && r < len)
-            ((T*)p.vnew)[((long)h * s.Ttot + t0 + r) * VD + vb * BV + vl] = from_f<T>(vn);
-          sVt[vl * PVT + r] = from_f<T>(vn * sDec[r]);
-        }
+        for (int e = 0; e < 4; ++e) acc[j][e] = to_f(sU[(16 * w + acc_row(e)) * PU + 16 * j + acc_col()]) - acc[j][e];
+        acc_store_t<T, PT>(sVt, 16 * w, 16 * j, acc[j]);
+      }
     }
     __syncthreads();
+    if (!warm)
+      store_rows<T, BV, CH, PT>((T*)p.vnew + (((long)h * s.NTtot + gc) * VD + vb * BV) * CH, CH, sVt, BV);
 
     const float dlast = __expf(glast);
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
       hacc[i] *= dlast;
-      mma_tile<T, CH, 1, PK, 1, PVT>(hacc[i], sK + 16 * rb, sVt + 16 * cb * PVT);
+      mma_tile<T, CH, PT, 1, 1, PT>(hacc[i], sKdT + 16 * rb * PT, sVt + 16 * cb * PT);
     }
     __syncthreads();
   }
@@ -389,64 +422,81 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p) {
 }
 
 // -------------------------------------------------------------- k_output --
-template <typename T, int KD>
-__global__ __launch_bounds__(NTHR) void k_output(OutputParams p) {
+// One workgroup per (chunk, value head, V block of BV columns).
+template <typename T, int KD, int BV>
+__global__ __launch_bounds__(NTHR) void k_output(OutputParams p, int nvb) {
   constexpr int VD = KD;
   constexpr int PK = Pitch<T, KD>::value;
-  constexpr int PV = Pitch<T, VD>::value;
-  constexpr int PP = Pitch<T, CH>::value;
+  constexpr int PT = Pitch<T, CH>::value;
+  constexpr int PO = Pitch<T, BV>::value;
+  constexpr int NCB = BV / 16;
   __shared__ __align__(16) T sQ[CH * PK];
-  __shared__ __align__(16) T sK[CH * PK];
-  __shared__ __align__(16) T shT[VD * PK];
-  __shared__ __align__(16) T sVn[CH * PV];
-  __shared__ __align__(16) T sP[CH * PP];
+  __shared__ __align__(16) T sK[CH * PK];   // reused as the O staging tile
+  __shared__ __align__(16) T shT[BV * PK];
+  __shared__ __align__(16) T sVnT[BV * PT];
+  __shared__ __align__(16) T sP[CH * PT];
   __shared__ float sG[CH];
 
   const SeqTables& s = p.s;
-  const int c = blockIdx.x, h = blockIdx.y;
+  const int total = s.NTtot * p.Hv * nvb;
+  const int u = xcd_remap(blockIdx.x, total);
+  if (u >= total) return;
+  const int vb = u % nvb, h = (u / nvb) % p.Hv, c = u / (nvb * p.Hv);
   int n, t0, len;
   if (!locate_chunk(s, c, n, t0, len)) return;
   const int hk = h / (p.Hv / p.Hq);
   const int w = wave_id();
 
-  stage_rows<T, CH, KD, PK>(sQ, (const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-  stage_rows<T, CH, KD, PK>(sK, (const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-  stage_rows<T, VD, KD, PK>(shT, (const T*)p.hbuf + ((long)h * s.NTtot + c) * VD * KD, KD, VD);
-  stage_rows<T, CH, VD, PV>(sVn, (const T*)p.vnew + ((long)h * s.Ttot + t0) * VD, VD, len);
-  if (threadIdx.x < CH) sG[threadIdx.x] = p.gcum[(long)h * s.Ttot + t0 + min((int)threadIdx.x, len - 1)];
-  __syncthreads();
-
-  for (int jt = 0; jt < 4; ++jt) {  // P = lower(D * Q K^T), diagonal included
-    f32x4 a = zero4();
-    if (jt <= w) mma_tile<T, KD, PK, 1, 1, PK>(a, sQ + 16 * w * PK, sK + 16 * jt * PK);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + acc_row(e), cc = 16 * jt + acc_col();
-      const float pv = (r >= cc) ? __expf(sG[r] - sG[cc]) * a[e] : 0.f;
-      sP[r * PP + cc] = from_f<T>(pv);
-    }
+  {
+    TileRegs<T, CH, KD> rq, rk;
+    TileRegs<T, BV, KD> rh;
+    TileRegs<T, BV, CH> rvn;
+    rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    rh.load((const T*)p.hbuf + (((long)h * s.NTtot + c) * VD + vb * BV) * KD, KD, BV);
+    rvn.load((const T*)p.vnew + (((long)h * s.NTtot + c) * VD + vb * BV) * CH, CH, BV);
+    if (threadIdx.x < CH) sG[threadIdx.x] = p.gcum[(long)h * s.Ttot + t0 + min((int)threadIdx.x, len - 1)];
+    rq.template store<PK>(sQ);
+    rk.template store<PK>(sK);
+    rh.template store<PK>(shT);
+    rvn.template store<PT>(sVnT);
   }
   __syncthreads();
 
-  f32x4 acc[VD / 16];
+  // P = lower(D * Q K^T) (diagonal included), formed as P^T = K Q^T so that
+  // each lane writes four consecutive key positions of one row of P.
+  for (int j = 0; j < 4; ++j) {
+    f32x4 a = zero4();
+    if (j >= w) {
+      mma_tile<T, KD, PK, 1, 1, PK>(a, sK + 16 * w * PK, sQ + 16 * j * PK);
 #pragma unroll
-  for (int j = 0; j < VD / 16; ++j) acc[j] = zero4();
-  mma_row<T, KD, VD / 16, PK, 1, 1, PK>(acc, sQ + 16 * w * PK, shT);
+      for (int e = 0; e < 4; ++e) {
+        const int sidx = 16 * w + acc_row(e), t = 16 * j + acc_col();
+        a[e] = (t >= sidx) ? __expf(sG[t] - sG[sidx]) * a[e] : 0.f;
+      }
+    }
+    acc_store_t<T, PT>(sP, 16 * w, 16 * j, a);
+  }
+  __syncthreads();
+
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) acc[j] = zero4();
+  mma_row<T, KD, NCB, PK, 1, 1, PK>(acc, sQ + 16 * w * PK, shT);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float gm = __expf(sG[16 * w + acc_row(e)]);
 #pragma unroll
-    for (int j = 0; j < VD / 16; ++j) acc[j][e] *= gm;
+    for (int j = 0; j < NCB; ++j) acc[j][e] *= gm;
   }
-  mma_row<T, CH, VD / 16, PP, 1, PV, 1>(acc, sP + 16 * w * PP, sVn, 16 * (w + 1));
-  T* og = (T*)p.o;
+  mma_row<T, CH, NCB, PT, 1, 1, PT>(acc, sP + 16 * w * PT, sVnT, 16 * (w + 1));
+  T* sO = sK;
 #pragma unroll
-  for (int j = 0; j < VD / 16; ++j)
+  for (int j = 0; j < NCB; ++j)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + acc_row(e);
-      if (r < len) og[((long)(t0 + r) * p.Hv + h) * VD + 16 * j + acc_col()] = from_f<T>(p.scale * acc[j][e]);
-    }
+    for (int e = 0; e < 4; ++e) sO[(16 * w + acc_row(e)) * PO + 16 * j + acc_col()] = from_f<T>(p.scale * acc[j][e]);
+  __syncthreads();
+  store_rows<T, CH, BV, PO>((T*)p.o + ((long)t0 * p.Hv + h) * VD + vb * BV, (long)p.Hv * VD, sO, len);
 }
 
 // ------------------------------------------------------------- launchers --
@@ -466,24 +516,29 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t st) {
   return err;
 }
 
+static unsigned padded_grid(long total) { return (unsigned)(((total + 7) / 8) * 8); }
+
 template <typename T, int KD>
 static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
   hipError_t err;
-  GDR_LAUNCH("intra_wy", (k_intra<T, KD>), dim3(p.s.NTtot, p.Hv), st, p);
+  GDR_LAUNCH("intra_wy", (k_intra<T, KD>), dim3(padded_grid((long)p.s.NTtot * p.Hv)), st, p);
   return err;
 }
 
 template <typename T, int KD, int BV>
 static hipError_t state_impl(const StateParams& p, int total_segs, hipStream_t st) {
   hipError_t err;
-  GDR_LAUNCH("chunk_state", (k_state<T, KD, BV>), dim3(total_segs, p.Hv * p.nvb), st, p);
+  const int total = total_segs * p.Hv * p.nvb;
+  GDR_LAUNCH("chunk_state", (k_state<T, KD, BV>), dim3(padded_grid(total)), st, p, total);
   return err;
 }
 
 template <typename T, int KD>
 static hipError_t output_impl(const OutputParams& p, hipStream_t st) {
   hipError_t err;
-  GDR_LAUNCH("chunk_output", (k_output<T, KD>), dim3(p.s.NTtot, p.Hv), st, p);
+  constexpr int BV = KD == 128 ? 64 : KD;
+  const int nvb = KD / BV;
+  GDR_LAUNCH("chunk_output", (k_output<T, KD, BV>), dim3(padded_grid((long)p.s.NTtot * p.Hv * nvb)), st, p, nvb);
   return err;
 }
 

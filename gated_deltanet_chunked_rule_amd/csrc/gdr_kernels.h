@@ -5,7 +5,7 @@
 //   gcum  fp32 [Hv][Ttot]          chunk-local inclusive cumsum of g
 //   cert  fp32 [Hv][NTtot]         chunk gate sum, +inf if some beta|k|^2 is outside [0, 2]
 //   W, U  T    [Hv][Ttot][K|V]     W = A diag(beta*Gamma) K,  U = A diag(beta) V
-//   vnew  T    [Hv][Ttot][V]       Vnew = U - W h (the chunk's corrected values)
+//   vnew  T    [Hv][NTtot][V][64]  Vnew = U - W h per chunk, stored transposed
 //   hbuf  T    [Hv][NTtot][V][K]   state entering each chunk, stored transposed
 //   A     fp32 [Hv][Ttot][64]      rows of the chunk's A (backward only)
 //   dhbuf T    [Hv][NTtot][V][K]   state gradient leaving each chunk (transposed)
