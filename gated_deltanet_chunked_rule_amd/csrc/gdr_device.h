@@ -179,6 +179,47 @@ struct TileRegs {
   }
 };
 
+// A 64-row tile (rows = tokens) loaded with lane l of every wave on row l and
+// the waves splitting the 16-byte column groups.  Its transposed store then
+// has consecutive lanes writing consecutive LDS addresses (no bank
+// conflicts), and the row store writes one 16-byte group per lane.
+template <typename T, int D>
+struct TileCols {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int NCG = D / VEC;
+  static constexpr int NV = NCG / NWAVE;
+  static_assert(NCG % NWAVE == 0, "column groups must split evenly over the waves");
+  uint4 v[NV];
+  __device__ __forceinline__ void load(const T* g, long gstride, int nrows) {
+    const int r = lane_id();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int cg = wave_id() + NWAVE * i;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < nrows) v[i] = *reinterpret_cast<const uint4*>(g + (long)r * gstride + cg * VEC);
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ void store(T* lds) const {
+    const int r = lane_id();
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      *reinterpret_cast<uint4*>(lds + r * P + (wave_id() + NWAVE * i) * VEC) = v[i];
+  }
+  // lds[c * PT + r] = s * tile(r, c), s the scale of this lane's row.
+  template <int PT>
+  __device__ __forceinline__ void store_t(T* lds, float s) const {
+    const int r = lane_id();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c0 = (wave_id() + NWAVE * i) * VEC;
+      const T* e = reinterpret_cast<const T*>(&v[i]);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) lds[(c0 + j) * PT + r] = from_f<T>(to_f(e[j]) * s);
+    }
+  }
+};
+
 // LDS rows [0, nrows) of an R x D tile (pitch P) -> global (row stride gstride),
 // 16-byte accesses.
 template <typename T, int R, int D, int P>

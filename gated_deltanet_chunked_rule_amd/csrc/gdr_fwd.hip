@@ -121,8 +121,8 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
   const int hk = h / (p.Hv / p.Hq);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
 
-  TileRegs<T, CH, KD> rk;
-  TileRegs<T, CH, VD> rv;
+  TileCols<T, KD> rk;
+  TileCols<T, VD> rv;
   rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
   rv.load((const T*)p.v + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, len);
   if (w == 0) {
@@ -219,8 +219,8 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
       if (p.A_out) *reinterpret_cast<float4*>(p.A_out + ((long)(t0 + r) * p.Hv + h) * CH + cc) = a;
     }
   }
-  rk.template store_t<PT>(rA, [&](int r) { return sB[r] * __expf(sG[r]); });
-  rv.template store_t<PT>(rB, [&](int r) { return sB[r]; });
+  rk.template store_t<PT>(rA, sB[l] * __expf(sG[l]));
+  rv.template store_t<PT>(rB, sB[l]);
   if constexpr (F32) {
     for (int i = tid; i < CH * CH; i += NTHR) sAt[(i / CH) * PT + i % CH] = sA[(i / CH) * PL + i % CH];
   } else {
@@ -330,9 +330,10 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
     }
   }
 
-  TileRegs<T, CH, KD> rw, rk;
+  TileRegs<T, CH, KD> rw;
+  TileCols<T, KD> rk;
   TileRegs<T, CH, BV> ru;
-  float gam[TileRegs<T, CH, KD>::NV];
+  float gam = 0.f;
   float glast_next = 0.f;
   auto prefetch = [&](int jc) {
     const int t0 = s.cu[n] + jc * CH;
@@ -341,11 +342,7 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
     rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
     ru.load((const T*)p.U + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, len);
     const float* gc = p.gcum + (long)h * s.Ttot + t0;
-#pragma unroll
-    for (int i = 0; i < TileRegs<T, CH, KD>::NV; ++i) {
-      const int r = rk.row(i);
-      gam[i] = (r < len) ? gc[r] : 0.f;
-    }
+    gam = (lane_id() < len) ? gc[lane_id()] : 0.f;
     glast_next = gc[len - 1];
   };
   if (cstart < cend) prefetch(cstart);
@@ -358,20 +355,8 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
     const float glast = glast_next;
     rw.template store<PK>(sW);
     ru.template store<PU>(sU);
-    {
-      float dec[TileRegs<T, CH, KD>::NV];
-#pragma unroll
-      for (int i = 0; i < TileRegs<T, CH, KD>::NV; ++i) dec[i] = (rk.row(i) < len) ? __expf(glast - gam[i]) : 0.f;
-      // transposed, decayed K: sKdT[d][t] = e^{gamma_n - gamma_t} k_t[d]
-#pragma unroll
-      for (int i = 0; i < TileRegs<T, CH, KD>::NV; ++i) {
-        const int idx = (int)threadIdx.x + i * NTHR;
-        const int r = idx / TileRegs<T, CH, KD>::VPR, cc = (idx % TileRegs<T, CH, KD>::VPR) * TileRegs<T, CH, KD>::VEC;
-        const T* e = reinterpret_cast<const T*>(&rk.v[i]);
-#pragma unroll
-        for (int j = 0; j < TileRegs<T, CH, KD>::VEC; ++j) sKdT[(cc + j) * PT + r] = from_f<T>(to_f(e[j]) * dec[i]);
-      }
-    }
+    // transposed, decayed K: sKdT[d][t] = e^{gamma_n - gamma_t} k_t[d]
+    rk.template store_t<PT>(sKdT, (lane_id() < len) ? __expf(glast - gam) : 0.f);
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
