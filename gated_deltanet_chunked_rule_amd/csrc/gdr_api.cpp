@@ -208,7 +208,7 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
                              const void* k, const void* v, const float* g, const float* beta,
                              float scale, const float* h0, const int32_t* cu_dev, void* o,
                              float* ht, float* g_cum_out, float* A_out, float* A_ws,
-                             const float* A_in, int L, hipStream_t st) {
+                             const float* A_in, int L, bool bwd, hipStream_t st) {
   hipError_t e;
   gdr::PlanParams pp;
   pp.cu_in = cu_dev;
@@ -239,7 +239,7 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
   sp.nvb = P.nvb;
   int segs = 0;
   for (int c : P.chunks) segs += std::max(1, (c + L - 1) / L);
-  if ((e = gdr::launch_state(P.dt, P.K, P.BV, sp, segs, st)) != hipSuccess) return hip_fail(e, "state launch");
+  if ((e = gdr::launch_state(P.dt, P.K, P.BV, sp, segs, bwd, st)) != hipSuccess) return hip_fail(e, "state launch");
   if (o && P.NTtot > 0) {
     gdr::OutputParams op;
     op.s = s; op.q = q; op.k = k; op.hbuf = ws + Lo.hbuf; op.vnew = ws + Lo.vnew;
@@ -267,6 +267,10 @@ size_t gdr_chunk_bwd_workspace_size(const gdr_shape* shape, const gdr_options* o
                                     const int32_t* cu_seqlens_host) {
   Problem P;
   if (analyze(shape, opts, cu_seqlens_host, cu_seqlens_host != nullptr, P) != GDR_OK) return 0;
+  if (P.dt == gdr::DType::F32 && P.K > 32) {
+    fail(GDR_ERR_UNSUPPORTED, "fp32 backward supports K == 32");
+    return 0;
+  }
   return layout(P, true).total;
 }
 
@@ -309,7 +313,7 @@ gdr_status gdr_chunk_fwd(const gdr_shape* shape, const gdr_options* opts, const 
     return fail(GDR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(Lo.total) + " bytes");
   char* ws = static_cast<char*>(workspace);
   return run_forward_chain(P, Lo, ws, q, k, v, g, beta, scale, initial_state, cu_seqlens, o,
-                           final_state, g_cum_out, A_out, nullptr, nullptr, P.L,
+                           final_state, g_cum_out, A_out, nullptr, nullptr, P.L, false,
                            static_cast<hipStream_t>(stream));
 }
 
@@ -325,6 +329,7 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
   Problem P;
   gdr_status st = analyze(shape, opts, cu_seqlens_host, cu_seqlens != nullptr, P);
   if (st != GDR_OK) return st;
+  if (P.dt == gdr::DType::F32 && P.K > 32) return fail(GDR_ERR_UNSUPPORTED, "fp32 backward supports K == 32");
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(GDR_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (P.Ttot > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dbeta || !dg))
     return fail(GDR_ERR_INVALID_ARG, "q, k, v, g, beta, d_o, dq, dk, dv, dbeta and dg must be non-NULL");
@@ -341,7 +346,7 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
   // the backward: the reverse pass needs every chunk's exact state).
   const int Lfull = std::max(P.NTmax, 1);
   st = run_forward_chain(P, Lo, ws, q, k, v, g, beta, scale, initial_state, cu_seqlens, nullptr,
-                         nullptr, nullptr, nullptr, reinterpret_cast<float*>(ws + Lo.A), A, Lfull, hs);
+                         nullptr, nullptr, nullptr, reinterpret_cast<float*>(ws + Lo.A), A, Lfull, true, hs);
   if (st != GDR_OK) return st;
   if (P.NTtot == 0 && !dh0) return GDR_OK;
   const gdr::SeqTables s = tables(P, Lo, ws);
@@ -351,7 +356,8 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
   dp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
   dp.dht = dht; dp.dh0 = dh0; dp.dhbuf = ws + Lo.dhbuf; dp.dvn = ws + Lo.dvn;
   dp.Hq = P.Hq; dp.Hv = P.Hv; dp.scale = scale; dp.nvb = P.nvb;
-  if ((e = gdr::launch_dstate(P.dt, P.K, P.BV, dp, hs)) != hipSuccess) return hip_fail(e, "dstate launch");
+  if ((e = gdr::launch_dstate(P.dt, P.K, P.BV, dp, P.N * P.Hv * P.nvb, hs)) != hipSuccess)
+    return hip_fail(e, "dstate launch");
   if (P.NTtot > 0) {
     gdr::GradParams gp;
     gp.s = s; gp.q = q; gp.k = k; gp.v = v; gp.d_o = d_o; gp.hbuf = ws + Lo.hbuf;

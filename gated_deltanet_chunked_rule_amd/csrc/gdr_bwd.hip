@@ -1,8 +1,658 @@
-// gdr_bwd.hip -- backward kernels (placeholder until the reverse pass lands).
+// gdr_bwd.hip -- backward kernels of the chunked gated delta rule on gfx950.
+//
+// The backward takes q, k, v, g, beta, (A), do, dht, scale, initial_state and
+// returns dq, dk, dv, dbeta, dg, dh0 (FlashQLA curated summary, section
+// "使用方式與需求", low-level backward listing); the chunk states are not an
+// input, so they are recomputed.  The pages call the backward the hardest part
+// of the method, built there as a warp-specialised pipeline under tight
+// on-chip memory (same page, section "後向傳播挑戰與warp專屬管線"); here it is
+// three passes:
+//   1. recompute (forward kernels): g_cum, A, W, U, every chunk's entry state
+//      h and Vnew = U - W h;
+//   2. k_dstate, serial in reverse over chunks per (sequence, value head,
+//      V block): with dh+ the gradient of the state leaving a chunk,
+//        dVnew = s P^T dO + diag(e^{gamma_n - gamma}) K dh+
+//        dh    = Gamma_n dh+ + s (diag(Gamma) Q)^T dO - W^T dVnew
+//      (P = lower(D * Q K^T)); it stores dh+ and dVnew per chunk and dh0;
+//   3. k_grads, fully parallel per (chunk, query/key head), looping over the
+//      value heads of the group so dq and dk are summed without atomics:
+//        dP = s lower(dO Vnew^T),  dQ = dP*D K + s diag(Gamma) dO h^T
+//        dW = -dVnew h^T,  dA = lower_strict(dW (b Gamma K)^T + dVnew (b V)^T)
+//        dKb = A^T dW,  dVb = A^T dVnew,  dL = lower_strict(-A^T dA A^T)
+//        dK = (dP*D)^T Q + (E + E^T) K + diag(b Gamma) dKb
+//             + diag(e^{gamma_n - gamma}) Vnew dh+^T,   E = dL * diag(b) D
+//        dV = diag(b) dVb,  dbeta and dgamma from the same terms,
+//        dg = reverse cumulative sum of dgamma over the chunk.
+#include <math.h>
+#include <type_traits>
+
 #include "gdr_device.h"
 #include "gdr_kernels.h"
 
 namespace gdr {
-hipError_t launch_dstate(DType, int, int, const DStateParams&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_grads(DType, int, const GradParams&, hipStream_t) { return hipErrorNotSupported; }
+
+__device__ __forceinline__ bool locate_chunk_b(const SeqTables& s, int c, int& n, int& t0, int& len) {
+  if (c >= s.NTtot) return false;
+  n = find_seq(s.chunk_off, s.N, c);
+  t0 = s.cu[n] + (c - s.chunk_off[n]) * CH;
+  len = min(CH, s.cu[n + 1] - t0);
+  return len > 0 && t0 >= 0 && (long)t0 + len <= s.Ttot;
+}
+
+// Sum over the 16 lanes that share a row of an accumulator tile (lanes with
+// equal lane/16); every lane of the group receives the sum.
+__device__ __forceinline__ float row_group_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Sum over the four lane groups that share a column (lane % 16).
+__device__ __forceinline__ float col_group_sum(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// -------------------------------------------------------------- k_dstate --
+template <typename T, int KD, int BV>
+__global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items) {
+  constexpr int VD = KD;
+  constexpr int PK = Pitch<T, KD>::value;
+  constexpr int PT = Pitch<T, CH>::value;
+  constexpr int PU = Pitch<T, BV>::value;
+  constexpr int NCB = BV / 16;
+  constexpr int NTILE = (KD / 16) * NCB;
+  constexpr int TPW = NTILE / NWAVE;
+  static_assert(NTILE % NWAVE == 0, "state tiles must split evenly over the waves");
+  __shared__ __align__(16) T sQ[CH * PK];
+  __shared__ __align__(16) T sK[CH * PK];
+  __shared__ __align__(16) T sQgT[KD * PT];   // s Gamma_t q_t[d]  as [d][t]
+  __shared__ __align__(16) T sWnT[KD * PT];   // -W[t][d]          as [d][t]
+  __shared__ __align__(16) T sdOT[BV * PT];   // dO[t][v]          as [v][t]
+  __shared__ __align__(16) T sPt[CH * PT];    // s P[t][s]         as [s][t]
+  __shared__ __align__(16) T sdhT[BV * PK];   // dh+[d][v]         as [v][d]
+  __shared__ __align__(16) T sdVT[BV * PT];   // dVnew[t][v]       as [v][t]
+  __shared__ __align__(16) T sdVr[CH * PU];   // dVnew rows (global store staging)
+  __shared__ __align__(16) T sdhr[KD * PU];   // dh+ rows   (global store staging)
+  __shared__ float sG[CH];
+
+  const SeqTables& s = p.s;
+  const int u = xcd_remap(blockIdx.x, total_items);
+  if (u >= total_items) return;
+  const int vb = u % p.nvb;
+  const int h = (u / p.nvb) % p.Hv;
+  const int n = u / (p.nvb * p.Hv);
+  if (n >= s.N) return;
+  const int c0 = s.chunk_off[n];
+  const int nch = s.chunk_off[n + 1] - c0;
+  if (c0 < 0 || nch < 0 || c0 + nch > s.NTtot) return;
+  const int hk = h / (p.Hv / p.Hq);
+  const int w = wave_id(), l = lane_id();
+
+  f32x4 hacc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 16 * rb + acc_row(e), v = vb * BV + 16 * cb + acc_col();
+      hacc[i][e] = p.dht ? p.dht[(((long)n * p.Hv + h) * KD + d) * VD + v] : 0.f;
+    }
+  }
+
+  TileCols<T, KD> rq, rk, rw;
+  TileCols<T, BV> rdo;
+  float gam_next = 0.f, glast_next = 0.f;
+  auto prefetch = [&](int jc) {
+    const int t0 = s.cu[n] + jc * CH;
+    const int len = min(CH, s.cu[n + 1] - t0);
+    rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
+    rdo.load((const T*)p.d_o + ((long)t0 * p.Hv + h) * VD + vb * BV, (long)p.Hv * VD, len);
+    const float* gc = p.gcum + (long)h * s.Ttot + t0;
+    glast_next = gc[len - 1];
+    gam_next = (l < len) ? gc[l] : glast_next;
+  };
+  if (nch > 0) prefetch(nch - 1);
+
+  for (int jc = nch - 1; jc >= 0; --jc) {
+    const int gc = c0 + jc;
+    const int t0 = s.cu[n] + jc * CH;
+    const int len = min(CH, s.cu[n + 1] - t0);
+    if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) break;
+    const float glast = glast_next, gam = gam_next;
+    rq.template store<PK>(sQ);
+    rk.template store<PK>(sK);
+    rq.template store_t<PT>(sQgT, (l < len) ? p.scale * __expf(gam) : 0.f);
+    rw.template store_t<PT>(sWnT, -1.f);
+    rdo.template store_t<PT>(sdOT, 1.f);
+    if (w == 0) sG[l] = gam;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
+      acc_store_t<T, PK>(sdhT, 16 * rb, 16 * cb, hacc[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sdhr[(16 * rb + acc_row(e)) * PU + 16 * cb + acc_col()] = from_f<T>(hacc[i][e]);
+    }
+    __syncthreads();
+    if (jc > 0) prefetch(jc - 1);
+    store_rows<T, KD, BV, PU>((T*)p.dhbuf + ((long)h * s.NTtot + gc) * KD * VD + vb * BV, VD, sdhr, KD);
+
+    // s P^T as [s][t]: tiles of P = lower(D * Q K^T) with t-block w.
+    for (int j = 0; j < 4; ++j) {
+      f32x4 a = zero4();
+      if (j <= w) {
+        mma_tile<T, KD, PK, 1, 1, PK>(a, sQ + 16 * w * PK, sK + 16 * j * PK);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * w + acc_row(e), sidx = 16 * j + acc_col();
+          a[e] = (t >= sidx) ? p.scale * __expf(sG[t] - sG[sidx]) * a[e] : 0.f;
+        }
+      }
+      acc_store_t<T, PT>(sPt, 16 * w, 16 * j, a);
+    }
+    __syncthreads();
+
+    {  // dVnew rows of block w
+      f32x4 acc[NCB];
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) acc[j] = zero4();
+      mma_row<T, KD, NCB, PK, 1, 1, PK>(acc, sK + 16 * w * PK, sdhT);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + acc_row(e);
+        const float dec = (r < len) ? __expf(glast - sG[r]) : 0.f;
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) acc[j][e] *= dec;
+      }
+      mma_row<T, CH, NCB, PT, 1, 1, PT>(acc, sPt + 16 * w * PT, sdOT);
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) {
+        acc_store_t<T, PT>(sdVT, 16 * w, 16 * j, acc[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sdVr[(16 * w + acc_row(e)) * PU + 16 * j + acc_col()] = from_f<T>(acc[j][e]);
+      }
+    }
+    __syncthreads();
+    store_rows<T, CH, BV, PU>((T*)p.dvn + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, sdVr, len);
+
+    const float gl = __expf(glast);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
+      hacc[i] *= gl;
+      mma_tile<T, CH, PT, 1, 1, PT>(hacc[i], sQgT + 16 * rb * PT, sdOT + 16 * cb * PT);
+      mma_tile<T, CH, PT, 1, 1, PT>(hacc[i], sWnT + 16 * rb * PT, sdVT + 16 * cb * PT);
+    }
+    __syncthreads();
+  }
+
+  if (p.dh0) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 16 * rb + acc_row(e), v = vb * BV + 16 * cb + acc_col();
+        p.dh0[(((long)n * p.Hv + h) * KD + d) * VD + v] = hacc[i][e];
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- k_grads --
+// LDS: permanent K rows, K^T and Q^T; three 64-row regions R1..R3 and four
+// 64x64 tiles S0..S3 whose contents change phase by phase (see comments).
+template <typename T, int KD>
+__global__ __launch_bounds__(NTHR) void k_grads(GradParams p) {
+  constexpr int VD = KD;
+  constexpr int PK = Pitch<T, KD>::value;
+  constexpr int PT = Pitch<T, CH>::value;
+  constexpr int PL = 68;
+  constexpr int NKT = KD / 16;
+  constexpr int NVT = VD / 16;
+  constexpr int SZ_R = ((CH * PK > KD * PT ? CH * PK : KD * PT) * (int)sizeof(T) > CH * PL * 4)
+                           ? (CH * PK > KD * PT ? CH * PK : KD * PT) * (int)sizeof(T)
+                           : CH * PL * 4;
+  constexpr int SZ_S = CH * PT * (int)sizeof(T);
+  static_assert(2 * SZ_S >= CH * PK * (int)sizeof(T), "S2+S3 must hold 64 value rows");
+  __shared__ __align__(16) T sK[CH * PK];
+  __shared__ __align__(16) T sKT[KD * PT];
+  __shared__ __align__(16) T sQT[KD * PT];
+  __shared__ __align__(16) char rbuf[3 * SZ_R + 4 * SZ_S];
+  __shared__ float sG[CH], sB[CH], sGm[CH], sDec[CH], sdg[CH], sdb[CH];
+  __shared__ float colp[NWAVE][CH];
+  __shared__ float red[2][NWAVE];
+  T* R1 = reinterpret_cast<T*>(rbuf);
+  T* R2 = reinterpret_cast<T*>(rbuf + SZ_R);
+  T* R3 = reinterpret_cast<T*>(rbuf + 2 * SZ_R);
+  T* S0 = reinterpret_cast<T*>(rbuf + 3 * SZ_R);
+  T* S1 = reinterpret_cast<T*>(rbuf + 3 * SZ_R + SZ_S);
+  T* S2 = reinterpret_cast<T*>(rbuf + 3 * SZ_R + 2 * SZ_S);
+  T* S3 = reinterpret_cast<T*>(rbuf + 3 * SZ_R + 3 * SZ_S);
+
+  const SeqTables& s = p.s;
+  const int total = s.NTtot * p.Hq;
+  const int u = xcd_remap(blockIdx.x, total);
+  if (u >= total) return;
+  const int c = u / p.Hq, hk = u % p.Hq;
+  int n, t0, len;
+  if (!locate_chunk_b(s, c, n, t0, len)) return;
+  const int G = p.Hv / p.Hq;
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+
+  // group-shared tiles: K rows, K^T, Q^T; raw Q K^T and K K^T (row block w)
+  f32x4 Sqk[4], Skk[4];
+  {
+    TileCols<T, KD> rq, rk;
+    rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    rq.template store<PK>(R1);
+    rk.template store<PK>(sK);
+    rq.template store_t<PT>(sQT, 1.f);
+    rk.template store_t<PT>(sKT, 1.f);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { Sqk[j] = zero4(); Skk[j] = zero4(); }
+  mma_row<T, KD, 4, PK, 1, 1, PK>(Sqk, R1 + 16 * w * PK, sK);
+  mma_row<T, KD, 4, PK, 1, 1, PK>(Skk, sK + 16 * w * PK, sK);
+  f32x4 dq[NKT], dk[NKT];
+#pragma unroll
+  for (int j = 0; j < NKT; ++j) { dq[j] = zero4(); dk[j] = zero4(); }
+  __syncthreads();
+
+  for (int gi = 0; gi < G; ++gi) {
+    const int h = hk * G + gi;
+    const long hT = (long)h * s.Ttot;
+    // ---- ph1: per-head rows and scalars
+    float glast;
+    {
+      const float* gc = p.gcum + hT + t0;
+      glast = gc[len - 1];
+      if (w == 0) {
+        const float gm = (l < len) ? gc[l] : glast;
+        sG[l] = gm;
+        sB[l] = (l < len) ? p.beta[(long)(t0 + l) * p.Hv + h] : 0.f;
+        sGm[l] = (l < len) ? __expf(gm) : 0.f;
+        sDec[l] = (l < len) ? __expf(glast - gm) : 0.f;
+        sdg[l] = 0.f;
+        sdb[l] = 0.f;
+      }
+      colp[w][l] = 0.f;
+    }
+    TileCols<T, VD> rdvn, rv;
+    {
+      TileCols<T, VD> rdo, rvn;
+      rdo.load((const T*)p.d_o + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, len);
+      rvn.load((const T*)p.vnew + (hT + t0) * VD, VD, len);
+      rdvn.load((const T*)p.dvn + (hT + t0) * VD, VD, len);
+      rv.load((const T*)p.v + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, len);
+      TileCols<float, CH> ra;   // A rows (fp32): row-major -> S0, transposed -> S1
+      ra.load(p.A_ws + (hT + t0) * CH, CH, len);
+#pragma unroll
+      for (int i = 0; i < TileCols<float, CH>::NV; ++i) {
+        const int c0 = (w + NWAVE * i) * 4;
+        const float* e = reinterpret_cast<const float*>(&ra.v[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          S0[l * PT + c0 + j] = from_f<T>(e[j]);
+          S1[(c0 + j) * PT + l] = from_f<T>(e[j]);
+        }
+      }
+      rdo.template store<PK>(R1);
+      rvn.template store<PK>(R2);
+      rdvn.template store<PK>(R3);
+    }
+    __syncthreads();
+
+    // ---- ph2: dP (regs), dQ_inter, dW (regs), dKhat; gate terms
+    f32x4 dP[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dP[j] = zero4();
+    mma_row<T, VD, 4, PK, 1, 1, PK>(dP, R1 + 16 * w * PK, R2);
+    float rowx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float colx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * w + acc_row(e), sidx = 16 * j + acc_col();
+        const float D = (t >= sidx) ? __expf(sG[t] - sG[sidx]) : 0.f;
+        const float dpd = p.scale * dP[j][e] * D;
+        const float x = dpd * Sqk[j][e];
+        dP[j][e] = dpd;                // now (dP * D)
+        rowx[e] += x;
+        colx += x;
+      }
+      colx = col_group_sum(colx);
+      if (l < 16) colp[w][16 * j + l] -= colx;
+    }
+
+    const T* hb = (const T*)p.hbuf + ((long)h * s.NTtot + c) * KD * VD;    // [d][v]
+    const T* dhb = (const T*)p.dhbuf + ((long)h * s.NTtot + c) * KD * VD;  // [d][v]
+    f32x4 aw[NKT];
+    {
+      f32x4 aq[NKT];
+#pragma unroll
+      for (int j = 0; j < NKT; ++j) { aq[j] = zero4(); aw[j] = zero4(); }
+      constexpr int KS = Mma<T>::KSTEP;
+#pragma unroll
+      for (int k0 = 0; k0 < VD; k0 += KS) {
+        const auto fdo = Mma<T>::template load<PK, 1>(R1 + 16 * w * PK + k0);
+        const auto fdv = Mma<T>::template load<PK, 1>(R3 + 16 * w * PK + k0);
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          const auto fh = Mma<T>::template load<VD, 1>(hb + 16 * j * VD + k0);
+          aq[j] = Mma<T>::op(fdo, fh, aq[j]);
+          aw[j] = Mma<T>::op(fdv, fh, aw[j]);
+        }
+      }
+      // dQ_inter = s Gamma_t (dO h^T)_t ; dgamma_t += <q_t, dQ_inter_t>
+      float qd[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * w + acc_row(e);
+        const float sc = p.scale * sGm[t];
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          const float v = sc * aq[j][e];
+          dq[j][e] += v;
+          qd[e] += v * to_f(sQT[(16 * j + acc_col()) * PT + t]);
+          aw[j][e] = -aw[j][e];        // dW = -dVnew h^T
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rowx[e] += qd[e];   // per-lane partial, reduced at the end
+    }
+    {
+      // dKhat = Vnew dh+^T; dK += diag(dec) dKhat; r_t = <k_t, dec_t dKhat_t>
+      f32x4 ak[NKT];
+#pragma unroll
+      for (int j = 0; j < NKT; ++j) ak[j] = zero4();
+      float hd = 0.f;
+      constexpr int KS = Mma<T>::KSTEP;
+#pragma unroll
+      for (int k0 = 0; k0 < VD; k0 += KS) {
+        const auto fvn = Mma<T>::template load<PK, 1>(R2 + 16 * w * PK + k0);
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          const auto fdh = Mma<T>::template load<VD, 1>(dhb + 16 * j * VD + k0);
+          ak[j] = Mma<T>::op(fvn, fdh, ak[j]);
+          if (w == 0) {  // <dh+, h> over the whole state, once
+            const auto fh = Mma<T>::template load<VD, 1>(hb + 16 * j * VD + k0);
+            if constexpr (std::is_same<T, float>::value) {
+              hd += fh * fdh;
+            } else {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) hd += to_f(fh[q]) * to_f(fdh[q]);
+            }
+          }
+        }
+      }
+      float rk[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * w + acc_row(e);
+        const float dec = sDec[t];
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          const float v = dec * ak[j][e];
+          dk[j][e] += v;
+          rk[e] += v * to_f(sK[t * PK + 16 * j + acc_col()]);
+        }
+      }
+      float rsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rowx[e] -= rk[e];                              // per-lane partial
+        rsum += rk[e];
+      }
+      rsum = wave_sum(rsum);
+      hd = wave_sum(hd);
+      if (l == 0) { red[0][w] = rsum; red[1][w] = (w == 0) ? hd : 0.f; }
+    }
+    __syncthreads();
+
+    // ---- ph3: dW rows -> R1, dW^T -> R2, value rows -> S2..S3
+#pragma unroll
+    for (int j = 0; j < NKT; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) R1[(16 * w + acc_row(e)) * PK + 16 * j + acc_col()] = from_f<T>(aw[j][e]);
+      acc_store_t<T, PT>(R2, 16 * w, 16 * j, aw[j]);
+    }
+    rv.template store<PK>(S2);
+    __syncthreads();
+
+    // ---- ph4: dA (strict lower) and dKb = A^T dW
+    f32x4 dA[4];
+    {
+      f32x4 ta[4], tb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { ta[j] = zero4(); tb[j] = zero4(); }
+      mma_row<T, KD, 4, PK, 1, 1, PK>(ta, R1 + 16 * w * PK, sK);
+      mma_row<T, VD, 4, PK, 1, 1, PK>(tb, R3 + 16 * w * PK, S2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * w + acc_row(e), sidx = 16 * j + acc_col();
+          dA[j][e] = (t > sidx) ? sB[sidx] * (sGm[sidx] * ta[j][e] + tb[j][e]) : 0.f;
+        }
+    }
+    {
+      f32x4 akb[NKT];
+#pragma unroll
+      for (int j = 0; j < NKT; ++j) akb[j] = zero4();
+      mma_row<T, CH, NKT, PT, 1, 1, PT>(akb, S1 + 16 * w * PT, R2);
+      float kk[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * w + acc_row(e);
+        const float bg = sB[t] * sGm[t];
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          dk[j][e] += bg * akb[j][e];
+          kk[e] += akb[j][e] * to_f(sK[t * PK + 16 * j + acc_col()]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * w + acc_row(e);
+        rowx[e] += sB[t] * sGm[t] * kk[e];              // per-lane partial
+        const float ks = row_group_sum(kk[e]);          // <dKb_t, k_t>
+        if (acc_col() == 0) sdb[t] += sGm[t] * ks;
+      }
+    }
+    __syncthreads();
+
+    // ---- ph5: dVnew^T -> R1, dA^T -> R2
+    rdvn.template store_t<PT>(R1, 1.f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc_store_t<T, PT>(R2, 16 * w, 16 * j, dA[j]);
+    __syncthreads();
+
+    // ---- ph6: dVb = A^T dVnew -> dv (staged in R3); M1 = A^T dA
+    f32x4 m1[4];
+    {
+      f32x4 av[NVT];
+#pragma unroll
+      for (int j = 0; j < NVT; ++j) av[j] = zero4();
+      mma_row<T, CH, NVT, PT, 1, 1, PT>(av, S1 + 16 * w * PT, R1);
+      float vv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * w + acc_row(e);
+        const float b = sB[t];
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) {
+          vv[e] += av[j][e] * to_f(S2[t * PK + 16 * j + acc_col()]);
+          R3[t * PK + 16 * j + acc_col()] = from_f<T>(b * av[j][e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float vs = row_group_sum(vv[e]);
+        if (acc_col() == 0) sdb[16 * w + acc_row(e)] += vs;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m1[j] = zero4();
+      mma_row<T, CH, 4, PT, 1, 1, PT>(m1, S1 + 16 * w * PT, R2);
+    }
+    __syncthreads();
+    store_rows<T, CH, VD, PK>((T*)p.dv + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, R3, len);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S2[(16 * w + acc_row(e)) * PT + 16 * j + acc_col()] = from_f<T>(m1[j][e]);
+    __syncthreads();
+
+    // ---- ph8: dL = strict_lower(-M1 A^T); E = dL * diag(b) D; gate/beta terms
+    float* E32 = reinterpret_cast<float*>(R1);
+    {
+      f32x4 dl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dl[j] = zero4();
+      mma_row<T, CH, 4, PT, 1, 1, PT>(dl, S2 + 16 * w * PT, S0);
+      float bsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float colx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * w + acc_row(e), sidx = 16 * j + acc_col();
+          float ev = 0.f;
+          if (t > sidx) {
+            const float D = __expf(sG[t] - sG[sidx]);
+            const float dlv = -dl[j][e];
+            const float y = dlv * D * Skk[j][e];
+            bsum[e] += y;
+            ev = dlv * sB[t] * D;
+            const float x = sB[t] * y;
+            rowx[e] += x;
+            colx += x;
+          }
+          E32[t * PL + sidx] = ev;
+        }
+        colx = col_group_sum(colx);
+        if (l < 16) colp[w][16 * j + l] -= colx;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float bs = row_group_sum(bsum[e]);
+        if (acc_col() == 0) sdb[16 * w + acc_row(e)] += bs;
+      }
+    }
+    // (dP * D) rows -> R2, its transpose -> S3
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) R2[(16 * w + acc_row(e)) * PT + 16 * j + acc_col()] = from_f<T>(dP[j][e]);
+      acc_store_t<T, PT>(S3, 16 * w, 16 * j, dP[j]);
+    }
+    // row-sum gate terms of this wave's rows
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float rs = row_group_sum(rowx[e]);
+      if (acc_col() == 0) sdg[16 * w + acc_row(e)] += rs;
+    }
+    __syncthreads();
+    // F = E + E^T -> S1
+    for (int i = tid; i < CH * CH; i += NTHR) {
+      const int r = i / CH, cc = i % CH;
+      S1[r * PT + cc] = from_f<T>(E32[r * PL + cc] + E32[cc * PL + r]);
+    }
+    __syncthreads();
+
+    // ---- ph9: dQ += (dP*D) K; dK += (dP*D)^T Q + F K
+    mma_row<T, CH, NKT, PT, 1, 1, PT>(dq, R2 + 16 * w * PT, sKT);
+    mma_row<T, CH, NKT, PT, 1, 1, PT>(dk, S3 + 16 * w * PT, sQT);
+    mma_row<T, CH, NKT, PT, 1, 1, PT>(dk, S1 + 16 * w * PT, sKT);
+
+    // gate: dgamma_t = row terms - column terms (+ last-row terms); dg is its
+    // reverse cumulative sum over the chunk's tokens.
+    if (w == 0) {
+      float dgm = sdg[l] + colp[0][l] + colp[1][l] + colp[2][l] + colp[3][l];
+      if (l == len - 1) {
+        const float rs = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+        dgm += rs + __expf(glast) * red[1][0];
+      }
+      dgm = (l < len) ? dgm : 0.f;
+      // suffix sum: scan over reversed lanes
+      const float rev = __shfl(dgm, 63 - l, 64);
+      const float sc = wave_inclusive_scan(rev);
+      const float dgv = __shfl(sc, 63 - l, 64);
+      if (l < len) {
+        p.dg[(long)(t0 + l) * p.Hv + h] = dgv;
+        p.dbeta[(long)(t0 + l) * p.Hv + h] = sdb[l];
+      }
+    }
+    __syncthreads();
+  }
+
+  // dq, dk rows -> LDS -> global
+#pragma unroll
+  for (int j = 0; j < NKT; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      R1[(16 * w + acc_row(e)) * PK + 16 * j + acc_col()] = from_f<T>(dq[j][e]);
+      R2[(16 * w + acc_row(e)) * PK + 16 * j + acc_col()] = from_f<T>(dk[j][e]);
+    }
+  __syncthreads();
+  store_rows<T, CH, KD, PK>((T*)p.dq + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, R1, len);
+  store_rows<T, CH, KD, PK>((T*)p.dk + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, R2, len);
+}
+
+// ------------------------------------------------------------- launchers --
+static unsigned padded_grid_b(long total) { return (unsigned)(((total + 7) / 8) * 8); }
+
+template <typename T, int KD, int BV>
+static hipError_t dstate_impl(const DStateParams& p, int total, hipStream_t st) {
+  timing_before("chunk_dstate", st);
+  hipLaunchKernelGGL((k_dstate<T, KD, BV>), dim3(padded_grid_b(total)), dim3(NTHR), 0, st, p, total);
+  hipError_t err = hipGetLastError();
+  timing_after(st);
+  return err;
+}
+
+template <typename T, int KD>
+static hipError_t grads_impl(const GradParams& p, hipStream_t st) {
+  timing_before("chunk_grads", st);
+  hipLaunchKernelGGL((k_grads<T, KD>), dim3(padded_grid_b((long)p.s.NTtot * p.Hq)), dim3(NTHR), 0, st, p);
+  hipError_t err = hipGetLastError();
+  timing_after(st);
+  return err;
+}
+
+hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, int total, hipStream_t st) {
+  if (dt == DType::BF16) {
+    if (KD == 32 && BV == 32) return dstate_impl<bf16, 32, 32>(p, total, st);
+    if (KD == 64 && BV == 32) return dstate_impl<bf16, 64, 32>(p, total, st);
+    if (KD == 128 && BV == 64) return dstate_impl<bf16, 128, 64>(p, total, st);
+  } else {
+    if (KD == 32 && BV == 32) return dstate_impl<float, 32, 32>(p, total, st);
+    if (KD == 64 && BV == 32) return dstate_impl<float, 64, 32>(p, total, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_grads(DType dt, int KD, const GradParams& p, hipStream_t st) {
+  if (dt == DType::BF16) {
+    if (KD == 32) return grads_impl<bf16, 32>(p, st);
+    if (KD == 64) return grads_impl<bf16, 64>(p, st);
+    if (KD == 128) return grads_impl<bf16, 128>(p, st);
+  } else {
+    if (KD == 32) return grads_impl<float, 32>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace gdr

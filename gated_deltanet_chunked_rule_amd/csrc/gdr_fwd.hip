@@ -263,7 +263,12 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
 // One workgroup per (sequence, value head, V block, CP segment), serial over
 // the segment's chunks.  h (K x BV) stays in fp32 MFMA accumulators; the next
 // chunk's W, K, U rows are fetched into registers while the current one runs.
-template <typename T, int KD, int BV>
+// ROWS = false (forward): hbuf holds each chunk's entry state transposed
+// [V][K] and vnew holds Vnew transposed per chunk [V][64] -- the layouts the
+// output kernel reads as MFMA operands.  ROWS = true (backward recompute):
+// hbuf holds [K][V] and vnew holds token rows [Ttot][V], the layouts the
+// gradient kernels read.
+template <typename T, int KD, int BV, bool ROWS>
 __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) {
   constexpr int VD = KD;
   constexpr int PK = Pitch<T, KD>::value;
@@ -278,6 +283,9 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
   __shared__ __align__(16) T sU[CH * PU];
   __shared__ __align__(16) T shT[BV * PK];
   __shared__ __align__(16) T sVt[BV * PT];
+  __shared__ __align__(16) T sRows[ROWS ? KD * PU + CH * PU : 8];  // [K][BV] state, then [64][BV] Vnew
+  T* sHr = sRows;
+  T* sVr = sRows + (ROWS ? KD * PU : 0);
 
   const SeqTables& s = p.s;
   const int u = xcd_remap(blockIdx.x, total_items);
@@ -361,11 +369,19 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
     for (int i = 0; i < TPW; ++i) {
       const int ti = w * TPW + i, rb = ti / NCB, cb = ti % NCB;
       acc_store_t<T, PK>(shT, 16 * rb, 16 * cb, hacc[i]);
+      if constexpr (ROWS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sHr[(16 * rb + acc_row(e)) * PU + 16 * cb + acc_col()] = from_f<T>(hacc[i][e]);
+      }
     }
     __syncthreads();
     if (jc + 1 < cend) prefetch(jc + 1);
-    if (!warm && p.hbuf)
-      store_rows<T, BV, KD, PK>((T*)p.hbuf + (((long)h * s.NTtot + gc) * VD + vb * BV) * KD, KD, shT, BV);
+    if (!warm && p.hbuf) {
+      if constexpr (ROWS)
+        store_rows<T, KD, BV, PU>((T*)p.hbuf + ((long)h * s.NTtot + gc) * KD * VD + vb * BV, VD, sHr, KD);
+      else
+        store_rows<T, BV, KD, PK>((T*)p.hbuf + (((long)h * s.NTtot + gc) * VD + vb * BV) * KD, KD, shT, BV);
+    }
 
     {  // Vnew = U - W h, staged transposed (tokens contiguous)
       f32x4 acc[NCB];
@@ -377,11 +393,19 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[j][e] = to_f(sU[(16 * w + acc_row(e)) * PU + 16 * j + acc_col()]) - acc[j][e];
         acc_store_t<T, PT>(sVt, 16 * w, 16 * j, acc[j]);
+        if constexpr (ROWS) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sVr[(16 * w + acc_row(e)) * PU + 16 * j + acc_col()] = from_f<T>(acc[j][e]);
+        }
       }
     }
     __syncthreads();
-    if (!warm)
-      store_rows<T, BV, CH, PT>((T*)p.vnew + (((long)h * s.NTtot + gc) * VD + vb * BV) * CH, CH, sVt, BV);
+    if (!warm) {
+      if constexpr (ROWS)
+        store_rows<T, CH, BV, PU>((T*)p.vnew + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, sVr, len);
+      else
+        store_rows<T, BV, CH, PT>((T*)p.vnew + (((long)h * s.NTtot + gc) * VD + vb * BV) * CH, CH, sVt, BV);
+    }
 
     const float dlast = __expf(glast);
 #pragma unroll
@@ -511,10 +535,13 @@ static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
 }
 
 template <typename T, int KD, int BV>
-static hipError_t state_impl(const StateParams& p, int total_segs, hipStream_t st) {
+static hipError_t state_impl(const StateParams& p, int total_segs, bool rows, hipStream_t st) {
   hipError_t err;
   const int total = total_segs * p.Hv * p.nvb;
-  GDR_LAUNCH("chunk_state", (k_state<T, KD, BV>), dim3(padded_grid(total)), st, p, total);
+  if (rows)
+    GDR_LAUNCH("chunk_state_rows", (k_state<T, KD, BV, true>), dim3(padded_grid(total)), st, p, total);
+  else
+    GDR_LAUNCH("chunk_state", (k_state<T, KD, BV, false>), dim3(padded_grid(total)), st, p, total);
   return err;
 }
 
@@ -539,15 +566,15 @@ hipError_t launch_intra(DType dt, int KD, const IntraParams& p, hipStream_t st) 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int total_segs, hipStream_t st) {
+hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int total_segs, bool rows,
+                        hipStream_t st) {
   if (dt == DType::BF16) {
-    if (KD == 32 && BV == 32) return state_impl<bf16, 32, 32>(p, total_segs, st);
-    if (KD == 64 && BV == 32) return state_impl<bf16, 64, 32>(p, total_segs, st);
-    if (KD == 128 && BV == 32) return state_impl<bf16, 128, 32>(p, total_segs, st);
-    if (KD == 128 && BV == 64) return state_impl<bf16, 128, 64>(p, total_segs, st);
+    if (KD == 32 && BV == 32) return state_impl<bf16, 32, 32>(p, total_segs, rows, st);
+    if (KD == 64 && BV == 32) return state_impl<bf16, 64, 32>(p, total_segs, rows, st);
+    if (KD == 128 && BV == 64) return state_impl<bf16, 128, 64>(p, total_segs, rows, st);
   } else {
-    if (KD == 32 && BV == 32) return state_impl<float, 32, 32>(p, total_segs, st);
-    if (KD == 64 && BV == 32) return state_impl<float, 64, 32>(p, total_segs, st);
+    if (KD == 32 && BV == 32) return state_impl<float, 32, 32>(p, total_segs, rows, st);
+    if (KD == 64 && BV == 32) return state_impl<float, 64, 32>(p, total_segs, rows, st);
   }
   return hipErrorInvalidValue;
 }

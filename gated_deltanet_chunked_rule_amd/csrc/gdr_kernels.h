@@ -5,11 +5,13 @@
 //   gcum  fp32 [Hv][Ttot]          chunk-local inclusive cumsum of g
 //   cert  fp32 [Hv][NTtot]         chunk gate sum, +inf if some beta|k|^2 is outside [0, 2]
 //   W, U  T    [Hv][Ttot][K|V]     W = A diag(beta*Gamma) K,  U = A diag(beta) V
-//   vnew  T    [Hv][NTtot][V][64]  Vnew = U - W h per chunk, stored transposed
-//   hbuf  T    [Hv][NTtot][V][K]   state entering each chunk, stored transposed
+//   vnew  T    forward: [Hv][NTtot][V][64]  Vnew = U - W h per chunk, transposed
+//              backward: [Hv][Ttot][V]     the same values as token rows
+//   hbuf  T    forward: [Hv][NTtot][V][K]  state entering each chunk, transposed
+//              backward: [Hv][NTtot][K][V] the same states, row-major
 //   A     fp32 [Hv][Ttot][64]      rows of the chunk's A (backward only)
-//   dhbuf T    [Hv][NTtot][V][K]   state gradient leaving each chunk (transposed)
-//   dvn   T    [Hv][Ttot][V]       gradient of Vnew
+//   dhbuf T    [Hv][NTtot][K][V]   gradient of the state leaving each chunk
+//   dvn   T    [Hv][Ttot][V]       gradient of Vnew (token rows)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -97,9 +99,10 @@ struct GradParams {          // per-chunk gradients
 // Kernel launchers; each returns hipGetLastError() of its launch.
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_intra(DType dt, int KD, const IntraParams& p, hipStream_t st);
-hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int total_segs, hipStream_t st);
+hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int total_segs, bool rows,
+                        hipStream_t st);
 hipError_t launch_output(DType dt, int KD, const OutputParams& p, hipStream_t st);
-hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, hipStream_t st);
+hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, int total_items, hipStream_t st);
 hipError_t launch_grads(DType dt, int KD, const GradParams& p, hipStream_t st);
 
 // Kernel timing hooks (gdr_timing.cpp).

@@ -40,7 +40,8 @@
  * Chunks: 64 tokens, restarting at every sequence start; the last chunk of a
  *   sequence may be short.
  * Supported: K, V in {32, 64, 128} with K == V; Hv a multiple of Hq;
- *   dtype bf16 (q, k, v, o, do, dq, dk, dv in bfloat16) or fp32.
+ *   dtype bf16 (q, k, v, o, do, dq, dk, dv in bfloat16) or fp32; fp32 needs
+ *   K <= 64 in the forward and K == 32 in the backward.
  * Errors: arguments are validated on the host before anything is enqueued; a
  *   negative status is returned and gdr_last_error() describes it.  Launch
  *   failures map to GDR_ERR_HIP.  Faults inside kernels surface at the

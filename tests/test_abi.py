@@ -143,3 +143,10 @@ def test_planner_ragged_and_empty_sequences():
     assert info["num_seqs"] == 4
     assert info["total_chunks"] == 0 + 2 + 0 + 3 and info["max_chunks"] == 3
     assert info["total_segments"] == 4             # every sequence gets a state work item
+
+
+def test_bwd_fp32_k64_unsupported():
+    lib = gdr.load_library()
+    sh = shape(K=64, V=64)
+    assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(sh), None, None) == 0
+    assert "fp32 backward" in last_error()
