@@ -24,7 +24,7 @@ gdr_status fail(gdr_status s, const std::string& msg) {
 
 constexpr int kChunk = 64;
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kStateWgPerCU = 2;   // state workgroups resident per CU (LDS-bound)
+constexpr int kStateWgPerCU = 1;   // fused state workgroups (8 waves) resident per CU
 constexpr size_t kAlign = 256;
 
 struct Problem {
@@ -60,7 +60,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int choose_segment(const Problem& P) {
   const int W = P.W;
   const long slots = (long)kCUs * kStateWgPerCU;
-  const long units = (long)P.Hv * P.nvb;
+  const long units = (long)P.Hv;     // the fused pass covers all V columns per workgroup
   const int NTmax = std::max(P.NTmax, 1);
   const long base = units * (long)P.N;
   if (base >= slots || NTmax <= 2 * W + 1) return NTmax;
@@ -203,7 +203,9 @@ gdr_status hip_fail(hipError_t e, const char* what) {
   return fail(GDR_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Plan tables + the forward chain (intra, state, optional output).
+// Plan tables + the forward chain: intra-chunk WY, then either the fused
+// state+output pass (forward) or the state pass storing every chunk's entry
+// state (backward recompute).
 gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const void* q,
                              const void* k, const void* v, const float* g, const float* beta,
                              float scale, const float* h0, const int32_t* cu_dev, void* o,
@@ -230,22 +232,28 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     ip.A_ws = A_ws; ip.A_out = A_out; ip.A_in = A_in;
     if ((e = gdr::launch_intra(P.dt, P.K, ip, st)) != hipSuccess) return hip_fail(e, "intra launch");
   }
-  gdr::StateParams sp;
-  sp.s = s; sp.k = k; sp.W = ws + Lo.W; sp.U = ws + Lo.U;
-  sp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
-  sp.cert = reinterpret_cast<const float*>(ws + Lo.cert);
-  sp.h0 = h0; sp.ht = ht; sp.hbuf = ws + Lo.hbuf; sp.vnew = ws + Lo.vnew;
-  sp.Hq = P.Hq; sp.Hv = P.Hv; sp.seg_chunks = L; sp.warmup = P.W; sp.log_eps = P.log_eps;
-  sp.nvb = P.nvb;
   int segs = 0;
   for (int c : P.chunks) segs += std::max(1, (c + L - 1) / L);
-  if ((e = gdr::launch_state(P.dt, P.K, P.BV, sp, segs, bwd, st)) != hipSuccess) return hip_fail(e, "state launch");
-  if (o && P.NTtot > 0) {
-    gdr::OutputParams op;
-    op.s = s; op.q = q; op.k = k; op.hbuf = ws + Lo.hbuf; op.vnew = ws + Lo.vnew;
-    op.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
-    op.o = o; op.Hq = P.Hq; op.Hv = P.Hv; op.scale = scale;
-    if ((e = gdr::launch_output(P.dt, P.K, op, st)) != hipSuccess) return hip_fail(e, "output launch");
+  if (!bwd) {
+    // forward: state recurrence fused with the output
+    gdr::FusedParams fp;
+    fp.s = s; fp.q = q; fp.k = k; fp.W = ws + Lo.W; fp.U = ws + Lo.U;
+    fp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
+    fp.cert = reinterpret_cast<const float*>(ws + Lo.cert);
+    fp.h0 = h0; fp.ht = ht; fp.o = o;
+    fp.Hq = P.Hq; fp.Hv = P.Hv; fp.seg_chunks = L; fp.warmup = P.W;
+    fp.log_eps = P.log_eps; fp.scale = scale;
+    if ((e = gdr::launch_fused(P.dt, P.K, fp, segs, st)) != hipSuccess) return hip_fail(e, "fused launch");
+  } else {
+    // backward recompute: every chunk's entry state and Vnew, row layouts
+    gdr::StateParams sp;
+    sp.s = s; sp.k = k; sp.W = ws + Lo.W; sp.U = ws + Lo.U;
+    sp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
+    sp.cert = reinterpret_cast<const float*>(ws + Lo.cert);
+    sp.h0 = h0; sp.ht = ht; sp.hbuf = ws + Lo.hbuf; sp.vnew = ws + Lo.vnew;
+    sp.Hq = P.Hq; sp.Hv = P.Hv; sp.seg_chunks = L; sp.warmup = P.W; sp.log_eps = P.log_eps;
+    sp.nvb = P.nvb;
+    if ((e = gdr::launch_state(P.dt, P.K, P.BV, sp, segs, true, st)) != hipSuccess) return hip_fail(e, "state launch");
   }
   return GDR_OK;
 }
@@ -283,11 +291,11 @@ gdr_status gdr_chunk_fwd_plan(const gdr_shape* shape, const gdr_options* opts,
   out->num_seqs = P.N;
   out->total_chunks = P.NTtot;
   out->max_chunks = P.NTmax;
-  out->v_blocks = P.nvb;
+  out->v_blocks = 1;
   out->segment_chunks = P.L;
   out->warmup_chunks = (P.L < P.NTmax) ? P.W : 0;
   out->total_segments = P.total_segs;
-  out->state_workgroups = P.total_segs * P.Hv * P.nvb;
+  out->state_workgroups = P.total_segs * P.Hv;
   return GDR_OK;
 }
 

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
 #pragma unroll
       for (int e = 0; e < 4; ++e) sdhr[(16 * rb + acc_row(e)) * PU + 16 * cb + acc_col()] = from_f<T>(hacc[i][e]);
     }
-    __syncthreads();
+    lds_barrier();
     if (jc > 0) prefetch(jc - 1);
     store_rows<T, KD, BV, PU>((T*)p.dhbuf + ((long)h * s.NTtot + gc) * KD * VD + vb * BV, VD, sdhr, KD);
 
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
       }
       acc_store_t<T, PT>(sPt, 16 * w, 16 * j, a);
     }
-    __syncthreads();
+    lds_barrier();
 
     {  // dVnew rows of block w
       f32x4 acc[NCB];
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
         for (int e = 0; e < 4; ++e) sdVr[(16 * w + acc_row(e)) * PU + 16 * j + acc_col()] = from_f<T>(acc[j][e]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     store_rows<T, CH, BV, PU>((T*)p.dvn + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, sdVr, len);
 
     const float gl = __expf(glast);
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
       mma_tile<T, CH, PT, 1, 1, PT>(hacc[i], sQgT + 16 * rb * PT, sdOT + 16 * cb * PT);
       mma_tile<T, CH, PT, 1, 1, PT>(hacc[i], sWnT + 16 * rb * PT, sdVT + 16 * cb * PT);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   if (p.dh0) {
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(NTHR) void k_grads(GradParams p) {
       rvn.template store<PK>(R2);
       rdvn.template store<PK>(R3);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- ph2: dP (regs), dQ_inter, dW (regs), dKhat; gate terms
     f32x4 dP[4];
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(NTHR) void k_grads(GradParams p) {
       hd = wave_sum(hd);
       if (l == 0) { red[0][w] = rsum; red[1][w] = (w == 0) ? hd : 0.f; }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- ph3: dW rows -> R1, dW^T -> R2, value rows -> S2..S3
 #pragma unroll
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(NTHR) void k_grads(GradParams p) {
       acc_store_t<T, PT>(R2, 16 * w, 16 * j, aw[j]);
     }
     rv.template store<PK>(S2);
-    __syncthreads();
+    lds_barrier();
 
     // ---- ph4: dA (strict lower) and dKb = A^T dW
     f32x4 dA[4];
@@ -472,13 +472,13 @@ __global__ __launch_bounds__(NTHR) void k_grads(GradParams p) {
         if (acc_col() == 0) sdb[t] += sGm[t] * ks;
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- ph5: dVnew^T -> R1, dA^T -> R2
     rdvn.template store_t<PT>(R1, 1.f);
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc_store_t<T, PT>(R2, 16 * w, 16 * j, dA[j]);
-    __syncthreads();
+    lds_barrier();
 
     // ---- ph6: dVb = A^T dVnew -> dv (staged in R3); M1 = A^T dA
     f32x4 m1[4];
@@ -507,13 +507,13 @@ __global__ __launch_bounds__(NTHR) void k_grads(GradParams p) {
       for (int j = 0; j < 4; ++j) m1[j] = zero4();
       mma_row<T, CH, 4, PT, 1, 1, PT>(m1, S1 + 16 * w * PT, R2);
     }
-    __syncthreads();
+    lds_barrier();
     store_rows<T, CH, VD, PK>((T*)p.dv + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, R3, len);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) S2[(16 * w + acc_row(e)) * PT + 16 * j + acc_col()] = from_f<T>(m1[j][e]);
-    __syncthreads();
+    lds_barrier();
 
     // ---- ph8: dL = strict_lower(-M1 A^T); E = dL * diag(b) D; gate/beta terms
     float* E32 = reinterpret_cast<float*>(R1);
@@ -564,13 +564,13 @@ __global__ __launch_bounds__(NTHR) void k_grads(GradParams p) {
       const float rs = row_group_sum(rowx[e]);
       if (acc_col() == 0) sdg[16 * w + acc_row(e)] += rs;
     }
-    __syncthreads();
+    lds_barrier();
     // F = E + E^T -> S1
     for (int i = tid; i < CH * CH; i += NTHR) {
       const int r = i / CH, cc = i % CH;
       S1[r * PT + cc] = from_f<T>(E32[r * PL + cc] + E32[cc * PL + r]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- ph9: dQ += (dP*D) K; dK += (dP*D)^T Q + F K
     mma_row<T, CH, NKT, PT, 1, 1, PT>(dq, R2 + 16 * w * PT, sKT);
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(NTHR) void k_grads(GradParams p) {
         p.dbeta[(long)(t0 + l) * p.Hv + h] = sdb[l];
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // dq, dk rows -> LDS -> global

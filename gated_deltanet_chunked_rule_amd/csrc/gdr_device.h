@@ -34,6 +34,19 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also waits
+// for every outstanding global load and store of the wave (vmcnt(0)), which
+// would stall on the next chunk's prefetch and on pending output stores; here
+// each wave waits for its own LDS operations (lgkmcnt(0)) and then meets the
+// others at s_barrier.  Global data that other waves read through LDS is
+// always moved there by LDS stores, which this covers.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt = max, expcnt = max, lgkmcnt = 0
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return static_cast<T>(x); }
 
@@ -116,49 +129,32 @@ __device__ __forceinline__ int acc_row(int j) { return 4 * (lane_id() >> 4) + j;
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }
 
 // ------------------------------------------------------------- staging --
-// Copies rows [0, nrows) of an R x D tile from global memory (row stride
-// `gstride` elements) to LDS (row pitch P); rows >= nrows are zero-filled.
-// 16-byte vector accesses; D * sizeof(T) must be a multiple of 16.
-template <typename T, int R, int D, int P>
-__device__ __forceinline__ void stage_rows(T* lds, const T* g, long gstride, int nrows) {
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int VPR = D / VEC;
-  static_assert(D % VEC == 0, "row length must be a multiple of 16 bytes");
-  static_assert((P * sizeof(T)) % 16 == 0, "LDS pitch must keep 16-byte alignment");
-  for (int i = threadIdx.x; i < R * VPR; i += NTHR) {
-    const int r = i / VPR, c = (i % VPR) * VEC;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (r < nrows) val = *reinterpret_cast<const uint4*>(g + (long)r * gstride + c);
-    *reinterpret_cast<uint4*>(lds + r * P + c) = val;
-  }
-}
-
 // Global rows -> registers -> LDS.  load() issues every 16-byte global read of
 // an R x D tile (rows >= nrows read as zero) before anything is written, so a
 // tile's reads overlap; store() writes the rows to LDS (pitch P) and
 // store_t() writes the transpose (LDS element (c, r) = scale(r) * tile(r, c)).
-template <typename T, int R, int D>
+template <typename T, int R, int D, int NTH = NTHR>
 struct TileRegs {
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int VPR = D / VEC;
-  static constexpr int NV = (R * VPR + NTHR - 1) / NTHR;
+  static constexpr int NV = (R * VPR + NTH - 1) / NTH;
   static_assert(D % VEC == 0, "row length must be a multiple of 16 bytes");
   uint4 v[NV];
   __device__ __forceinline__ void load(const T* g, long gstride, int nrows) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int idx = (int)threadIdx.x + i * NTHR;
+      const int idx = (int)threadIdx.x + i * NTH;
       const int r = idx / VPR, c = (idx % VPR) * VEC;
       v[i] = make_uint4(0u, 0u, 0u, 0u);
       if (idx < R * VPR && r < nrows) v[i] = *reinterpret_cast<const uint4*>(g + (long)r * gstride + c);
     }
   }
-  __device__ __forceinline__ int row(int i) const { return ((int)threadIdx.x + i * NTHR) / VPR; }
+  __device__ __forceinline__ int row(int i) const { return ((int)threadIdx.x + i * NTH) / VPR; }
   template <int P>
   __device__ __forceinline__ void store(T* lds) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int idx = (int)threadIdx.x + i * NTHR;
+      const int idx = (int)threadIdx.x + i * NTH;
       const int r = idx / VPR, c = (idx % VPR) * VEC;
       if (idx < R * VPR) *reinterpret_cast<uint4*>(lds + r * P + c) = v[i];
     }
@@ -167,7 +163,7 @@ struct TileRegs {
   __device__ __forceinline__ void store_t(T* lds, F scale) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int idx = (int)threadIdx.x + i * NTHR;
+      const int idx = (int)threadIdx.x + i * NTH;
       const int r = idx / VPR, c = (idx % VPR) * VEC;
       if (idx < R * VPR) {
         const float s = scale(r);
@@ -183,28 +179,29 @@ struct TileRegs {
 // the waves splitting the 16-byte column groups.  Its transposed store then
 // has consecutive lanes writing consecutive LDS addresses (no bank
 // conflicts), and the row store writes one 16-byte group per lane.
-template <typename T, int D>
+template <typename T, int D, int NW = NWAVE>
 struct TileCols {
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int NCG = D / VEC;
-  static constexpr int NV = NCG / NWAVE;
-  static_assert(NCG % NWAVE == 0, "column groups must split evenly over the waves");
+  static constexpr int NV = (NCG + NW - 1) / NW;   // waves beyond NCG groups stay idle
   uint4 v[NV];
   __device__ __forceinline__ void load(const T* g, long gstride, int nrows) {
     const int r = lane_id();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int cg = wave_id() + NWAVE * i;
+      const int cg = wave_id() + NW * i;
       v[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nrows) v[i] = *reinterpret_cast<const uint4*>(g + (long)r * gstride + cg * VEC);
+      if (cg < NCG && r < nrows) v[i] = *reinterpret_cast<const uint4*>(g + (long)r * gstride + cg * VEC);
     }
   }
   template <int P>
   __device__ __forceinline__ void store(T* lds) const {
     const int r = lane_id();
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      *reinterpret_cast<uint4*>(lds + r * P + (wave_id() + NWAVE * i) * VEC) = v[i];
+    for (int i = 0; i < NV; ++i) {
+      const int cg = wave_id() + NW * i;
+      if (cg < NCG) *reinterpret_cast<uint4*>(lds + r * P + cg * VEC) = v[i];
+    }
   }
   // lds[c * PT + r] = s * tile(r, c), s the scale of this lane's row.
   template <int PT>
@@ -212,21 +209,23 @@ struct TileCols {
     const int r = lane_id();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c0 = (wave_id() + NWAVE * i) * VEC;
-      const T* e = reinterpret_cast<const T*>(&v[i]);
+      const int cg = wave_id() + NW * i;
+      if (cg < NCG) {
+        const T* e = reinterpret_cast<const T*>(&v[i]);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) lds[(c0 + j) * PT + r] = from_f<T>(to_f(e[j]) * s);
+        for (int j = 0; j < VEC; ++j) lds[(cg * VEC + j) * PT + r] = from_f<T>(to_f(e[j]) * s);
+      }
     }
   }
 };
 
 // LDS rows [0, nrows) of an R x D tile (pitch P) -> global (row stride gstride),
 // 16-byte accesses.
-template <typename T, int R, int D, int P>
+template <typename T, int R, int D, int P, int NTH = NTHR>
 __device__ __forceinline__ void store_rows(T* g, long gstride, const T* lds, int nrows) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int VPR = D / VEC;
-  for (int i = threadIdx.x; i < R * VPR; i += NTHR) {
+  for (int i = threadIdx.x; i < R * VPR; i += NTH) {
     const int r = i / VPR, c = (i % VPR) * VEC;
     if (r < nrows) *reinterpret_cast<uint4*>(g + (long)r * gstride + c) = *reinterpret_cast<const uint4*>(lds + r * P + c);
   }

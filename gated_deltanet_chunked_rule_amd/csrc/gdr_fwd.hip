@@ -15,9 +15,10 @@
 //   k_plan    token/chunk/segment offset tables (one workgroup)
 //   k_intra   per (chunk, value head): gate cumsum, K K^T, blocked fp32
 //             triangular inverse, W and U on MFMA            [fully parallel]
-//   k_state   per (sequence, value head, V block, CP segment): the serial
-//             chunk recurrence with h in fp32 registers        [serial part]
-//   k_output  per (chunk, value head): O                       [fully parallel]
+//   k_fused   per (sequence, value head, CP segment): the serial chunk
+//             recurrence with h in fp32 registers, fused with O  [serial part]
+//   (k_state  the same recurrence storing every chunk's entry state, for the
+//             backward's recompute)
 // The split of the serial state pass into context-parallel segments rebuilt
 // by a gate-decay warmup follows the pages' automatic single-card CP (FlashQLA
 // curated summary, section "平衡解決方案：雙核心融合與自動CP"; Tongyi page,
@@ -263,11 +264,9 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
 // One workgroup per (sequence, value head, V block, CP segment), serial over
 // the segment's chunks.  h (K x BV) stays in fp32 MFMA accumulators; the next
 // chunk's W, K, U rows are fetched into registers while the current one runs.
-// ROWS = false (forward): hbuf holds each chunk's entry state transposed
-// [V][K] and vnew holds Vnew transposed per chunk [V][64] -- the layouts the
-// output kernel reads as MFMA operands.  ROWS = true (backward recompute):
-// hbuf holds [K][V] and vnew holds token rows [Ttot][V], the layouts the
-// gradient kernels read.
+// Used by the backward to recompute every chunk's entry state: hbuf receives
+// [K][V] per chunk and vnew the token rows [Ttot][V] (the layouts the gradient
+// kernels read).  ROWS = false keeps the transposed per-chunk layouts.
 template <typename T, int KD, int BV, bool ROWS>
 __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) {
   constexpr int VD = KD;
@@ -374,7 +373,7 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
         for (int e = 0; e < 4; ++e) sHr[(16 * rb + acc_row(e)) * PU + 16 * cb + acc_col()] = from_f<T>(hacc[i][e]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (jc + 1 < cend) prefetch(jc + 1);
     if (!warm && p.hbuf) {
       if constexpr (ROWS)
@@ -399,7 +398,7 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (!warm) {
       if constexpr (ROWS)
         store_rows<T, CH, BV, PU>((T*)p.vnew + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, sVr, len);
@@ -414,7 +413,7 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
       hacc[i] *= dlast;
       mma_tile<T, CH, PT, 1, 1, PT>(hacc[i], sKdT + 16 * rb * PT, sVt + 16 * cb * PT);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   if (write_final && p.ht) {
@@ -430,82 +429,215 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
   }
 }
 
-// -------------------------------------------------------------- k_output --
-// One workgroup per (chunk, value head, V block of BV columns).
-template <typename T, int KD, int BV>
-__global__ __launch_bounds__(NTHR) void k_output(OutputParams p, int nvb) {
+// ---------------------------------------------------------------- k_fused --
+// The serial chunk recurrence fused with the output (the pages' second fused
+// forward kernel: FlashQLA curated summary, section
+// "平衡解決方案：雙核心融合與自動CP"): one 8-wave workgroup per (sequence,
+// value head, CP segment) covering all V columns, so W, K, Q and P are staged
+// once per chunk and the chunk states never leave the chip.  Per chunk:
+//   P^T = lower(D * K Q^T) * s      (from K and Q rows; skipped in warmup)
+//   Vnew = U - W h,  O = s Gamma (Q h) + P Vnew   (W h and Q h share B tiles)
+//   h' = Gamma_n h + (diag(e^{gamma_n - gamma}) K)^T Vnew
+// Waves: output tiles (rows 16*(w%4), column half w/4); state tiles 8 per wave.
+template <typename T, int KD>
+__global__ __launch_bounds__(512) void k_fused(FusedParams p, int total_items) {
+  constexpr int NT = 512, NW = 8;
   constexpr int VD = KD;
   constexpr int PK = Pitch<T, KD>::value;
   constexpr int PT = Pitch<T, CH>::value;
-  constexpr int PO = Pitch<T, BV>::value;
-  constexpr int NCB = BV / 16;
+  constexpr int NKB = KD / 16, NVB = VD / 16;
+  constexpr int NST = NKB * NVB;
+  constexpr int HT = (NST + NW - 1) / NW;
+  constexpr int OCB = NVB / 2;
+  static_assert(NVB % 2 == 0, "V must split into two column halves");
+  __shared__ __align__(16) T sW[CH * PK];     // W rows; O staging after W h
   __shared__ __align__(16) T sQ[CH * PK];
-  __shared__ __align__(16) T sK[CH * PK];   // reused as the O staging tile
-  __shared__ __align__(16) T shT[BV * PK];
-  __shared__ __align__(16) T sVnT[BV * PT];
-  __shared__ __align__(16) T sP[CH * PT];
+  __shared__ __align__(16) T sK[CH * PK];
+  __shared__ __align__(16) T sU[CH * PK];
+  __shared__ __align__(16) T sKdT[KD * PT];   // e^{gamma_n - gamma_t} k_t[d] as [d][t]
+  __shared__ __align__(16) T shT[VD * PK];    // h[d][v] as [v][d]
+  __shared__ __align__(16) T sVt[VD * PT];    // Vnew[t][v] as [v][t]
+  __shared__ __align__(16) T sP[CH * PT];     // s P[t][s] rows
   __shared__ float sG[CH];
 
   const SeqTables& s = p.s;
-  const int total = s.NTtot * p.Hv * nvb;
-  const int u = xcd_remap(blockIdx.x, total);
-  if (u >= total) return;
-  const int vb = u % nvb, h = (u / nvb) % p.Hv, c = u / (nvb * p.Hv);
-  int n, t0, len;
-  if (!locate_chunk(s, c, n, t0, len)) return;
+  const int u = xcd_remap(blockIdx.x, total_items);
+  if (u >= total_items) return;
+  const int h = u % p.Hv;
+  const int item = u / p.Hv;
+  const int n = find_seq(s.seg_off, s.N, item);
+  const int pseg = item - s.seg_off[n];
+  const int nseg = s.seg_off[n + 1] - s.seg_off[n];
+  const int c0 = s.chunk_off[n];
+  const int nch = s.chunk_off[n + 1] - c0;
+  if (pseg < 0 || pseg >= nseg || c0 < 0 || c0 + nch > s.NTtot) return;
+  const int L = p.seg_chunks;
   const int hk = h / (p.Hv / p.Hq);
-  const int w = wave_id();
+  const int w = wave_id(), l = lane_id();
+  const int orb = w & 3, ocol = (w >> 2) * OCB;   // output row block, first column tile
 
-  {
-    TileRegs<T, CH, KD> rq, rk;
-    TileRegs<T, BV, KD> rh;
-    TileRegs<T, BV, CH> rvn;
-    rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-    rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-    rh.load((const T*)p.hbuf + (((long)h * s.NTtot + c) * VD + vb * BV) * KD, KD, BV);
-    rvn.load((const T*)p.vnew + (((long)h * s.NTtot + c) * VD + vb * BV) * CH, CH, BV);
-    if (threadIdx.x < CH) sG[threadIdx.x] = p.gcum[(long)h * s.Ttot + t0 + min((int)threadIdx.x, len - 1)];
-    rq.template store<PK>(sQ);
-    rk.template store<PK>(sK);
-    rh.template store<PK>(shT);
-    rvn.template store<PT>(sVnT);
+  int ok = 1;
+  for (int q = 1 + (int)threadIdx.x; q < nseg; q += NT) {
+    const int ws = q * L - p.warmup;
+    if (ws > 0) {
+      float sum = 0.f;
+      for (int cc = ws; cc < q * L; ++cc) sum += p.cert[(long)h * s.NTtot + c0 + cc];
+      if (!(sum <= p.log_eps)) ok = 0;
+    }
   }
-  __syncthreads();
+  const bool certified = !__syncthreads_or(!ok);
+  int cstart, cbeg, cend;
+  bool write_final;
+  if (!certified) {
+    if (pseg != 0) return;             // segment 0 runs the whole head serially
+    cstart = 0; cbeg = 0; cend = nch; write_final = true;
+  } else {
+    cbeg = pseg * L;
+    cend = min(cbeg + L, nch);
+    cstart = (pseg == 0) ? 0 : max(0, cbeg - p.warmup);
+    write_final = (pseg == nseg - 1);
+  }
 
-  // P = lower(D * Q K^T) (diagonal included), formed as P^T = K Q^T so that
-  // each lane writes four consecutive key positions of one row of P.
-  for (int j = 0; j < 4; ++j) {
-    f32x4 a = zero4();
-    if (j >= w) {
-      mma_tile<T, KD, PK, 1, 1, PK>(a, sK + 16 * w * PK, sQ + 16 * j * PK);
+  f32x4 hacc[HT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int sidx = 16 * w + acc_row(e), t = 16 * j + acc_col();
-        a[e] = (t >= sidx) ? __expf(sG[t] - sG[sidx]) * a[e] : 0.f;
+  for (int i = 0; i < HT; ++i) {
+    const int ti = w * HT + i, rb = ti / NVB, cb = ti % NVB;
+    hacc[i] = zero4();
+    if (ti < NST && cstart == 0 && p.h0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hacc[i][e] = p.h0[(((long)n * p.Hv + h) * KD + 16 * rb + acc_row(e)) * VD + 16 * cb + acc_col()];
+    }
+  }
+
+  TileRegs<T, CH, KD, NT> rw, ru;
+  TileCols<T, KD, NW> rq, rk;
+  float gam_next = 0.f, glast_next = 0.f;
+  auto prefetch = [&](int jc) {
+    const int t0 = s.cu[n] + jc * CH;
+    const int len = min(CH, s.cu[n + 1] - t0);
+    rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
+    ru.load((const T*)p.U + ((long)h * s.Ttot + t0) * VD, VD, len);
+    rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    if (jc >= cbeg) rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
+    const float* gc = p.gcum + (long)h * s.Ttot + t0;
+    glast_next = gc[len - 1];
+    gam_next = (l < len) ? gc[l] : glast_next;
+  };
+  if (cstart < cend) prefetch(cstart);
+
+  for (int jc = cstart; jc < cend; ++jc) {
+    const int t0 = s.cu[n] + jc * CH;
+    const int len = min(CH, s.cu[n + 1] - t0);
+    if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) break;
+    const bool warm = jc < cbeg;
+    const float glast = glast_next, gam = gam_next;
+    rw.template store<PK>(sW);
+    ru.template store<PK>(sU);
+    rk.template store_t<PT>(sKdT, (l < len) ? __expf(glast - gam) : 0.f);
+    if (!warm) {
+      rk.template store<PK>(sK);
+      rq.template store<PK>(sQ);
+    }
+    if (w == 0) sG[l] = gam;
+#pragma unroll
+    for (int i = 0; i < HT; ++i) {
+      const int ti = w * HT + i;
+      if (ti < NST) acc_store_t<T, PK>(shT, 16 * (ti / NVB), 16 * (ti % NVB), hacc[i]);
+    }
+    lds_barrier();
+    if (jc + 1 < cend) prefetch(jc + 1);
+
+    if (!warm) {  // s P as rows [t][s], from P^T tiles (s-block w%4, t-blocks of this half)
+      const int is = w & 3, jt0 = 2 * (w >> 2);
+      f32x4 a2[2] = {zero4(), zero4()};
+      mma_row<T, KD, 2, PK, 1, 1, PK>(a2, sK + 16 * is * PK, sQ + 16 * jt0 * PK);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jt = jt0 + jj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sidx = 16 * is + acc_row(e), t = 16 * jt + acc_col();
+          a2[jj][e] = (t >= sidx) ? p.scale * __expf(sG[t] - sG[sidx]) * a2[jj][e] : 0.f;
+        }
+        acc_store_t<T, PT>(sP, 16 * is, 16 * jt, a2[jj]);
       }
     }
-    acc_store_t<T, PT>(sP, 16 * w, 16 * j, a);
-  }
-  __syncthreads();
+    f32x4 oacc[OCB];
+    {  // Vnew = U - W h and (if not warm) Q h, sharing the h^T operand tiles
+      f32x4 vacc[OCB];
+#pragma unroll
+      for (int j = 0; j < OCB; ++j) { vacc[j] = zero4(); oacc[j] = zero4(); }
+      constexpr int KS = Mma<T>::KSTEP;
+#pragma unroll
+      for (int k0 = 0; k0 < KD; k0 += KS) {
+        const auto fw = Mma<T>::template load<PK, 1>(sW + 16 * orb * PK + k0);
+        const auto fq = Mma<T>::template load<PK, 1>(sQ + 16 * orb * PK + k0);
+#pragma unroll
+        for (int j = 0; j < OCB; ++j) {
+          const auto fb = Mma<T>::template load<PK, 1>(shT + 16 * (ocol + j) * PK + k0);
+          vacc[j] = Mma<T>::op(fw, fb, vacc[j]);
+          if (!warm) oacc[j] = Mma<T>::op(fq, fb, oacc[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < OCB; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vacc[j][e] = to_f(sU[(16 * orb + acc_row(e)) * PK + 16 * (ocol + j) + acc_col()]) - vacc[j][e];
+        acc_store_t<T, PT>(sVt, 16 * orb, 16 * (ocol + j), vacc[j]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float gm = p.scale * __expf(sG[16 * orb + acc_row(e)]);
+#pragma unroll
+        for (int j = 0; j < OCB; ++j) oacc[j][e] *= gm;
+      }
+    }
+    lds_barrier();
 
-  f32x4 acc[NCB];
+    if (!warm) {  // O += s P Vnew, staged as rows in sW
+      mma_row<T, CH, OCB, PT, 1, 1, PT>(oacc, sP + 16 * orb * PT, sVt + 16 * ocol * PT, 16 * (orb + 1));
 #pragma unroll
-  for (int j = 0; j < NCB; ++j) acc[j] = zero4();
-  mma_row<T, KD, NCB, PK, 1, 1, PK>(acc, sQ + 16 * w * PK, shT);
+      for (int j = 0; j < OCB; ++j)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float gm = __expf(sG[16 * w + acc_row(e)]);
+        for (int e = 0; e < 4; ++e)
+          sW[(16 * orb + acc_row(e)) * PK + 16 * (ocol + j) + acc_col()] = from_f<T>(oacc[j][e]);
+    }
+    const float dlast = __expf(glast);
+    if constexpr (HT * NW == NST && NVB % HT == 0) {
+      const int ti0 = w * HT;
 #pragma unroll
-    for (int j = 0; j < NCB; ++j) acc[j][e] *= gm;
+      for (int i = 0; i < HT; ++i) hacc[i] *= dlast;
+      mma_row<T, CH, HT, PT, 1, 1, PT>(hacc, sKdT + 16 * (ti0 / NVB) * PT, sVt + 16 * (ti0 % NVB) * PT);
+    } else {
+#pragma unroll
+      for (int i = 0; i < HT; ++i) {
+        const int ti = w * HT + i;
+        if (ti < NST) {
+          hacc[i] *= dlast;
+          mma_tile<T, CH, PT, 1, 1, PT>(hacc[i], sKdT + 16 * (ti / NVB) * PT, sVt + 16 * (ti % NVB) * PT);
+        }
+      }
+    }
+    lds_barrier();
+    if (!warm) {
+      store_rows<T, CH, VD, PK, NT>((T*)p.o + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, sW, len);
+      lds_barrier();
+    }
   }
-  mma_row<T, CH, NCB, PT, 1, 1, PT>(acc, sP + 16 * w * PT, sVnT, 16 * (w + 1));
-  T* sO = sK;
+
+  if (write_final && p.ht) {
 #pragma unroll
-  for (int j = 0; j < NCB; ++j)
+    for (int i = 0; i < HT; ++i) {
+      const int ti = w * HT + i, rb = ti / NVB, cb = ti % NVB;
+      if (ti < NST) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sO[(16 * w + acc_row(e)) * PO + 16 * j + acc_col()] = from_f<T>(p.scale * acc[j][e]);
-  __syncthreads();
-  store_rows<T, CH, BV, PO>((T*)p.o + ((long)t0 * p.Hv + h) * VD + vb * BV, (long)p.Hv * VD, sO, len);
+        for (int e = 0; e < 4; ++e)
+          p.ht[(((long)n * p.Hv + h) * KD + 16 * rb + acc_row(e)) * VD + 16 * cb + acc_col()] = hacc[i][e];
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------- launchers --
@@ -538,19 +670,18 @@ template <typename T, int KD, int BV>
 static hipError_t state_impl(const StateParams& p, int total_segs, bool rows, hipStream_t st) {
   hipError_t err;
   const int total = total_segs * p.Hv * p.nvb;
-  if (rows)
-    GDR_LAUNCH("chunk_state_rows", (k_state<T, KD, BV, true>), dim3(padded_grid(total)), st, p, total);
-  else
-    GDR_LAUNCH("chunk_state", (k_state<T, KD, BV, false>), dim3(padded_grid(total)), st, p, total);
+  if (!rows) return hipErrorInvalidValue;
+  GDR_LAUNCH("chunk_state_rows", (k_state<T, KD, BV, true>), dim3(padded_grid(total)), st, p, total);
   return err;
 }
 
 template <typename T, int KD>
-static hipError_t output_impl(const OutputParams& p, hipStream_t st) {
-  hipError_t err;
-  constexpr int BV = KD == 128 ? 64 : KD;
-  const int nvb = KD / BV;
-  GDR_LAUNCH("chunk_output", (k_output<T, KD, BV>), dim3(padded_grid((long)p.s.NTtot * p.Hv * nvb)), st, p, nvb);
+static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t st) {
+  const int total = total_segs * p.Hv;
+  timing_before("chunk_fused", st);
+  hipLaunchKernelGGL((k_fused<T, KD>), dim3(padded_grid(total)), dim3(512), 0, st, p, total);
+  hipError_t err = hipGetLastError();
+  timing_after(st);
   return err;
 }
 
@@ -579,14 +710,14 @@ hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int tota
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_output(DType dt, int KD, const OutputParams& p, hipStream_t st) {
+hipError_t launch_fused(DType dt, int KD, const FusedParams& p, int total_segs, hipStream_t st) {
   if (dt == DType::BF16) {
-    if (KD == 32) return output_impl<bf16, 32>(p, st);
-    if (KD == 64) return output_impl<bf16, 64>(p, st);
-    if (KD == 128) return output_impl<bf16, 128>(p, st);
+    if (KD == 32) return fused_impl<bf16, 32>(p, total_segs, st);
+    if (KD == 64) return fused_impl<bf16, 64>(p, total_segs, st);
+    if (KD == 128) return fused_impl<bf16, 128>(p, total_segs, st);
   } else {
-    if (KD == 32) return output_impl<float, 32>(p, st);
-    if (KD == 64) return output_impl<float, 64>(p, st);
+    if (KD == 32) return fused_impl<float, 32>(p, total_segs, st);
+    if (KD == 64) return fused_impl<float, 64>(p, total_segs, st);
   }
   return hipErrorInvalidValue;
 }

@@ -64,13 +64,16 @@ struct StateParams {
   int nvb;                   // V blocks per head
 };
 
-struct OutputParams {
+struct FusedParams {         // forward state recurrence fused with the output
   SeqTables s;
-  const void *q, *k, *hbuf, *vnew;
-  const float* gcum;
+  const void *q, *k, *W, *U;
+  const float *gcum, *cert;
+  const float* h0;           // nullable [N][Hv][K][V]
+  float* ht;                 // nullable [N][Hv][K][V]
   void* o;                   // [Ttot][Hv][V]
   int Hq, Hv;
-  float scale;
+  int seg_chunks, warmup;
+  float log_eps, scale;
 };
 
 struct DStateParams {        // reverse state pass
@@ -101,7 +104,7 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_intra(DType dt, int KD, const IntraParams& p, hipStream_t st);
 hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int total_segs, bool rows,
                         hipStream_t st);
-hipError_t launch_output(DType dt, int KD, const OutputParams& p, hipStream_t st);
+hipError_t launch_fused(DType dt, int KD, const FusedParams& p, int total_segs, hipStream_t st);
 hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, int total_items, hipStream_t st);
 hipError_t launch_grads(DType dt, int KD, const GradParams& p, hipStream_t st);
 

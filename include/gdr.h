@@ -100,7 +100,7 @@ typedef struct {
   int32_t num_seqs;          /* N */
   int32_t total_chunks;      /* sum over sequences of ceil(len / 64) */
   int32_t max_chunks;        /* longest sequence, in chunks */
-  int32_t v_blocks;          /* state column blocks per head (V / block width) */
+  int32_t v_blocks;          /* state column blocks per workgroup of the state pass */
   int32_t segment_chunks;    /* chunks per CP segment (>= max_chunks: no CP) */
   int32_t warmup_chunks;     /* warmup chunks per segment (0 without CP) */
   int32_t total_segments;    /* sum over sequences of ceil(chunks / segment_chunks) */

@@ -118,7 +118,7 @@ def plan(B, T, Hq, Hv, K, cu=None, mode=gdr.CP_AUTO, seg=0, warm=0):
 
 def test_planner_cp_for_few_heads_long_context():
     info = plan(1, 65536, 4, 8, 128)
-    assert info["total_chunks"] == 1024 and info["v_blocks"] == 2
+    assert info["total_chunks"] == 1024 and info["v_blocks"] == 1
     assert info["segment_chunks"] < 1024 and info["warmup_chunks"] == 8
     assert info["state_workgroups"] >= 256         # fills the 256 CUs
 
