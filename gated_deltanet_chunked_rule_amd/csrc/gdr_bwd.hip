@@ -110,16 +110,18 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
   TileCols<T, KD> rq, rk, rw;
   TileCols<T, BV> rdo;
   float gam_next = 0.f, glast_next = 0.f;
-  auto prefetch = [&](int jc) {
-    const int t0 = s.cu[n] + jc * CH;
-    const int len = min(CH, s.cu[n + 1] - t0);
+  auto prefetch = [&](int jc) {  // unconditional; empty range before the first chunk
+    const bool valid = jc >= 0;
+    const int t0 = s.cu[n] + max(jc, 0) * CH;
+    const int len = valid ? min(CH, s.cu[n + 1] - t0) : 0;
     rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
     rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
     rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
     rdo.load((const T*)p.d_o + ((long)t0 * p.Hv + h) * VD + vb * BV, (long)p.Hv * VD, len);
-    const float* gc = p.gcum + (long)h * s.Ttot + t0;
-    glast_next = gc[len - 1];
-    gam_next = (l < len) ? gc[l] : glast_next;
+    const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
+    glast_next = buf_load_f32(gr, (uint32_t)(len - 1) * 4u);
+    const float gv = buf_load_f32(gr, (uint32_t)l * 4u);
+    gam_next = (l < len) ? gv : glast_next;
   };
   if (nch > 0) prefetch(nch - 1);
 
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
       for (int e = 0; e < 4; ++e) sdhr[(16 * rb + acc_row(e)) * PU + 16 * cb + acc_col()] = from_f<T>(hacc[i][e]);
     }
     lds_barrier();
-    if (jc > 0) prefetch(jc - 1);
+    prefetch(jc - 1);
     store_rows<T, KD, BV, PU>((T*)p.dhbuf + ((long)h * s.NTtot + gc) * KD * VD + vb * BV, VD, sdhr, KD);
 
     // s P^T as [s][t]: tiles of P = lower(D * Q K^T) with t-block w.

@@ -26,7 +26,9 @@ constexpr int NTHR = 256;   // threads per workgroup
 constexpr int NWAVE = 4;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// The wave index is wave-uniform: read it into a scalar register so that
+// branches and addresses derived from it stay scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Orders LDS traffic between the lanes of one wave (no workgroup barrier).
 __device__ __forceinline__ void wave_sync() {
@@ -49,6 +51,32 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return static_cast<T>(x); }
+
+// ------------------------------------------------------- raw buffers --
+// Tile loads and stores go through raw buffer descriptors whose record count
+// covers exactly the tile's valid rows: the hardware returns zero for loads
+// and drops stores outside that range, so partial chunks need no per-row
+// branches, and offsets are 32-bit.  Word 3 is the gfx9-family default.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  uint4 u;
+  __builtin_memcpy(&u, &v, 16);
+  return u;
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 u) {
+  decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)) v;
+  __builtin_memcpy(&v, &u, 16);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 
 // LDS row pitch (elements) for a row of D elements: +16 bytes keeps 16-byte
 // alignment and shifts consecutive rows by four banks.
@@ -141,12 +169,14 @@ struct TileRegs {
   static_assert(D % VEC == 0, "row length must be a multiple of 16 bytes");
   uint4 v[NV];
   __device__ __forceinline__ void load(const T* g, long gstride, int nrows) {
+    const rsrc_t rr = make_rsrc(g, (long)nrows * gstride * (long)sizeof(T));
+    const uint32_t rs = (uint32_t)(gstride * (long)sizeof(T));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int idx = (int)threadIdx.x + i * NTH;
-      const int r = idx / VPR, c = (idx % VPR) * VEC;
-      v[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < R * VPR && r < nrows) v[i] = *reinterpret_cast<const uint4*>(g + (long)r * gstride + c);
+      const int r = idx / VPR, c = idx % VPR;
+      if ((R * VPR) % NTH == 0 || idx < R * VPR) v[i] = buf_load16(rr, (uint32_t)r * rs + (uint32_t)c * 16u);
+      else v[i] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
   __device__ __forceinline__ int row(int i) const { return ((int)threadIdx.x + i * NTH) / VPR; }
@@ -186,12 +216,13 @@ struct TileCols {
   static constexpr int NV = (NCG + NW - 1) / NW;   // waves beyond NCG groups stay idle
   uint4 v[NV];
   __device__ __forceinline__ void load(const T* g, long gstride, int nrows) {
-    const int r = lane_id();
+    const rsrc_t rr = make_rsrc(g, (long)nrows * gstride * (long)sizeof(T));
+    const uint32_t off = (uint32_t)lane_id() * (uint32_t)(gstride * (long)sizeof(T));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int cg = wave_id() + NW * i;
-      v[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (cg < NCG && r < nrows) v[i] = *reinterpret_cast<const uint4*>(g + (long)r * gstride + cg * VEC);
+      if (NCG % NW == 0 || cg < NCG) v[i] = buf_load16(rr, off + (uint32_t)cg * 16u);
+      else v[i] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
   template <int P>
@@ -225,9 +256,12 @@ template <typename T, int R, int D, int P, int NTH = NTHR>
 __device__ __forceinline__ void store_rows(T* g, long gstride, const T* lds, int nrows) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int VPR = D / VEC;
+  const rsrc_t rr = make_rsrc(g, (long)nrows * gstride * (long)sizeof(T));
+  const uint32_t rs = (uint32_t)(gstride * (long)sizeof(T));
+#pragma unroll
   for (int i = threadIdx.x; i < R * VPR; i += NTH) {
-    const int r = i / VPR, c = (i % VPR) * VEC;
-    if (r < nrows) *reinterpret_cast<uint4*>(g + (long)r * gstride + c) = *reinterpret_cast<const uint4*>(lds + r * P + c);
+    const int r = i / VPR, c = i % VPR;
+    buf_store16(rr, (uint32_t)r * rs + (uint32_t)c * 16u, *reinterpret_cast<const uint4*>(lds + r * P + c * VEC));
   }
 }
 

@@ -342,15 +342,17 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
   TileRegs<T, CH, BV> ru;
   float gam = 0.f;
   float glast_next = 0.f;
-  auto prefetch = [&](int jc) {
-    const int t0 = s.cu[n] + jc * CH;
-    const int len = min(CH, s.cu[n + 1] - t0);
+  auto prefetch = [&](int jc) {  // unconditional; empty range past the segment
+    const bool valid = jc < cend;
+    const int t0 = s.cu[n] + min(jc, cend - 1) * CH;
+    const int len = valid ? min(CH, s.cu[n + 1] - t0) : 0;
     rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
     rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
     ru.load((const T*)p.U + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, len);
-    const float* gc = p.gcum + (long)h * s.Ttot + t0;
-    gam = (lane_id() < len) ? gc[lane_id()] : 0.f;
-    glast_next = gc[len - 1];
+    const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
+    const float gv = buf_load_f32(gr, (uint32_t)lane_id() * 4u);
+    gam = (lane_id() < len) ? gv : 0.f;
+    glast_next = buf_load_f32(gr, (uint32_t)(len - 1) * 4u);
   };
   if (cstart < cend) prefetch(cstart);
 
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
       }
     }
     lds_barrier();
-    if (jc + 1 < cend) prefetch(jc + 1);
+    prefetch(jc + 1);
     if (!warm && p.hbuf) {
       if constexpr (ROWS)
         store_rows<T, KD, BV, PU>((T*)p.hbuf + ((long)h * s.NTtot + gc) * KD * VD + vb * BV, VD, sHr, KD);
@@ -513,16 +515,22 @@ __global__ __launch_bounds__(512) void k_fused(FusedParams p, int total_items) {
   TileRegs<T, CH, KD, NT> rw, ru;
   TileCols<T, KD, NW> rq, rk;
   float gam_next = 0.f, glast_next = 0.f;
+  // Loads of chunk jc into registers.  Issued unconditionally (a chunk past
+  // the segment gets an empty range: zeros, no memory traffic) so that no
+  // control-flow join forces the compiler to wait for them early.
   auto prefetch = [&](int jc) {
-    const int t0 = s.cu[n] + jc * CH;
-    const int len = min(CH, s.cu[n + 1] - t0);
+    const bool valid = jc < cend;
+    const int t0 = s.cu[n] + min(jc, cend - 1) * CH;
+    const int len = valid ? min(CH, s.cu[n + 1] - t0) : 0;
+    const int lenq = (jc >= cbeg) ? len : 0;
     rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
     ru.load((const T*)p.U + ((long)h * s.Ttot + t0) * VD, VD, len);
     rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-    if (jc >= cbeg) rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-    const float* gc = p.gcum + (long)h * s.Ttot + t0;
-    glast_next = gc[len - 1];
-    gam_next = (l < len) ? gc[l] : glast_next;
+    rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, lenq);
+    const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
+    glast_next = buf_load_f32(gr, (uint32_t)(len - 1) * 4u);
+    const float gv = buf_load_f32(gr, (uint32_t)l * 4u);
+    gam_next = (l < len) ? gv : glast_next;
   };
   if (cstart < cend) prefetch(cstart);
 
@@ -546,7 +554,7 @@ __global__ __launch_bounds__(512) void k_fused(FusedParams p, int total_items) {
       if (ti < NST) acc_store_t<T, PK>(shT, 16 * (ti / NVB), 16 * (ti % NVB), hacc[i]);
     }
     lds_barrier();
-    if (jc + 1 < cend) prefetch(jc + 1);
+    prefetch(jc + 1);
 
     if (!warm) {  // s P as rows [t][s], from P^T tiles (s-block w%4, t-blocks of this half)
       const int is = w & 3, jt0 = 2 * (w >> 2);
@@ -569,16 +577,20 @@ __global__ __launch_bounds__(512) void k_fused(FusedParams p, int total_items) {
 #pragma unroll
       for (int j = 0; j < OCB; ++j) { vacc[j] = zero4(); oacc[j] = zero4(); }
       constexpr int KS = Mma<T>::KSTEP;
+      if (!warm) {
 #pragma unroll
-      for (int k0 = 0; k0 < KD; k0 += KS) {
-        const auto fw = Mma<T>::template load<PK, 1>(sW + 16 * orb * PK + k0);
-        const auto fq = Mma<T>::template load<PK, 1>(sQ + 16 * orb * PK + k0);
+        for (int k0 = 0; k0 < KD; k0 += KS) {
+          const auto fw = Mma<T>::template load<PK, 1>(sW + 16 * orb * PK + k0);
+          const auto fq = Mma<T>::template load<PK, 1>(sQ + 16 * orb * PK + k0);
 #pragma unroll
-        for (int j = 0; j < OCB; ++j) {
-          const auto fb = Mma<T>::template load<PK, 1>(shT + 16 * (ocol + j) * PK + k0);
-          vacc[j] = Mma<T>::op(fw, fb, vacc[j]);
-          if (!warm) oacc[j] = Mma<T>::op(fq, fb, oacc[j]);
+          for (int j = 0; j < OCB; ++j) {
+            const auto fb = Mma<T>::template load<PK, 1>(shT + 16 * (ocol + j) * PK + k0);
+            vacc[j] = Mma<T>::op(fw, fb, vacc[j]);
+            oacc[j] = Mma<T>::op(fq, fb, oacc[j]);
+          }
         }
+      } else {
+        mma_row<T, KD, OCB, PK, 1, 1, PK>(vacc, sW + 16 * orb * PK, shT + 16 * ocol * PK);
       }
 #pragma unroll
       for (int j = 0; j < OCB; ++j) {
