@@ -49,6 +49,19 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Workgroup-wide OR of a per-thread flag through LDS (flags[NW] scratch),
+// without the memory fence of __syncthreads_or.
+template <int NW>
+__device__ __forceinline__ bool lds_any(int pred, int* flags) {
+  const bool wave_any = __builtin_amdgcn_ballot_w64(pred != 0) != 0;
+  if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = wave_any ? 1 : 0;
+  lds_barrier();
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) any |= flags[i];
+  return any != 0;
+}
+
 template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return static_cast<T>(x); }
 

@@ -24,6 +24,7 @@
 // curated summary, section "平衡解決方案：雙核心融合與自動CP"; Tongyi page,
 // section "FlashQLAの主な利点").
 #include <math.h>
+#include <algorithm>
 #include <type_traits>
 
 #include "gdr_device.h"
@@ -87,11 +88,19 @@ __device__ __forceinline__ bool locate_chunk(const SeqTables& s, int c, int& n, 
 }
 
 // --------------------------------------------------------------- k_intra --
-// One workgroup per (chunk, value head).  LDS regions are reused across the
+// Persistent: each workgroup walks a contiguous range of (chunk, value head)
+// items (value heads of one chunk adjacent, so the shared K tile is an L2
+// hit) and fetches the next item's K, V, g and beta into a second register
+// set while the current one is computed.  LDS regions are reused across the
 // phases (A: K rows -> (b Gamma K)^T -> W staging; B: inverse scratch ->
 // (b V)^T -> U staging; C: L -> A in the working dtype; D: A in fp32).
+struct IntraItem {
+  int c, h, hk, n, t0, len;
+  bool ok;
+};
+
 template <typename T, int KD>
-__global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
+__global__ __launch_bounds__(NTHR) void k_intra(IntraParams p, int total_items, int per_wg, int nwg) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
   constexpr int PK = Pitch<T, KD>::value;     // row-major K / W / U rows
@@ -106,6 +115,7 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
   static_assert(CH * PT * (int)sizeof(T) <= SZ_C, "A tile must fit region C");
   __shared__ __align__(16) char smem[SZ_A + SZ_B + SZ_C + SZ_D];
   __shared__ float sG[CH], sB[CH];
+  __shared__ int sFlag[NWAVE];
   T* rA = reinterpret_cast<T*>(smem);
   T* rB = reinterpret_cast<T*>(smem + SZ_A);
   float* sL = reinterpret_cast<float*>(smem + SZ_A + SZ_B);
@@ -114,31 +124,46 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
   float* sX = reinterpret_cast<float*>(rB);
 
   const SeqTables& s = p.s;
-  const int u = xcd_remap(blockIdx.x, s.NTtot * p.Hv);
-  if (u >= s.NTtot * p.Hv) return;
-  const int c = u / p.Hv, h = u % p.Hv;
-  int n, t0, len;
-  if (!locate_chunk(s, c, n, t0, len)) return;
-  const int hk = h / (p.Hv / p.Hq);
+  const int x = xcd_remap(blockIdx.x, nwg);
+  const int u0 = x * per_wg, u1 = min(total_items, u0 + per_wg);
+  if (u0 >= u1) return;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
 
-  TileCols<T, KD> rk;
-  TileCols<T, VD> rv;
-  rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-  rv.load((const T*)p.v + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, len);
-  if (w == 0) {
-    const float gv = (l < len) ? p.g[(long)(t0 + l) * p.Hv + h] : 0.f;
-    const float bv = (l < len) ? p.beta[(long)(t0 + l) * p.Hv + h] : 0.f;
-    const float gc = wave_inclusive_scan(gv);
-    sG[l] = gc;
-    sB[l] = bv;
-    if (l < len) {
-      p.gcum[(long)h * s.Ttot + t0 + l] = gc;
-      if (p.g_cum_out) p.g_cum_out[(long)(t0 + l) * p.Hv + h] = gc;
+  auto locate = [&](int u, IntraItem& it) {
+    it.ok = false;
+    if (u >= u1) return;
+    it.c = u / p.Hv;
+    it.h = u % p.Hv;
+    it.hk = it.h / (p.Hv / p.Hq);
+    it.ok = locate_chunk(s, it.c, it.n, it.t0, it.len);
+  };
+  // Loads of one item (an invalid item gets empty ranges: zeros, no traffic).
+  auto fetch = [&](const IntraItem& it, TileCols<T, KD>& rk, TileCols<T, VD>& rv, float& gv, float& bv) {
+    const int len = it.ok ? it.len : 0;
+    const int t0 = it.ok ? it.t0 : 0;
+    rk.load((const T*)p.k + ((long)t0 * p.Hq + it.hk) * KD, (long)p.Hq * KD, len);
+    rv.load((const T*)p.v + ((long)t0 * p.Hv + it.h) * VD, (long)p.Hv * VD, len);
+    const rsrc_t gr = make_rsrc(p.g + (long)t0 * p.Hv + it.h, (long)len * p.Hv * 4);
+    const rsrc_t br = make_rsrc(p.beta + (long)t0 * p.Hv + it.h, (long)len * p.Hv * 4);
+    gv = buf_load_f32(gr, (uint32_t)(l * p.Hv) * 4u);
+    bv = buf_load_f32(br, (uint32_t)(l * p.Hv) * 4u);
+  };
+
+  auto run = [&](const IntraItem& it, TileCols<T, KD>& rk, TileCols<T, VD>& rv, float gvc, float bvc,
+                 const IntraItem& nx, TileCols<T, KD>& rkn, TileCols<T, VD>& rvn, float& gvn, float& bvn) {
+    const int t0 = it.t0, len = it.len, h = it.h;
+    if (w == 0) {
+      const float gc = wave_inclusive_scan((l < len) ? gvc : 0.f);
+      sG[l] = gc;
+      sB[l] = (l < len) ? bvc : 0.f;
+      if (l < len) {
+        p.gcum[(long)h * s.Ttot + t0 + l] = gc;
+        if (p.g_cum_out) p.g_cum_out[(long)(t0 + l) * p.Hv + h] = gc;
+      }
     }
-  }
-  rk.template store<PK>(rA);
-  __syncthreads();
+    rk.template store<PK>(rA);
+    lds_barrier();
+    fetch(nx, rkn, rvn, gvn, bvn);
 
   // L = strict_lower(diag(b) (D * K K^T)); the diagonal of K K^T certifies
   // 0 <= b |k|^2 <= 2 (non-expansive steps) for the context-parallel warmup.
@@ -158,8 +183,8 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
       sL[r * PL + cc] = lv;
     }
   }
-  const int any_bad = __syncthreads_or(bad);
-  if (tid == 0) p.cert[(long)h * s.NTtot + c] = any_bad ? INFINITY : sG[len - 1];
+  const int any_bad = lds_any<NWAVE>(bad, sFlag);
+  if (tid == 0) p.cert[(long)h * s.NTtot + it.c] = any_bad ? INFINITY : sG[len - 1];
 
   if (p.A_in) {
     for (int i = tid; i < CH * CH; i += NTHR) {
@@ -168,7 +193,7 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
       if (r < len) a = (cc < len) ? p.A_in[((long)(t0 + r) * p.Hv + h) * CH + cc] : 0.f;
       sA[r * PL + cc] = a;
     }
-    __syncthreads();
+    lds_barrier();
   } else {
     // Blocked inverse of the unit lower triangular I + L in fp32: diagonal
     // 16x16 blocks by forward substitution (one wave each) ...
@@ -189,7 +214,7 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
       const int r = i / CH, cc = i % CH;
       if ((cc >> 4) > (r >> 4)) sA[r * PL + cc] = 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     // ... then the off-diagonal blocks by distance from the diagonal:
     // A_ij = -A_ii * sum_{j <= m < i} L_im A_mj.
     for (int d = 1; d < 4; ++d) {
@@ -207,7 +232,7 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sA[(16 * i + acc_row(e)) * PL + 16 * j + acc_col()] = -yacc[e];
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 
@@ -233,7 +258,7 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
       *reinterpret_cast<bf16x4*>(sAt + r * PT + cc) = pk;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // W^T = (b Gamma K)^T A^T and U^T = (b V)^T A^T; A is lower triangular, so
   // output column block j only contracts over tokens < 16 (j + 1).
@@ -248,16 +273,34 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p) {
     mma_tile<T, CH, PT, 1, 1, PT>(wacc[i], rA + 16 * rb * PT, sAt + 16 * cb * PT, 16 * (cb + 1));
     mma_tile<T, CH, PT, 1, 1, PT>(uacc[i], rB + 16 * rb * PT, sAt + 16 * cb * PT, 16 * (cb + 1));
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int ti = w * TPW + i, rb = ti / 4, cb = ti % 4;
     acc_store_t<T, PK>(rA, 16 * rb, 16 * cb, wacc[i]);
     acc_store_t<T, PK>(rB, 16 * rb, 16 * cb, uacc[i]);
   }
-  __syncthreads();
+  lds_barrier();
   store_rows<T, CH, KD, PK>((T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, rA, len);
   store_rows<T, CH, VD, PK>((T*)p.U + ((long)h * s.Ttot + t0) * VD, VD, rB, len);
+    lds_barrier();   // staging regions are rewritten by the next item
+  };
+
+  IntraItem cur, nxt;
+  TileCols<T, KD> rk0, rk1;
+  TileCols<T, VD> rv0, rv1;
+  float g0 = 0.f, b0 = 0.f, g1 = 0.f, b1 = 0.f;
+  locate(u0, cur);
+  fetch(cur, rk0, rv0, g0, b0);
+  for (int u = u0; u < u1; u += 2) {
+    locate(u + 1, nxt);
+    if (cur.ok) run(cur, rk0, rv0, g0, b0, nxt, rk1, rv1, g1, b1);
+    else fetch(nxt, rk1, rv1, g1, b1);
+    if (u + 1 >= u1) break;
+    locate(u + 2, cur);
+    if (nxt.ok) run(nxt, rk1, rv1, g1, b1, cur, rk0, rv0, g0, b0);
+    else fetch(cur, rk0, rv0, g0, b0);
+  }
 }
 
 // --------------------------------------------------------------- k_state --
@@ -674,7 +717,11 @@ static unsigned padded_grid(long total) { return (unsigned)(((total + 7) / 8) * 
 template <typename T, int KD>
 static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
   hipError_t err;
-  GDR_LAUNCH("intra_wy", (k_intra<T, KD>), dim3(padded_grid((long)p.s.NTtot * p.Hv)), st, p);
+  // persistent grid: two workgroups per CU, each over a contiguous item range
+  const long total = (long)p.s.NTtot * p.Hv;
+  const int nwg = (int)std::min<long>(padded_grid(total), 2 * 256);
+  const int per_wg = (int)((total + nwg - 1) / nwg);
+  GDR_LAUNCH("intra_wy", (k_intra<T, KD>), dim3(nwg), st, p, (int)total, per_wg, nwg);
   return err;
 }
 
