@@ -19,6 +19,8 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_long_context.json")
 MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 MFMA
 METRIC = "GDN chunked-prefill fwd tokens/s (B=1,T=64K,Hv=8) + % MFMA/HBM roofline"
 
@@ -39,6 +41,34 @@ def per_kernel_work(w, G):
         "chunk_output": (2 * K * e / G + K * V * e / C + V * e + 4 + V * e,
                          2 * C * K + 2 * K * V + 2 * C * V),
     }
+
+
+def sources_sha256() -> str:
+    """Hash of the kernel sources; counter-derived traffic is valid only for it."""
+    import hashlib
+    d = os.path.join(ROOT, "gated_deltanet_chunked_rule_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what
+    the counter reads for a device copy of known size), or None when the
+    summary is missing or was taken on different kernel sources."""
+    import json
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256() or kernel not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel]
+    return 1024.0 * (k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"])
 
 
 def main():
@@ -68,7 +98,6 @@ def main():
     G = w.Hv // w.Hq
     plan = gdr.gdr_chunk_fwd_plan(q, v)
     # workspace allocated once, outside the timed region
-    o, ht, _, _ = gdr.gdr_chunk_fwd(q, k, v, g, beta, scale)
     ws = torch.empty(gdr.fwd_workspace_bytes(q, v), device=dev, dtype=torch.uint8)
 
     def step():
@@ -114,7 +143,7 @@ def main():
         roof = {"bound": "mfma", "achieved": flops_tv * tv / (avg_ms * 1e-3) / 1e12,
                 "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["kernel_avg_us"] = avg_ms * 1e3
 
