@@ -34,12 +34,9 @@ def per_kernel_work(w, G):
         # k, v, g, beta in; W, U, g_cum out; K K^T, A W-solve, A U-solve (+inverse)
         "intra_wy": (K * e / G + V * e + 8 + (K + V) * e + 4,
                      2 * C * K + 2 * C * K + 2 * C * V + C * C // 3),
-        # W, U, k, g_cum in; Vnew and the chunk entry state out
-        "chunk_state": (K * e + V * e + K * e / G + 4 + V * e + K * V * e / C,
-                        4 * K * V),
-        # q, k, chunk state, Vnew, g_cum in; o out
-        "chunk_output": (2 * K * e / G + K * V * e / C + V * e + 4 + V * e,
-                         2 * C * K + 2 * K * V + 2 * C * V),
+        # W, U, k, q, g_cum in; o out (states and Vnew stay on chip)
+        "chunk_fused": (K * e + V * e + 2 * K * e / G + 4 + V * e,
+                        4 * K * V + 2 * K * V + 2 * C * K + 2 * C * V),
     }
 
 

@@ -196,6 +196,7 @@ gdr::SeqTables tables(const Problem& P, const Layout& Lo, char* ws) {
   s.N = P.N;
   s.Ttot = P.Ttot;
   s.NTtot = P.NTtot;
+  s.T_uniform = P.packed ? 0 : P.T;
   return s;
 }
 

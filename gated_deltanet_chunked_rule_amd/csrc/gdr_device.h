@@ -263,6 +263,105 @@ struct TileCols {
   }
 };
 
+// A 64-row tile loaded like TileCols (lane l of every wave on row l) but with
+// wave w holding the contiguous 16-byte column groups [w*NV, (w+1)*NV), i.e.
+// elements [w*D/4, (w+1)*D/4) of its row.  store_perm() writes it to LDS with
+// the columns permuted: element d of a row goes to column 16*(d % NT) + d / NT
+// (NT = D / 16).  The 16 columns of MFMA column tile j then hold the elements
+// {NT*c + j : c < 16}, so the accumulators that one lane holds over the NT
+// column tiles of a product X * tile are NT consecutive elements of one output
+// row, which go back to memory as a single vector store.  Each lane writes
+// NT pieces of 4 elements (8 bytes in bf16).
+template <typename T, int D>
+struct RowSlab {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int NV = D / VEC / NWAVE;
+  static constexpr int NT = D / 16;
+  static_assert(NV >= 1 && D % (VEC * NWAVE) == 0, "row must split into 16-byte groups over the waves");
+  uint4 v[NV];
+  __device__ __forceinline__ void load(const T* g, long gstride, int nrows) {
+    const rsrc_t rr = make_rsrc(g, (long)nrows * gstride * (long)sizeof(T));
+    const uint32_t off = (uint32_t)lane_id() * (uint32_t)(gstride * (long)sizeof(T)) + (uint32_t)(wave_id() * NV * 16);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = buf_load16(rr, off + (uint32_t)i * 16u);
+  }
+  template <int P>
+  __device__ __forceinline__ void store_perm(T* lds) const {
+    T* row = lds + lane_id() * P + 4 * wave_id();
+    if constexpr (sizeof(T) == 2) {
+      const uint16_t* e = reinterpret_cast<const uint16_t*>(v);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        uint2 pk;
+        pk.x = (uint32_t)e[j] | ((uint32_t)e[j + NT] << 16);
+        pk.y = (uint32_t)e[j + 2 * NT] | ((uint32_t)e[j + 3 * NT] << 16);
+        *reinterpret_cast<uint2*>(row + 16 * j) = pk;
+      }
+    } else {
+      const uint32_t* e = reinterpret_cast<const uint32_t*>(v);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        *reinterpret_cast<uint4*>(row + 16 * j) = make_uint4(e[j], e[j + NT], e[j + 2 * NT], e[j + 3 * NT]);
+    }
+  }
+};
+
+// bf16 MFMA fragment (A or B operand of V_MFMA_F32_16X16X32_BF16) read from a
+// row-major LDS matrix M (pitch P elements) whose rows run along the
+// contraction: lane l receives M[8*(l/16) + j][l % 16], j < 8, for m pointing
+// at the block's (0, 0).  Two DS_READ_B64_TR_B16: within each group of 16
+// lanes that instruction gathers a 4 x 16 block, lane s supplying the 8-byte
+// piece at row s/4, columns 4*(s%4).., and lane t receiving column t of the
+// four rows (lane layout checked on the device).  m must be 8-byte aligned
+// and P a multiple of 4.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* m, int P) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int l = lane_id(), s = l & 15;
+  const bf16* a = m + (8 * (l >> 4) + (s >> 2)) * P + 4 * (s & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + 4 * P));
+  bf16x8 f;
+  __builtin_memcpy(&f, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&f) + 8, &hi, 8);
+  return f;
+}
+
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, uint2 u) {
+  decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)) v;
+  __builtin_memcpy(&v, &u, 8);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, uint32_t u) {
+  __builtin_amdgcn_raw_buffer_store_b32(u, r, off, 0, 0);
+}
+
+// Row e of this lane's accumulators over NT column tiles (each lane holds
+// rows 4*(l/16)+e, column l%16 of every tile) -> NT consecutive elements at
+// byte offset off: one 4-, 8- or 16-byte buffer store.
+template <typename T, int NT>
+__device__ __forceinline__ void store_acc_row(rsrc_t r, uint32_t off, const f32x4 (&acc)[NT], int e) {
+  constexpr int BYTES = NT * (int)sizeof(T);
+  static_assert(BYTES == 4 || BYTES == 8 || BYTES == 16, "row vector must be 4, 8 or 16 bytes");
+  uint32_t w[BYTES / 4];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) {
+      bf16 lo = from_f<bf16>(acc[2 * i][e]), hi = from_f<bf16>(acc[2 * i + 1][e]);
+      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const float f = acc[i][e];  // bit_cast of a vector element lvalue drops the index
+      w[i] = __builtin_bit_cast(uint32_t, f);
+    }
+  }
+  if constexpr (BYTES == 16) buf_store16(r, off, make_uint4(w[0], w[1], w[2], w[3]));
+  else if constexpr (BYTES == 8) buf_store8(r, off, make_uint2(w[0], w[1]));
+  else buf_store4(r, off, w[0]);
+}
+
 // LDS rows [0, nrows) of an R x D tile (pitch P) -> global (row stride gstride),
 // 16-byte accesses.
 template <typename T, int R, int D, int P, int NTH = NTHR>

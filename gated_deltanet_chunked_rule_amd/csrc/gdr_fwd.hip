@@ -90,55 +90,128 @@ __device__ __forceinline__ bool locate_chunk(const SeqTables& s, int c, int& n, 
 // --------------------------------------------------------------- k_intra --
 // Persistent: each workgroup walks a contiguous range of (chunk, value head)
 // items (value heads of one chunk adjacent, so the shared K tile is an L2
-// hit) and fetches the next item's K, V, g and beta into a second register
-// set while the current one is computed.  LDS regions are reused across the
-// phases (A: K rows -> (b Gamma K)^T -> W staging; B: inverse scratch ->
-// (b V)^T -> U staging; C: L -> A in the working dtype; D: A in fp32).
+// hit) and loads the next item's K, V, g and beta into a second register set
+// while the current one is computed.  Wave i owns row block i (tokens
+// 16i..16i+15) of A, W and U.  Per item:
+//   1. K, V -> LDS with permuted columns (RowSlab); gate scan.
+//   2. L = strict_lower(diag(b)(D * K K^T)) in fp32, ten lower 16x16 tiles
+//      spread 3/2/3/2 over the waves; the diagonal of K K^T certifies
+//      0 <= b |k|^2 <= 2 for the context-parallel warmup.
+//   3. Inverse of the unit lower triangular I + L, blocked by 16: wave i
+//      inverts its diagonal block by forward substitution, A_ii, and forms
+//      M_ij = A_ii L_ij (j < i).  Since A_ij = -A_ii sum_{j<=m<i} L_im A_mj,
+//        A_i,i-1 = -M_i,i-1 A_i-1,i-1
+//        A_20 = -M_20 A_00 + M_21 T_10,         T_10 = M_10 A_00
+//        A_31 = -M_31 A_11 + M_32 T_21,         T_21 = M_21 A_11
+//        A_30 = -M_30 A_00 + M_31 T_10 - M_32 A_20
+//      so each wave derives its whole row block from the shared M and A_ii
+//      tiles, keeping intermediates in registers: a register tile enters a
+//      product only as the right factor, whose accumulator layout already is
+//      an MFMA B operand once the contraction index is permuted to match.
+//   4. A' = A diag(b Gamma), A'' = A diag(b) in the working dtype, stored
+//      transposed over the fp32 tiles.
+//   5. W = A' K and U = A'' V: both operands are read with transposing LDS
+//      loads, and each lane stores NT consecutive columns of its rows.
+// Five workgroup barriers per item.
 struct IntraItem {
   int c, h, hk, n, t0, len;
   bool ok;
 };
 
+// acc + X Y for 16 x 16 fp32 tiles in LDS (pitch P); contraction index 4s + q
+// at step s for lane group q.
+template <int P>
+__device__ __forceinline__ f32x4 mm_ll(f32x4 acc, const float* X, const float* Y) {
+  const int l = lane_id(), q = l >> 4, t = l & 15;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[t * P + 4 * s + q], Y[(4 * s + q) * P + t], acc, 0, 0, 0);
+  return acc;
+}
+// acc + X R, R a 16 x 16 accumulator tile in registers (lane group q holds
+// its rows 4q..4q+3): at step s group q contracts over index 4q + s, for
+// which it holds R's row in element s.
+template <int P>
+__device__ __forceinline__ f32x4 mm_lr(f32x4 acc, const float* X, f32x4 R) {
+  const int l = lane_id(), q = l >> 4, t = l & 15;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[t * P + 4 * q + s], R[s], acc, 0, 0, 0);
+  return acc;
+}
+// LDS tile -> accumulator layout, and back.
+template <int P>
+__device__ __forceinline__ f32x4 ld_acc(const float* X) {
+  f32x4 a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] = X[acc_row(e) * P + acc_col()];
+  return a;
+}
+template <int P>
+__device__ __forceinline__ void st_acc(float* X, f32x4 a) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) X[acc_row(e) * P + acc_col()] = a[e];
+}
+
+// Lower tiles (i, j) of K K^T computed by wave w (n-th of kk_count(w)).
+__device__ __forceinline__ int kk_count(int w) { return (w & 1) ? 2 : 3; }
+__device__ __forceinline__ void kk_tile(int w, int n, int& i, int& j) {
+  // w0: (0,0) (3,0) (3,1)   w1: (1,0) (1,1)   w2: (2,0) (2,1) (2,2)   w3: (3,2) (3,3)
+  if (w == 0) { i = n == 0 ? 0 : 3; j = n == 0 ? 0 : n - 1; }
+  else if (w == 1) { i = 1; j = n; }
+  else if (w == 2) { i = 2; j = n; }
+  else { i = 3; j = 2 + n; }
+}
+
 template <typename T, int KD>
-__global__ __launch_bounds__(NTHR) void k_intra(IntraParams p, int total_items, int per_wg, int nwg) {
+__global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_items, int per_wg, int nwg) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
-  constexpr int PK = Pitch<T, KD>::value;     // row-major K / W / U rows
-  constexpr int PT = Pitch<T, CH>::value;     // transposed tiles (64 tokens wide)
-  constexpr int PL = 68;                      // fp32 64-wide rows
-  constexpr int PX = 20;
-  constexpr int SZ_A = (CH * PK > KD * PT ? CH * PK : KD * PT) * (int)sizeof(T);
-  constexpr int SZ_B = (CH * PK > KD * PT ? CH * PK : KD * PT) * (int)sizeof(T);
-  constexpr int SZ_C = CH * PL * 4;
-  constexpr int SZ_D = CH * PL * 4;
-  static_assert(NWAVE * 16 * PX * 4 <= SZ_B, "inverse scratch must fit region B");
-  static_assert(CH * PT * (int)sizeof(T) <= SZ_C, "A tile must fit region C");
-  __shared__ __align__(16) char smem[SZ_A + SZ_B + SZ_C + SZ_D];
+  constexpr int NT = KD / 16;                 // column tiles of W and U
+  constexpr int PK = Pitch<T, KD>::value;     // K / V rows (permuted columns)
+  constexpr int PF = 68;                      // fp32 64-wide rows
+  constexpr int PA = 68;                      // transposed A' / A''
+  constexpr int SZ_K = CH * PK * (int)sizeof(T);
+  constexpr int SZ_F = CH * PF * 4;
+  constexpr int SZ_AT = 2 * CH * PA * (int)sizeof(T);
+  constexpr int SZ_X = F32 ? SZ_AT : 0;       // fp32: A' / A'' cannot overlay the fp32 tiles
+  static_assert(F32 || SZ_AT <= SZ_F, "A' and A'' must fit over the fp32 tiles");
+  __shared__ __align__(16) char smem[2 * SZ_K + SZ_F + SZ_X];
   __shared__ float sG[CH], sB[CH];
   __shared__ int sFlag[NWAVE];
-  T* rA = reinterpret_cast<T*>(smem);
-  T* rB = reinterpret_cast<T*>(smem + SZ_A);
-  float* sL = reinterpret_cast<float*>(smem + SZ_A + SZ_B);
-  float* sA = reinterpret_cast<float*>(smem + SZ_A + SZ_B + SZ_C);
-  T* sAt = reinterpret_cast<T*>(smem + SZ_A + SZ_B);  // over L once the inverse is done
-  float* sX = reinterpret_cast<float*>(rB);
+  T* sK = reinterpret_cast<T*>(smem);
+  T* sV = reinterpret_cast<T*>(smem + SZ_K);
+  float* sF = reinterpret_cast<float*>(smem + 2 * SZ_K);
+  T* sAw = reinterpret_cast<T*>(smem + 2 * SZ_K + (F32 ? SZ_F : 0));  // A'^T  [token j][token i]
+  T* sAu = sAw + CH * PA;                                              // A''^T
 
   const SeqTables& s = p.s;
   const int x = xcd_remap(blockIdx.x, nwg);
   const int u0 = x * per_wg, u1 = min(total_items, u0 + per_wg);
   if (u0 >= u1) return;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int q = l >> 4, t = l & 15;
+  auto tile = [&](int i, int j) { return sF + 16 * i * PF + 16 * j; };
 
   auto locate = [&](int u, IntraItem& it) {
     it.ok = false;
     if (u >= u1) return;
     it.c = u / p.Hv;
-    it.h = u % p.Hv;
+    it.h = u - it.c * p.Hv;
     it.hk = it.h / (p.Hv / p.Hq);
-    it.ok = locate_chunk(s, it.c, it.n, it.t0, it.len);
+    if (s.T_uniform > 0) {
+      const int nc = (s.T_uniform + CH - 1) / CH;
+      it.n = it.c / nc;
+      const int cj = it.c - it.n * nc;
+      it.t0 = it.n * s.T_uniform + cj * CH;
+      it.len = min(CH, s.T_uniform - cj * CH);
+      it.ok = it.c < s.NTtot && it.len > 0;
+    } else {
+      it.ok = locate_chunk(s, it.c, it.n, it.t0, it.len);
+    }
   };
   // Loads of one item (an invalid item gets empty ranges: zeros, no traffic).
-  auto fetch = [&](const IntraItem& it, TileCols<T, KD>& rk, TileCols<T, VD>& rv, float& gv, float& bv) {
+  auto fetch = [&](const IntraItem& it, RowSlab<T, KD>& rk, RowSlab<T, VD>& rv, float& gv, float& bv) {
     const int len = it.ok ? it.len : 0;
     const int t0 = it.ok ? it.t0 : 0;
     rk.load((const T*)p.k + ((long)t0 * p.Hq + it.hk) * KD, (long)p.Hq * KD, len);
@@ -149,9 +222,10 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p, int total_items, 
     bv = buf_load_f32(br, (uint32_t)(l * p.Hv) * 4u);
   };
 
-  auto run = [&](const IntraItem& it, TileCols<T, KD>& rk, TileCols<T, VD>& rv, float gvc, float bvc,
-                 const IntraItem& nx, TileCols<T, KD>& rkn, TileCols<T, VD>& rvn, float& gvn, float& bvn) {
+  auto run = [&](const IntraItem& it, RowSlab<T, KD>& rk, RowSlab<T, VD>& rv, float gvc, float bvc,
+                 const IntraItem& nx, RowSlab<T, KD>& rkn, RowSlab<T, VD>& rvn, float& gvn, float& bvn) {
     const int t0 = it.t0, len = it.len, h = it.h;
+    lds_barrier();  // the previous item is done with every LDS region
     if (w == 0) {
       const float gc = wave_inclusive_scan((l < len) ? gvc : 0.f);
       sG[l] = gc;
@@ -161,134 +235,172 @@ __global__ __launch_bounds__(NTHR) void k_intra(IntraParams p, int total_items, 
         if (p.g_cum_out) p.g_cum_out[(long)(t0 + l) * p.Hv + h] = gc;
       }
     }
-    rk.template store<PK>(rA);
+    rk.template store_perm<PK>(sK);
+    rv.template store_perm<PK>(sV);
     lds_barrier();
     fetch(nx, rkn, rvn, gvn, bvn);
 
-  // L = strict_lower(diag(b) (D * K K^T)); the diagonal of K K^T certifies
-  // 0 <= b |k|^2 <= 2 (non-expansive steps) for the context-parallel warmup.
-  int bad = 0;
-  for (int jt = 0; jt < 4; ++jt) {
-    f32x4 a = zero4();
-    if (jt <= w) mma_tile<T, KD, PK, 1, 1, PK>(a, rA + 16 * w * PK, rA + 16 * jt * PK);
+    // 2. L tiles.
+    {
+      const int cnt = kk_count(w);
+      f32x4 acc[3];
+      int ti[3], tj[3];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * w + acc_row(e), cc = 16 * jt + acc_col();
-      float lv = 0.f;
-      if (r > cc) lv = sB[r] * __expf(sG[r] - sG[cc]) * a[e];
-      if (r == cc && r < len) {
-        const float bn = sB[r] * a[e];
-        if (!(bn >= 0.f && bn <= 2.f)) bad = 1;
+      for (int n = 0; n < 3; ++n) {
+        acc[n] = zero4();
+        kk_tile(w, n, ti[n], tj[n]);
+        if (n < cnt) mma_tile<T, KD, PK, 1, 1, PK>(acc[n], sK + 16 * ti[n] * PK, sK + 16 * tj[n] * PK);
       }
-      sL[r * PL + cc] = lv;
+      int bad = 0;
+#pragma unroll
+      for (int n = 0; n < 3; ++n) {
+        if (n < cnt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ti[n] + acc_row(e), c = 16 * tj[n] + acc_col();
+            float lv = 0.f;
+            if (r > c) lv = sB[r] * __expf(sG[r] - sG[c]) * acc[n][e];
+            if (r == c && r < len) {
+              const float bn = sB[r] * acc[n][e];
+              if (!(bn >= 0.f && bn <= 2.f)) bad = 1;
+            }
+            sF[r * PF + c] = lv;
+          }
+        }
+      }
+      const bool wave_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+      if (l == 0) sFlag[w] = wave_bad ? 1 : 0;
     }
-  }
-  const int any_bad = lds_any<NWAVE>(bad, sFlag);
-  if (tid == 0) p.cert[(long)h * s.NTtot + it.c] = any_bad ? INFINITY : sG[len - 1];
+    lds_barrier();
+    if (tid == 0) {
+      const int any_bad = sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3];
+      p.cert[(long)h * s.NTtot + it.c] = any_bad ? INFINITY : sG[len - 1];
+    }
 
-  if (p.A_in) {
-    for (int i = tid; i < CH * CH; i += NTHR) {
-      const int r = i / CH, cc = i % CH;
-      float a = (r == cc) ? 1.f : 0.f;
-      if (r < len) a = (cc < len) ? p.A_in[((long)(t0 + r) * p.Hv + h) * CH + cc] : 0.f;
-      sA[r * PL + cc] = a;
-    }
-    lds_barrier();
-  } else {
-    // Blocked inverse of the unit lower triangular I + L in fp32: diagonal
-    // 16x16 blocks by forward substitution (one wave each) ...
-    if (l < 16) {
-      float x[16];
+    // 3. Row block w of A into registers a0..a3 (tile j), zero above the diagonal.
+    f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4(), a3 = zero4();
+    if (p.A_in) {
+      const float* src = p.A_in + ((long)t0 * p.Hv + h) * CH;
+      const long rs = (long)p.Hv * CH;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == l) ? 1.f : 0.f;
-        const float* Lr = sL + (16 * w + r) * PL + 16 * w;
-#pragma unroll
-        for (int jj = 0; jj < r; ++jj) acc -= Lr[jj] * x[jj];
-        x[r] = acc;
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + acc_row(e);
+        if (r < len) {
+          const float* row = src + (long)r * rs;
+          if (0 <= w && t < len) a0[e] = row[t];
+          if (1 <= w && 16 + t < len) a1[e] = row[16 + t];
+          if (2 <= w && 32 + t < len) a2[e] = row[32 + t];
+          if (3 <= w && 48 + t < len) a3[e] = row[48 + t];
+        }
       }
+    } else {
+      // Diagonal block by forward substitution (lane l < 16 solves column l),
+      // written over L_ww.
+      if (l < 16) {
+        float xs[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sA[(16 * w + r) * PL + 16 * w + l] = x[r];
-    }
-    for (int i = tid; i < CH * CH; i += NTHR) {
-      const int r = i / CH, cc = i % CH;
-      if ((cc >> 4) > (r >> 4)) sA[r * PL + cc] = 0.f;
-    }
-    lds_barrier();
-    // ... then the off-diagonal blocks by distance from the diagonal:
-    // A_ij = -A_ii * sum_{j <= m < i} L_im A_mj.
-    for (int d = 1; d < 4; ++d) {
-      if (w + d < 4) {
-        const int i = w + d, j = w;
-        float* X = sX + w * 16 * PX;
-        f32x4 xacc = zero4();
-        for (int m = j; m < i; ++m)
-          mma_tile<float, 16, PL, 1, PL, 1>(xacc, sL + 16 * i * PL + 16 * m, sA + 16 * m * PL + 16 * j);
+        for (int r = 0; r < 16; ++r) {
+          float acc = (r == l) ? 1.f : 0.f;
+          const float* Lr = sF + (16 * w + r) * PF + 16 * w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[acc_row(e) * PX + acc_col()] = xacc[e];
-        wave_sync();
-        f32x4 yacc = zero4();
-        mma_tile<float, 16, PL, 1, PX, 1>(yacc, sA + 16 * i * PL + 16 * i, X);
+          for (int jj = 0; jj < r; ++jj) acc -= Lr[jj] * xs[jj];
+          xs[r] = acc;
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sA[(16 * i + acc_row(e)) * PL + 16 * j + acc_col()] = -yacc[e];
+        for (int r = 0; r < 16; ++r) sF[(16 * w + r) * PF + 16 * w + l] = xs[r];
       }
+      wave_sync();
+      // M_wj = A_ww L_wj over L_wj.
+      for (int j = 0; j < w; ++j) st_acc<PF>(tile(w, j), mm_ll<PF>(zero4(), tile(w, w), tile(w, j)));
       lds_barrier();
+      const f32x4 dg = ld_acc<PF>(tile(w, w));
+      if (w == 0) {
+        a0 = dg;
+      } else if (w == 1) {
+        a0 = -mm_ll<PF>(zero4(), tile(1, 0), tile(0, 0));
+        a1 = dg;
+      } else if (w == 2) {
+        const f32x4 t10 = mm_ll<PF>(zero4(), tile(1, 0), tile(0, 0));
+        a0 = mm_lr<PF>(-mm_ll<PF>(zero4(), tile(2, 0), tile(0, 0)), tile(2, 1), t10);
+        a1 = -mm_ll<PF>(zero4(), tile(2, 1), tile(1, 1));
+        a2 = dg;
+      } else {
+        const f32x4 t10 = mm_ll<PF>(zero4(), tile(1, 0), tile(0, 0));
+        const f32x4 t21 = mm_ll<PF>(zero4(), tile(2, 1), tile(1, 1));
+        const f32x4 a20 = mm_lr<PF>(-mm_ll<PF>(zero4(), tile(2, 0), tile(0, 0)), tile(2, 1), t10);
+        a0 = mm_lr<PF>(mm_lr<PF>(-mm_ll<PF>(zero4(), tile(3, 0), tile(0, 0)), tile(3, 1), t10), tile(3, 2), -a20);
+        a1 = mm_lr<PF>(-mm_ll<PF>(zero4(), tile(3, 1), tile(1, 1)), tile(3, 2), t21);
+        a2 = -mm_ll<PF>(zero4(), tile(3, 2), tile(2, 2));
+        a3 = dg;
+      }
     }
-  }
-
-  // Export A; stage (b Gamma K)^T, (b V)^T and A in the working dtype.
-  if (p.A_ws || p.A_out) {
-    for (int i = tid; i < len * (CH / 4); i += NTHR) {
-      const int r = i / (CH / 4), cc = (i % (CH / 4)) * 4;
-      const float4 a = *reinterpret_cast<const float4*>(sA + r * PL + cc);
-      if (p.A_ws) *reinterpret_cast<float4*>(p.A_ws + ((long)h * s.Ttot + t0 + r) * CH + cc) = a;
-      if (p.A_out) *reinterpret_cast<float4*>(p.A_out + ((long)(t0 + r) * p.Hv + h) * CH + cc) = a;
-    }
-  }
-  rk.template store_t<PT>(rA, sB[l] * __expf(sG[l]));
-  rv.template store_t<PT>(rB, sB[l]);
-  if constexpr (F32) {
-    for (int i = tid; i < CH * CH; i += NTHR) sAt[(i / CH) * PT + i % CH] = sA[(i / CH) * PL + i % CH];
-  } else {
-    for (int i = tid; i < CH * CH / 4; i += NTHR) {
-      const int r = i / (CH / 4), cc = (i % (CH / 4)) * 4;
-      const float4 a = *reinterpret_cast<const float4*>(sA + r * PL + cc);
-      bf16x4 pk;
-      pk[0] = from_f<T>(a.x); pk[1] = from_f<T>(a.y); pk[2] = from_f<T>(a.z); pk[3] = from_f<T>(a.w);
-      *reinterpret_cast<bf16x4*>(sAt + r * PT + cc) = pk;
-    }
-  }
-  lds_barrier();
-
-  // W^T = (b Gamma K)^T A^T and U^T = (b V)^T A^T; A is lower triangular, so
-  // output column block j only contracts over tokens < 16 (j + 1).
-  constexpr int TILES = (KD / 16) * 4;
-  constexpr int TPW = TILES / NWAVE;
-  f32x4 wacc[TPW], uacc[TPW];
+    if (p.A_ws || p.A_out) {
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int ti = w * TPW + i, rb = ti / 4, cb = ti % 4;
-    wacc[i] = zero4();
-    uacc[i] = zero4();
-    mma_tile<T, CH, PT, 1, 1, PT>(wacc[i], rA + 16 * rb * PT, sAt + 16 * cb * PT, 16 * (cb + 1));
-    mma_tile<T, CH, PT, 1, 1, PT>(uacc[i], rB + 16 * rb * PT, sAt + 16 * cb * PT, 16 * (cb + 1));
-  }
-  lds_barrier();
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * w + acc_row(e);
+        if (r < len) {
+          const float v4[4] = {a0[e], a1[e], a2[e], a3[e]};
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int ti = w * TPW + i, rb = ti / 4, cb = ti % 4;
-    acc_store_t<T, PK>(rA, 16 * rb, 16 * cb, wacc[i]);
-    acc_store_t<T, PK>(rB, 16 * rb, 16 * cb, uacc[i]);
-  }
-  lds_barrier();
-  store_rows<T, CH, KD, PK>((T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, rA, len);
-  store_rows<T, CH, VD, PK>((T*)p.U + ((long)h * s.Ttot + t0) * VD, VD, rB, len);
-    lds_barrier();   // staging regions are rewritten by the next item
+          for (int j = 0; j < 4; ++j) {
+            if (p.A_ws) p.A_ws[((long)h * s.Ttot + t0 + r) * CH + 16 * j + t] = v4[j];
+            if (p.A_out) p.A_out[((long)(t0 + r) * p.Hv + h) * CH + 16 * j + t] = v4[j];
+          }
+        }
+      }
+    }
+
+    // 4. A' and A'' (column scales b Gamma and b), transposed, over the fp32 tiles.
+    float sw[4], su[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      su[j] = sB[16 * j + t];
+      sw[j] = su[j] * __expf(sG[16 * j + t]);
+    }
+    lds_barrier();
+    const int nks = F32 ? 4 * (w + 1) : (w + 2) / 2;  // contraction steps (A' is zero beyond 16(w+1))
+    const int ntile = F32 ? w + 1 : 2 * nks;          // A' tiles the steps read
+    {
+      const f32x4 av[4] = {a0, a1, a2, a3};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < ntile) {
+          acc_store_t<T, PA>(sAw, 16 * w, 16 * j, av[j], sw[j]);
+          acc_store_t<T, PA>(sAu, 16 * w, 16 * j, av[j], su[j]);
+        }
+      }
+    }
+    wave_sync();
+
+    // 5. W = A' K, U = A'' V for row block w.
+    auto gemm_store = [&](const T* sAT, const T* sX, void* dst, int D) {
+      f32x4 acc[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = zero4();
+      for (int ks = 0; ks < nks; ++ks) {
+        if constexpr (F32) {
+          const float a = sAT[(4 * ks + q) * PA + 16 * w + t];
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sX[(4 * ks + q) * PK + 16 * j + t], acc[j], 0, 0, 0);
+        } else {
+          const bf16x8 a = tr_frag(sAT + 32 * ks * PA + 16 * w, PA);
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, tr_frag(sX + 32 * ks * PK + 16 * j, PK), acc[j], 0, 0, 0);
+        }
+      }
+      const rsrc_t rr = make_rsrc((const T*)dst + ((long)h * s.Ttot + t0) * D, (long)len * D * (long)sizeof(T));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        store_acc_row<T, NT>(rr, (uint32_t)(((16 * w + acc_row(e)) * D + NT * t) * (int)sizeof(T)), acc, e);
+    };
+    gemm_store(sAw, sK, p.W, KD);
+    gemm_store(sAu, sV, p.U, VD);
   };
 
   IntraItem cur, nxt;
-  TileCols<T, KD> rk0, rk1;
-  TileCols<T, VD> rv0, rv1;
+  RowSlab<T, KD> rk0, rk1;
+  RowSlab<T, VD> rv0, rv1;
   float g0 = 0.f, b0 = 0.f, g1 = 0.f, b1 = 0.f;
   locate(u0, cur);
   fetch(cur, rk0, rv0, g0, b0);
@@ -717,9 +829,9 @@ static unsigned padded_grid(long total) { return (unsigned)(((total + 7) / 8) * 
 template <typename T, int KD>
 static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
   hipError_t err;
-  // persistent grid: two workgroups per CU, each over a contiguous item range
+  // persistent grid: three workgroups per CU, each over a contiguous item range
   const long total = (long)p.s.NTtot * p.Hv;
-  const int nwg = (int)std::min<long>(padded_grid(total), 2 * 256);
+  const int nwg = (int)std::min<long>(padded_grid(total), 3 * 256);
   const int per_wg = (int)((total + nwg - 1) / nwg);
   GDR_LAUNCH("intra_wy", (k_intra<T, KD>), dim3(nwg), st, p, (int)total, per_wg, nwg);
   return err;

@@ -28,6 +28,7 @@ struct SeqTables {
   int N;
   long Ttot;                 // tokens in the packed batch
   int NTtot;                 // chunks (host count; device tables must agree)
+  int T_uniform;             // > 0: N rows of T_uniform tokens (no cu_seqlens)
 };
 
 struct PlanParams {
