@@ -327,6 +327,42 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16* m, int P) {
   return f;
 }
 
+// Four rows r0..r0+3 (r0 may differ between the 16-lane groups) of a
+// row-major bf16 LDS matrix at column c0 + l%16: lane l receives
+// m[(r0 + i) * P + c0 + l % 16] as element i (one DS_READ_B64_TR_B16).
+__device__ __forceinline__ i16x4 tr4(const bf16* m, int P, int r0, int c0) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int s = lane_id() & 15;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(m + (r0 + (s >> 2)) * P + c0 + 4 * (s & 3)));
+}
+__device__ __forceinline__ bf16x8 cat4(i16x4 lo, i16x4 hi) {
+  bf16x8 f;
+  __builtin_memcpy(&f, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&f) + 8, &hi, 8);
+  return f;
+}
+// Two 4-element pieces of an LDS row: row[k0 .. k0+3] ++ row[k0+16 .. k0+19].
+__device__ __forceinline__ bf16x8 ld_a2(const bf16* row, int k0) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(row + k0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(row + k0 + 16);
+  bf16x8 f;
+  __builtin_memcpy(&f, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&f) + 8, &hi, 8);
+  return f;
+}
+// Accumulator tiles X, Y (rows 16b, 16b+16 of a matrix) as the B operand of
+// a bf16 MFMA step: lane group q contracts over rows 16b + 4q + j of X
+// (j < 4) then the same rows of Y.
+__device__ __forceinline__ bf16x8 pack_b(const f32x4& x, const f32x4& y) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = static_cast<bf16>(x[e]);
+    f[4 + e] = static_cast<bf16>(y[e]);
+  }
+  return f;
+}
+
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, uint2 u) {
   decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)) v;
   __builtin_memcpy(&v, &u, 8);

@@ -590,32 +590,71 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
 // The serial chunk recurrence fused with the output (the pages' second fused
 // forward kernel: FlashQLA curated summary, section
 // "平衡解決方案：雙核心融合與自動CP"): one 8-wave workgroup per (sequence,
-// value head, CP segment) covering all V columns, so W, K, Q and P are staged
-// once per chunk and the chunk states never leave the chip.  Per chunk:
-//   P^T = lower(D * K Q^T) * s      (from K and Q rows; skipped in warmup)
-//   Vnew = U - W h,  O = s Gamma (Q h) + P Vnew   (W h and Q h share B tiles)
-//   h' = Gamma_n h + (diag(e^{gamma_n - gamma}) K)^T Vnew
-// Waves: output tiles (rows 16*(w%4), column half w/4); state tiles 8 per wave.
+// value head, CP segment).  Wave w owns 16 state columns over all K rows, in
+// fp32 accumulators, so the recurrence needs no data from other waves:
+//   Vnew = U - W h            (h, as accumulators, is the MFMA B operand)
+//   h'   = Gamma_n h + K^T (d * Vnew),  d_t = e^{gamma_n - gamma_t}
+//                             (Vnew, as accumulators, is the B operand; K
+//                             is read with transposing LDS loads)
+//   O    = s Gamma (Q h) + P Vnew,  P = s lower(D * Q K^T)
+// The chunk inputs W, Q, K, U and the gate cumsums are copied from global
+// memory straight into LDS (buffer loads with the LDS destination bit),
+// double-buffered: the next chunk's copy is issued when a chunk starts and
+// waited for at its end, so it overlaps the whole chunk and costs no
+// registers.  Staged tiles are unpadded with the 16-byte pieces of each row
+// XOR-swizzled (row-dependent), which keeps the 8-byte fragment reads and
+// the transposing reads free of bank conflicts.  P tiles are shared (one or
+// two per wave); the bf16 output is staged in LDS and written as full rows.
+// Two workgroup barriers per chunk.  Two waves per SIMD hide each other's
+// LDS and MFMA latencies.
+// Row numbering: state tile rb, lane group g, element e holds K row
+// 32(rb/2) + 8g + 4(rb%2) + e, so the two tiles of a 32-row contraction step
+// give a lane K rows 32ks + 8g .. +7, and the W and Q fragments that match
+// them are single 16-byte LDS reads.  P is stored with its token columns
+// permuted the same way (32-token block, group g, half hh: column
+// 32ks + 16hh + 4g + e at position 32ks + 8g + 4hh + e) for P Vnew.
+template <int NCH>
+__device__ __forceinline__ int stage_swz(int r) {
+  if constexpr (NCH == 16) return 2 * (r & 7) + ((r >> 3) & 1);
+  else if constexpr (NCH == 8) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  else return (r >> 2) & (NCH - 1);
+}
+
 template <typename T, int KD>
-__global__ __launch_bounds__(512) void k_fused(FusedParams p, int total_items) {
-  constexpr int NT = 512, NW = 8;
+struct FusedLds {
+  static constexpr bool F32 = std::is_same<T, float>::value;
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int NCH = KD / VEC;                     // 16-byte pieces per row
+  static constexpr int TILE = CH * KD * (int)sizeof(T);    // bytes per staged tile
+  static constexpr int PP = Pitch<T, CH>::value;
+  static constexpr int SZ_P = CH * PP * (int)sizeof(T);
+  static constexpr int SZ_O = F32 ? 0 : TILE;
+  static constexpr int OFF_P = 8 * TILE, OFF_O = OFF_P + SZ_P, OFF_G = OFF_O + SZ_O;
+  static constexpr int OFF_D = OFF_G + 2 * CH * 4;         // per-row factors, 2 buffers x {d, s Gamma}
+  static constexpr int BYTES = OFF_D + 4 * CH * 4;
+};
+
+constexpr int FNW = 8, FNT = 64 * FNW;   // waves / threads of k_fused
+
+template <typename T, int KD>
+__global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
+  using LY = FusedLds<T, KD>;
+  constexpr bool F32 = LY::F32;
   constexpr int VD = KD;
-  constexpr int PK = Pitch<T, KD>::value;
-  constexpr int PT = Pitch<T, CH>::value;
-  constexpr int NKB = KD / 16, NVB = VD / 16;
-  constexpr int NST = NKB * NVB;
-  constexpr int HT = (NST + NW - 1) / NW;
-  constexpr int OCB = NVB / 2;
-  static_assert(NVB % 2 == 0, "V must split into two column halves");
-  __shared__ __align__(16) T sW[CH * PK];     // W rows; O staging after W h
-  __shared__ __align__(16) T sQ[CH * PK];
-  __shared__ __align__(16) T sK[CH * PK];
-  __shared__ __align__(16) T sU[CH * PK];
-  __shared__ __align__(16) T sKdT[KD * PT];   // e^{gamma_n - gamma_t} k_t[d] as [d][t]
-  __shared__ __align__(16) T shT[VD * PK];    // h[d][v] as [v][d]
-  __shared__ __align__(16) T sVt[VD * PT];    // Vnew[t][v] as [v][t]
-  __shared__ __align__(16) T sP[CH * PT];     // s P[t][s] rows
-  __shared__ float sG[CH];
+  constexpr int VEC = LY::VEC, NCH = LY::NCH, PP = LY::PP;
+  constexpr int NKB = KD / 16, NCB = VD / 16;
+  constexpr int NWV = NCB < FNW ? NCB : FNW;       // waves owning state columns
+  constexpr int CBW = NCB / NWV;                   // column tiles per owning wave
+  static_assert(CBW == 1, "one column tile per wave");
+  extern __shared__ __align__(16) char dsm[];
+  // staged tile b, m (m: 0 W, 1 Q, 2 K, 3 U)
+  auto tile = [&](int b, int m) { return reinterpret_cast<T*>(dsm + (2 * m + b) * LY::TILE); };
+  T* sP = reinterpret_cast<T*>(dsm + LY::OFF_P);
+  T* sO = reinterpret_cast<T*>(dsm + LY::OFF_O);
+  float* sGb = reinterpret_cast<float*>(dsm + LY::OFF_G);
+  float* sDb = reinterpret_cast<float*>(dsm + LY::OFF_D);   // [b][0]: e^{gamma_n - gamma_t} (0 past the chunk), [b][1]: s e^{gamma_t}
+  // element offset of (row, col) in a staged tile
+  auto tix = [](int r, int c) { return (r * NCH + ((c / VEC) ^ stage_swz<NCH>(r))) * VEC + (c % VEC); };
 
   const SeqTables& s = p.s;
   const int u = xcd_remap(blockIdx.x, total_items);
@@ -630,15 +669,16 @@ __global__ __launch_bounds__(512) void k_fused(FusedParams p, int total_items) {
   if (pseg < 0 || pseg >= nseg || c0 < 0 || c0 + nch > s.NTtot) return;
   const int L = p.seg_chunks;
   const int hk = h / (p.Hv / p.Hq);
-  const int w = wave_id(), l = lane_id();
-  const int orb = w & 3, ocol = (w >> 2) * OCB;   // output row block, first column tile
+  const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
+  const bool owner = w < NWV;
+  auto vcol = [&](int cb) { return CBW == 2 ? 32 * w + 2 * t + cb : 16 * w + t; };
 
   int ok = 1;
-  for (int q = 1 + (int)threadIdx.x; q < nseg; q += NT) {
-    const int ws = q * L - p.warmup;
+  for (int qq = 1 + (int)threadIdx.x; qq < nseg; qq += FNT) {
+    const int ws = qq * L - p.warmup;
     if (ws > 0) {
       float sum = 0.f;
-      for (int cc = ws; cc < q * L; ++cc) sum += p.cert[(long)h * s.NTtot + c0 + cc];
+      for (int cc = ws; cc < qq * L; ++cc) sum += p.cert[(long)h * s.NTtot + c0 + cc];
       if (!(sum <= p.log_eps)) ok = 0;
     }
   }
@@ -655,155 +695,338 @@ __global__ __launch_bounds__(512) void k_fused(FusedParams p, int total_items) {
     write_final = (pseg == nseg - 1);
   }
 
-  f32x4 hacc[HT];
+  const long hbase = ((long)n * p.Hv + h) * KD * VD;
+  auto krow = [&](int rb, int e) { return 32 * (rb >> 1) + 8 * q + 4 * (rb & 1) + e; };
+  f32x4 hs[NKB][CBW];
 #pragma unroll
-  for (int i = 0; i < HT; ++i) {
-    const int ti = w * HT + i, rb = ti / NVB, cb = ti % NVB;
-    hacc[i] = zero4();
-    if (ti < NST && cstart == 0 && p.h0) {
+  for (int rb = 0; rb < NKB; ++rb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        hacc[i][e] = p.h0[(((long)n * p.Hv + h) * KD + 16 * rb + acc_row(e)) * VD + 16 * cb + acc_col()];
+    for (int cb = 0; cb < CBW; ++cb) {
+      hs[rb][cb] = zero4();
+      if (owner && cstart == 0 && p.h0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hs[rb][cb][e] = p.h0[hbase + (long)(F32 ? 16 * rb + acc_row(e) : krow(rb, e)) * VD + vcol(cb)];
+      }
     }
-  }
 
-  TileRegs<T, CH, KD, NT> rw, ru;
-  TileCols<T, KD, NW> rq, rk;
-  float gam_next = 0.f, glast_next = 0.f;
-  // Loads of chunk jc into registers.  Issued unconditionally (a chunk past
-  // the segment gets an empty range: zeros, no memory traffic) so that no
-  // control-flow join forces the compiler to wait for them early.
-  auto prefetch = [&](int jc) {
-    const bool valid = jc < cend;
-    const int t0 = s.cu[n] + min(jc, cend - 1) * CH;
-    const int len = valid ? min(CH, s.cu[n + 1] - t0) : 0;
-    const int lenq = (jc >= cbeg) ? len : 0;
-    rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
-    ru.load((const T*)p.U + ((long)h * s.Ttot + t0) * VD, VD, len);
-    rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
-    rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, lenq);
-    const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
-    glast_next = buf_load_f32(gr, (uint32_t)(len - 1) * 4u);
-    const float gv = buf_load_f32(gr, (uint32_t)l * 4u);
-    gam_next = (l < len) ? gv : glast_next;
+  // Copies chunk jc's tiles into buffer b (rows past the chunk read as zero).
+  auto copy_chunk = [&](int jc, int b) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int t0 = s.cu[n] + jc * CH;
+    const int len = min(CH, s.cu[n + 1] - t0);
+    const bool with_q = jc >= cbeg;
+    auto one = [&](T* dst, const T* g, long gstride) {
+      const rsrc_t rr = make_rsrc(g, (long)len * gstride * (long)sizeof(T));
+#pragma unroll
+      for (int i = w; i < NCH; i += FNW) {   // 1 KB of LDS per instruction
+        const int pidx = 64 * i + l;
+        const int r = pidx / NCH, c = (pidx % NCH) ^ stage_swz<NCH>(r);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(dst + 64 * i * VEC), 16,
+                                                 (uint32_t)(r * gstride * (long)sizeof(T)) + (uint32_t)c * 16u, 0, 0, 0);
+      }
+    };
+    one(tile(b, 0), (const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD);
+    one(tile(b, 3), (const T*)p.U + ((long)h * s.Ttot + t0) * VD, VD);
+    one(tile(b, 2), (const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD);
+    if (with_q) one(tile(b, 1), (const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD);
+    if (w == 0) {
+      const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (lds_void*)(sGb + b * CH), 4, (uint32_t)l * 4u, 0, 0, 0);
+    }
   };
-  if (cstart < cend) prefetch(cstart);
+  // Waits for this wave's copies; wave 0 (which copied the gate cumsums of
+  // chunk jn into buffer bn) then derives that chunk's per-row factors; the
+  // barrier publishes everything.
+  auto wait_copies = [&](int jn, int bn) {
+    __builtin_amdgcn_s_waitcnt(0);   // vmcnt = 0 (the LDS copies), expcnt = 0, lgkmcnt = 0
+    if (w == 0 && jn < cend) {
+      const int tn = s.cu[n] + jn * CH;
+      const int ln = min(CH, s.cu[n + 1] - tn);
+      const float* g = sGb + bn * CH;
+      const float gl = g[max(ln, 1) - 1], gv = g[l];
+      sDb[(2 * bn) * CH + l] = (l < ln) ? __expf(gl - gv) : 0.f;
+      sDb[(2 * bn + 1) * CH + l] = p.scale * __expf(gv);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt = 0
+    }
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  // bf16 output rows of a chunk from sO to global memory.
+  auto store_o = [&](int ot0, int olen) {
+    if constexpr (!F32) {
+      const rsrc_t rr = make_rsrc((T*)p.o + ((long)ot0 * p.Hv + h) * VD, (long)olen * p.Hv * VD * (long)sizeof(T));
+      const uint32_t rs = (uint32_t)(p.Hv * VD * (int)sizeof(T));
+#pragma unroll
+      for (int i = threadIdx.x; i < CH * NCH; i += FNT) {
+        const int r = i / NCH, c = i % NCH;
+        buf_store16(rr, (uint32_t)r * rs + (uint32_t)c * 16u,
+                    *reinterpret_cast<const uint4*>(sO + (r * NCH + (c ^ stage_swz<NCH>(r))) * VEC));
+      }
+    }
+  };
 
+  if (cstart < cend) copy_chunk(cstart, 0);
+  wait_copies(cstart, 0);
+
+  int b = 0;
+  int prev_t0 = 0, prev_len = 0;
+  bool prev_out = false;
   for (int jc = cstart; jc < cend; ++jc) {
     const int t0 = s.cu[n] + jc * CH;
     const int len = min(CH, s.cu[n + 1] - t0);
     if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) break;
     const bool warm = jc < cbeg;
-    const float glast = glast_next, gam = gam_next;
-    rw.template store<PK>(sW);
-    ru.template store<PK>(sU);
-    rk.template store_t<PT>(sKdT, (l < len) ? __expf(glast - gam) : 0.f);
-    if (!warm) {
-      rk.template store<PK>(sK);
-      rq.template store<PK>(sQ);
-    }
-    if (w == 0) sG[l] = gam;
-#pragma unroll
-    for (int i = 0; i < HT; ++i) {
-      const int ti = w * HT + i;
-      if (ti < NST) acc_store_t<T, PK>(shT, 16 * (ti / NVB), 16 * (ti % NVB), hacc[i]);
-    }
-    lds_barrier();
-    prefetch(jc + 1);
+    if (jc + 1 < cend) copy_chunk(jc + 1, b ^ 1);
+    const T* sW = tile(b, 0);
+    const T* sQ = tile(b, 1);
+    const T* sK = tile(b, 2);
+    const T* sU = tile(b, 3);
+    const float* sG = sGb + b * CH;
+    const float* sD = sDb + (2 * b) * CH;
+    const float* sM = sDb + (2 * b + 1) * CH;
+    const float glast = sG[len - 1];
 
-    if (!warm) {  // s P as rows [t][s], from P^T tiles (s-block w%4, t-blocks of this half)
-      const int is = w & 3, jt0 = 2 * (w >> 2);
-      f32x4 a2[2] = {zero4(), zero4()};
-      mma_row<T, KD, 2, PK, 1, 1, PK>(a2, sK + 16 * is * PK, sQ + 16 * jt0 * PK);
+    if (prev_out) store_o(prev_t0, prev_len);
+
+    if (!warm) {  // P tiles: rows of tile ti, columns of tile tj
+      // The ten lower tiles and the upper tiles (0,1), (2,3) that the
+      // 32-token contraction steps read (masked to zero): waves 0-3 take two,
+      // waves 4-7 one.
+      constexpr int TI[12] = {3, 3, 2, 2, 3, 3, 2, 1, 1, 0, 0, 2};
+      constexpr int TJ[12] = {0, 1, 0, 1, 2, 3, 2, 0, 1, 0, 1, 3};
+      const int cnt = w < 4 ? 2 : 1;
+      int ti[2], tj[2];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int jt = jt0 + jj;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int sidx = 16 * is + acc_row(e), t = 16 * jt + acc_col();
-          a2[jj][e] = (t >= sidx) ? p.scale * __expf(sG[t] - sG[sidx]) * a2[jj][e] : 0.f;
-        }
-        acc_store_t<T, PT>(sP, 16 * is, 16 * jt, a2[jj]);
+      for (int m = 0; m < 2; ++m) {
+        const int idx = w < 4 ? 2 * w + m : 8 + (w - 4);
+        ti[m] = TI[idx];
+        tj[m] = TJ[idx];
       }
-    }
-    f32x4 oacc[OCB];
-    {  // Vnew = U - W h and (if not warm) Q h, sharing the h^T operand tiles
-      f32x4 vacc[OCB];
+      f32x4 pa[2] = {zero4(), zero4()};
+      if constexpr (F32) {
 #pragma unroll
-      for (int j = 0; j < OCB; ++j) { vacc[j] = zero4(); oacc[j] = zero4(); }
-      constexpr int KS = Mma<T>::KSTEP;
-      if (!warm) {
+        for (int k0 = 0; k0 < KD; k0 += 4)
 #pragma unroll
-        for (int k0 = 0; k0 < KD; k0 += KS) {
-          const auto fw = Mma<T>::template load<PK, 1>(sW + 16 * orb * PK + k0);
-          const auto fq = Mma<T>::template load<PK, 1>(sQ + 16 * orb * PK + k0);
+          for (int m = 0; m < 2; ++m)
+            pa[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[tix(16 * ti[m] + t, k0 + q)], sK[tix(16 * tj[m] + t, k0 + q)],
+                                                         pa[m], 0, 0, 0);
+      } else {
 #pragma unroll
-          for (int j = 0; j < OCB; ++j) {
-            const auto fb = Mma<T>::template load<PK, 1>(shT + 16 * (ocol + j) * PK + k0);
-            vacc[j] = Mma<T>::op(fw, fb, vacc[j]);
-            oacc[j] = Mma<T>::op(fq, fb, oacc[j]);
+        for (int k0 = 0; k0 < KD; k0 += 32) {
+          bf16x8 fa[2], fb[2];
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            fa[m] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * ti[m] + t, k0 + 8 * q));
+            fb[m] = *reinterpret_cast<const bf16x8*>(sK + tix(16 * tj[m] + t, k0 + 8 * q));
+          }
+#pragma unroll
+          for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[m], pa[m], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m < cnt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ti[m] + acc_row(e), c = 16 * tj[m] + acc_col();
+            const float v = (r >= c && r < len) ? p.scale * __expf(sG[r] - sG[c]) * pa[m][e] : 0.f;
+            const int pc = F32 ? c : (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
+            sP[r * PP + pc] = from_f<T>(v);
           }
         }
-      } else {
-        mma_row<T, KD, OCB, PK, 1, 1, PK>(vacc, sW + 16 * orb * PK, shT + 16 * ocol * PK);
-      }
-#pragma unroll
-      for (int j = 0; j < OCB; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vacc[j][e] = to_f(sU[(16 * orb + acc_row(e)) * PK + 16 * (ocol + j) + acc_col()]) - vacc[j][e];
-        acc_store_t<T, PT>(sVt, 16 * orb, 16 * (ocol + j), vacc[j]);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float gm = p.scale * __expf(sG[16 * orb + acc_row(e)]);
-#pragma unroll
-        for (int j = 0; j < OCB; ++j) oacc[j][e] *= gm;
       }
     }
-    lds_barrier();
 
-    if (!warm) {  // O += s P Vnew, staged as rows in sW
-      mma_row<T, CH, OCB, PT, 1, 1, PT>(oacc, sP + 16 * orb * PT, sVt + 16 * ocol * PT, 16 * (orb + 1));
+    f32x4 vn[4][CBW], oa[4][CBW];
 #pragma unroll
-      for (int j = 0; j < OCB; ++j)
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sW[(16 * orb + acc_row(e)) * PK + 16 * (ocol + j) + acc_col()] = from_f<T>(oacc[j][e]);
-    }
-    const float dlast = __expf(glast);
-    if constexpr (HT * NW == NST && NVB % HT == 0) {
-      const int ti0 = w * HT;
+      for (int cb = 0; cb < CBW; ++cb) { vn[tt][cb] = zero4(); oa[tt][cb] = zero4(); }
+    if (owner) {
+      // Vnew = U - W h and Q h.
+      if constexpr (F32) {
 #pragma unroll
-      for (int i = 0; i < HT; ++i) hacc[i] *= dlast;
-      mma_row<T, CH, HT, PT, 1, 1, PT>(hacc, sKdT + 16 * (ti0 / NVB) * PT, sVt + 16 * (ti0 % NVB) * PT);
-    } else {
+        for (int rb = 0; rb < NKB; ++rb)
 #pragma unroll
-      for (int i = 0; i < HT; ++i) {
-        const int ti = w * HT + i;
-        if (ti < NST) {
-          hacc[i] *= dlast;
-          mma_tile<T, CH, PT, 1, 1, PT>(hacc[i], sKdT + 16 * (ti / NVB) * PT, sVt + 16 * (ti % NVB) * PT);
+          for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              const int col = 16 * rb + 4 * q + st;
+              const float aw = sW[tix(16 * tt + t, col)];
+#pragma unroll
+              for (int cb = 0; cb < CBW; ++cb) vn[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw, hs[rb][cb][st], vn[tt][cb], 0, 0, 0);
+              if (!warm) {
+                const float aq = sQ[tix(16 * tt + t, col)];
+#pragma unroll
+                for (int cb = 0; cb < CBW; ++cb) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, hs[rb][cb][st], oa[tt][cb], 0, 0, 0);
+              }
+            }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KD / 32; ++ks) {
+          bf16x8 aw[4], aq[4], hb[CBW];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) aw[tt] = *reinterpret_cast<const bf16x8*>(sW + tix(16 * tt + t, 32 * ks + 8 * q));
+          if (!warm) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) aq[tt] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * tt + t, 32 * ks + 8 * q));
+          }
+#pragma unroll
+          for (int cb = 0; cb < CBW; ++cb) hb[cb] = pack_b(hs[2 * ks][cb], hs[2 * ks + 1][cb]);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int cb = 0; cb < CBW; ++cb) vn[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[tt], hb[cb], vn[tt][cb], 0, 0, 0);
+          if (!warm) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+              for (int cb = 0; cb < CBW; ++cb) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[tt], hb[cb], oa[tt][cb], 0, 0, 0);
+          }
+        }
+      }
+      float uv[4][4][CBW];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tt + acc_row(e);
+          if constexpr (CBW == 2 && !F32) {
+            const uint32_t pr = *reinterpret_cast<const uint32_t*>(sU + tix(r, 32 * w + 2 * t));
+            uv[tt][e][0] = __uint_as_float(pr << 16);
+            uv[tt][e][1] = __uint_as_float(pr & 0xffff0000u);
+          } else {
+#pragma unroll
+            for (int cb = 0; cb < CBW; ++cb) uv[tt][e][cb] = to_f(sU[tix(r, vcol(cb))]);
+          }
+        }
+      f32x4 vd[4][CBW];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tt + acc_row(e);
+          const float d = sD[r];
+          const float gm = sM[r];
+#pragma unroll
+          for (int cb = 0; cb < CBW; ++cb) {
+            vn[tt][cb][e] = uv[tt][e][cb] - vn[tt][cb][e];
+            vd[tt][cb][e] = vn[tt][cb][e] * d;
+            oa[tt][cb][e] *= gm;
+          }
+        }
+      // h' = Gamma_n h + K^T (d * Vnew).
+      const float gn = __expf(glast);
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CBW; ++cb) hs[rb][cb] *= gn;
+      if constexpr (F32) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int rb = 0; rb < NKB; ++rb) {
+              const float ak = sK[tix(16 * tt + 4 * q + st, 16 * rb + t)];
+#pragma unroll
+              for (int cb = 0; cb < CBW; ++cb)
+                hs[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, vd[tt][cb][st], hs[rb][cb], 0, 0, 0);
+            }
+      } else {
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const int sl = l & 15;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 ak[NKB], vb[CBW];
+#pragma unroll
+          for (int rb = 0; rb < NKB; ++rb) {
+            const int r0 = 32 * ks + 4 * q + (sl >> 2), cc = 32 * (rb >> 1) + 8 * (sl & 3) + 4 * (rb & 1);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sK + tix(r0, cc)));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sK + tix(r0 + 16, cc)));
+            ak[rb] = cat4(lo, hi);
+          }
+#pragma unroll
+          for (int cb = 0; cb < CBW; ++cb) vb[cb] = pack_b(vd[2 * ks][cb], vd[2 * ks + 1][cb]);
+#pragma unroll
+          for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < CBW; ++cb) hs[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[rb], vb[cb], hs[rb][cb], 0, 0, 0);
         }
       }
     }
-    lds_barrier();
-    if (!warm) {
-      store_rows<T, CH, VD, PK, NT>((T*)p.o + ((long)t0 * p.Hv + h) * VD, (long)p.Hv * VD, sW, len);
-      lds_barrier();
-    }
-  }
+    lds_barrier();  // P complete; the previous chunk's output rows are out of LDS
 
-  if (write_final && p.ht) {
+    if (!warm && owner) {  // O += P Vnew
+      if constexpr (F32) {
 #pragma unroll
-    for (int i = 0; i < HT; ++i) {
-      const int ti = w * HT + i, rb = ti / NVB, cb = ti % NVB;
-      if (ti < NST) {
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          p.ht[(((long)n * p.Hv + h) * KD + 16 * rb + acc_row(e)) * VD + 16 * cb + acc_col()] = hacc[i][e];
+          for (int tp = 0; tp <= tt; ++tp)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              const float ap = sP[(16 * tt + t) * PP + 16 * tp + 4 * q + st];
+#pragma unroll
+              for (int cb = 0; cb < CBW; ++cb)
+                oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ap, vn[tp][cb][st], oa[tt][cb], 0, 0, 0);
+            }
+        // fp32 output straight from the accumulators (16 lanes cover 64 contiguous bytes)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tt + acc_row(e);
+            if (r < len) {
+#pragma unroll
+              for (int cb = 0; cb < CBW; ++cb) ((T*)p.o)[((long)(t0 + r) * p.Hv + h) * VD + vcol(cb)] = oa[tt][cb][e];
+            }
+          }
+      } else {
+        bf16x8 ap[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int tt = 2 * ks; tt < 4; ++tt) ap[ks][tt] = *reinterpret_cast<const bf16x8*>(sP + (16 * tt + t) * PP + 32 * ks + 8 * q);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 vb[CBW];
+#pragma unroll
+          for (int cb = 0; cb < CBW; ++cb) vb[cb] = pack_b(vn[2 * ks][cb], vn[2 * ks + 1][cb]);
+#pragma unroll
+          for (int tt = 2 * ks; tt < 4; ++tt)
+#pragma unroll
+            for (int cb = 0; cb < CBW; ++cb) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[ks][tt], vb[cb], oa[tt][cb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tt + acc_row(e);
+            if constexpr (CBW == 2) {
+              bf16 lo = from_f<T>(oa[tt][0][e]), hi = from_f<T>(oa[tt][1][e]);
+              *reinterpret_cast<uint32_t*>(sO + tix(r, 32 * w + 2 * t)) =
+                  (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            } else {
+              sO[tix(r, vcol(0))] = from_f<T>(oa[tt][0][e]);
+            }
+          }
       }
     }
+    wait_copies(jc + 1, b ^ 1);   // the next chunk's tiles have landed; the output rows are staged
+    prev_out = !warm && !F32;
+    prev_t0 = t0;
+    prev_len = len;
+    b ^= 1;
+  }
+  if (prev_out) store_o(prev_t0, prev_len);
+
+  if (write_final && p.ht && owner) {
+#pragma unroll
+    for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p.ht[hbase + (long)(F32 ? 16 * rb + acc_row(e) : krow(rb, e)) * VD + vcol(cb)] = hs[rb][cb][e];
   }
 }
 
@@ -849,8 +1072,15 @@ static hipError_t state_impl(const StateParams& p, int total_segs, bool rows, hi
 template <typename T, int KD>
 static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t st) {
   const int total = total_segs * p.Hv;
+  constexpr int lds = FusedLds<T, KD>::BYTES;
+  static bool attr_set = false;   // dynamic LDS above 64 KB must be enabled per kernel
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_fused<T, KD>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   timing_before("chunk_fused", st);
-  hipLaunchKernelGGL((k_fused<T, KD>), dim3(padded_grid(total)), dim3(512), 0, st, p, total);
+  hipLaunchKernelGGL((k_fused<T, KD>), dim3(padded_grid(total)), dim3(FNT), lds, st, p, total);
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;
