@@ -620,6 +620,20 @@ __device__ __forceinline__ int stage_swz(int r) {
   else return (r >> 2) & (NCH - 1);
 }
 
+// One wave's share of copying a staged tile from global memory into LDS:
+// instruction j fills the 1 KB block w + 8j of the tile; off[j] is this
+// lane's byte offset in the source (rows past the descriptor range read 0).
+template <int NCP, int NCH, int FNWV, int VEC, typename T>
+__device__ __forceinline__ void lds_copy_tile(T* dst, rsrc_t rr, const uint32_t* off, int w) {
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int j = 0; j < NCP; ++j) {
+    const int i = w + FNWV * j;
+    if (NCH % FNWV == 0 || i < NCH)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(dst + 64 * i * VEC), 16, off[j], 0, 0, 0);
+  }
+}
+
 template <typename T, int KD>
 struct FusedLds {
   static constexpr bool F32 = std::is_same<T, float>::value;
@@ -709,30 +723,44 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
     }
 
-  // Copies chunk jc's tiles into buffer b (rows past the chunk read as zero).
-  auto copy_chunk = [&](int jc, int b) {
+  // Copies of chunk jc's tiles into buffer b (rows past the chunk read as
+  // zero), in four parts (0 W, 1 U, 2 K, 3 Q and the gate cumsums) that the
+  // chunk loop issues at different points, so that no wave stalls long on a
+  // full memory queue.  The per-lane byte offsets within a tile do not
+  // depend on the chunk.
+  constexpr int NCP = (NCH + FNW - 1) / FNW;   // copy instructions per wave and tile
+  uint32_t off_wu[NCP], off_qk[NCP];
+#pragma unroll
+  for (int j = 0; j < NCP; ++j) {
+    const int i = w + FNW * j;
+    const int pidx = 64 * i + l;
+    const int r = pidx / NCH, c = (pidx % NCH) ^ stage_swz<NCH>(r);
+    off_wu[j] = (uint32_t)(r * KD * (int)sizeof(T) + c * 16);
+    off_qk[j] = (uint32_t)(r * p.Hq * KD * (int)sizeof(T) + c * 16);
+  }
+  auto copy_part = [&](int jc, int b, int part) {
     typedef __attribute__((address_space(3))) void lds_void;
     const int t0 = s.cu[n] + jc * CH;
     const int len = min(CH, s.cu[n + 1] - t0);
-    const bool with_q = jc >= cbeg;
-    auto one = [&](T* dst, const T* g, long gstride) {
-      const rsrc_t rr = make_rsrc(g, (long)len * gstride * (long)sizeof(T));
-#pragma unroll
-      for (int i = w; i < NCH; i += FNW) {   // 1 KB of LDS per instruction
-        const int pidx = 64 * i + l;
-        const int r = pidx / NCH, c = (pidx % NCH) ^ stage_swz<NCH>(r);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(dst + 64 * i * VEC), 16,
-                                                 (uint32_t)(r * gstride * (long)sizeof(T)) + (uint32_t)c * 16u, 0, 0, 0);
+    const long wbytes = (long)len * KD * (long)sizeof(T), qbytes = wbytes * p.Hq;
+    if (part == 0)
+      lds_copy_tile<NCP, NCH, FNW, VEC>(tile(b, 0), make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
+    if (part == 1)
+      lds_copy_tile<NCP, NCH, FNW, VEC>(tile(b, 3), make_rsrc((const T*)p.U + ((long)h * s.Ttot + t0) * VD, wbytes), off_wu, w);
+    if (part == 2)
+      lds_copy_tile<NCP, NCH, FNW, VEC>(tile(b, 2), make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
+    if (part == 3) {
+      if (jc >= cbeg)
+        lds_copy_tile<NCP, NCH, FNW, VEC>(tile(b, 1), make_rsrc((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
+      if (w == 0) {
+        const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (lds_void*)(sGb + b * CH), 4, (uint32_t)l * 4u, 0, 0, 0);
       }
-    };
-    one(tile(b, 0), (const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD);
-    one(tile(b, 3), (const T*)p.U + ((long)h * s.Ttot + t0) * VD, VD);
-    one(tile(b, 2), (const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD);
-    if (with_q) one(tile(b, 1), (const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD);
-    if (w == 0) {
-      const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (lds_void*)(sGb + b * CH), 4, (uint32_t)l * 4u, 0, 0, 0);
     }
+  };
+  auto copy_chunk = [&](int jc, int b) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) copy_part(jc, b, part);
   };
   // Waits for this wave's copies; wave 0 (which copied the gate cumsums of
   // chunk jn into buffer bn) then derives that chunk's per-row factors; the
@@ -776,7 +804,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const int len = min(CH, s.cu[n + 1] - t0);
     if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) break;
     const bool warm = jc < cbeg;
-    if (jc + 1 < cend) copy_chunk(jc + 1, b ^ 1);
+    const bool more = jc + 1 < cend;
+    if (more) copy_part(jc + 1, b ^ 1, 0);
     const T* sW = tile(b, 0);
     const T* sQ = tile(b, 1);
     const T* sK = tile(b, 2);
@@ -785,8 +814,6 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const float* sD = sDb + (2 * b) * CH;
     const float* sM = sDb + (2 * b + 1) * CH;
     const float glast = sG[len - 1];
-
-    if (prev_out) store_o(prev_t0, prev_len);
 
     if (!warm) {  // P tiles: rows of tile ti, columns of tile tj
       // The ten lower tiles and the upper tiles (0,1), (2,3) that the
@@ -837,6 +864,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
     }
 
+    if (more) copy_part(jc + 1, b ^ 1, 1);
     f32x4 vn[4][CBW], oa[4][CBW];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -885,6 +913,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           }
         }
       }
+      if (more) copy_part(jc + 1, b ^ 1, 2);
       float uv[4][4][CBW];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -955,6 +984,9 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
         }
       }
     }
+    if (!owner && more) copy_part(jc + 1, b ^ 1, 2);
+    if (more) copy_part(jc + 1, b ^ 1, 3);
+    if (prev_out) store_o(prev_t0, prev_len);
     lds_barrier();  // P complete; the previous chunk's output rows are out of LDS
 
     if (!warm && owner) {  // O += P Vnew
