@@ -599,9 +599,12 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
 //   O    = s Gamma (Q h) + P Vnew,  P = s lower(D * Q K^T)
 // The chunk inputs W, Q, K, U and the gate cumsums are copied from global
 // memory straight into LDS (buffer loads with the LDS destination bit),
-// double-buffered: the next chunk's copy is issued when a chunk starts and
-// waited for at its end, so it overlaps the whole chunk and costs no
-// registers.  Staged tiles are unpadded with the 16-byte pieces of each row
+// double-buffered: the next chunk's copy is issued during a chunk and
+// waited for at its end, so it overlaps the chunk and costs no registers.
+// Every staged tile is its own LDS array and the chunk loop is unrolled by
+// two, so each chunk reads one fixed set of arrays and copies into the
+// other: the compiler then sees that the reads cannot alias the copies in
+// flight and does not wait for them before every LDS read.  Staged tiles are unpadded with the 16-byte pieces of each row
 // XOR-swizzled (row-dependent), which keeps the 8-byte fragment reads and
 // the transposing reads free of bank conflicts.  P tiles are shared (one or
 // two per wave); the bf16 output is staged in LDS and written as full rows.
@@ -620,53 +623,79 @@ __device__ __forceinline__ int stage_swz(int r) {
   else return (r >> 2) & (NCH - 1);
 }
 
+// Global -> LDS copy of 16 (or 4) bytes per lane: BUFFER_LOAD with the LDS
+// bit, lane l's bytes landing at lds + 16 l (4 l).  Issued through inline
+// assembly on purpose: the compiler's wait-count pass treats every later LDS
+// access as possibly aliasing a copy in flight and would wait for all
+// copies before it, serialising the copies with the chunk's compute.  The
+// kernels that use these wait for the copies themselves (vmcnt(0)) before
+// the barrier that publishes the data; nothing else in them uses M0.
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4v rsrc_words(rsrc_t r) {   // wave-uniform, in SGPRs
+  i32x4v v;
+  __builtin_memcpy(&v, &r, 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+__device__ __forceinline__ void lds_copy16(i32x4v rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_copy4(i32x4v rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+
 // One wave's share of copying a staged tile from global memory into LDS:
 // instruction j fills the 1 KB block w + 8j of the tile; off[j] is this
 // lane's byte offset in the source (rows past the descriptor range read 0).
 template <int NCP, int NCH, int FNWV, int VEC, typename T>
 __device__ __forceinline__ void lds_copy_tile(T* dst, rsrc_t rr, const uint32_t* off, int w) {
-  typedef __attribute__((address_space(3))) void lds_void;
+  const i32x4v rv = rsrc_words(rr);
 #pragma unroll
   for (int j = 0; j < NCP; ++j) {
     const int i = w + FNWV * j;
-    if (NCH % FNWV == 0 || i < NCH)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)(dst + 64 * i * VEC), 16, off[j], 0, 0, 0);
+    if (NCH % FNWV == 0 || i < NCH) lds_copy16(rv, off[j], lds_addr(dst + 64 * i * VEC));
   }
 }
 
-template <typename T, int KD>
-struct FusedLds {
-  static constexpr bool F32 = std::is_same<T, float>::value;
-  static constexpr int VEC = 16 / (int)sizeof(T);
-  static constexpr int NCH = KD / VEC;                     // 16-byte pieces per row
-  static constexpr int TILE = CH * KD * (int)sizeof(T);    // bytes per staged tile
-  static constexpr int PP = Pitch<T, CH>::value;
-  static constexpr int SZ_P = CH * PP * (int)sizeof(T);
-  static constexpr int SZ_O = F32 ? 0 : TILE;
-  static constexpr int OFF_P = 8 * TILE, OFF_O = OFF_P + SZ_P, OFF_G = OFF_O + SZ_O;
-  static constexpr int OFF_D = OFF_G + 2 * CH * 4;         // per-row factors, 2 buffers x {d, s Gamma}
-  static constexpr int BYTES = OFF_D + 4 * CH * 4;
+template <typename T>
+struct FusedBufs {   // one buffer of staged chunk inputs
+  T *W, *Q, *K, *U;
+  float *G, *D;      // gate cumsums; per-row factors {e^{gamma_n - gamma_t}, s e^{gamma_t}}
 };
+template <int V> using ic = std::integral_constant<int, V>;
 
 constexpr int FNW = 8, FNT = 64 * FNW;   // waves / threads of k_fused
 
 template <typename T, int KD>
 __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
-  using LY = FusedLds<T, KD>;
-  constexpr bool F32 = LY::F32;
+  constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
-  constexpr int VEC = LY::VEC, NCH = LY::NCH, PP = LY::PP;
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int NCH = KD / VEC;                    // 16-byte pieces per staged row
+  constexpr int PP = Pitch<T, CH>::value;
+  constexpr int TE = CH * KD;                      // elements per staged tile
   constexpr int NKB = KD / 16, NCB = VD / 16;
   constexpr int NWV = NCB < FNW ? NCB : FNW;       // waves owning state columns
   constexpr int CBW = NCB / NWV;                   // column tiles per owning wave
   static_assert(CBW == 1, "one column tile per wave");
-  extern __shared__ __align__(16) char dsm[];
-  // staged tile b, m (m: 0 W, 1 Q, 2 K, 3 U)
-  auto tile = [&](int b, int m) { return reinterpret_cast<T*>(dsm + (2 * m + b) * LY::TILE); };
-  T* sP = reinterpret_cast<T*>(dsm + LY::OFF_P);
-  T* sO = reinterpret_cast<T*>(dsm + LY::OFF_O);
-  float* sGb = reinterpret_cast<float*>(dsm + LY::OFF_G);
-  float* sDb = reinterpret_cast<float*>(dsm + LY::OFF_D);   // [b][0]: e^{gamma_n - gamma_t} (0 past the chunk), [b][1]: s e^{gamma_t}
+  __shared__ __align__(16) T sW0[TE], sQ0[TE], sK0[TE], sU0[TE], sW1[TE], sQ1[TE], sK1[TE], sU1[TE];
+  __shared__ __align__(16) T sP[CH * PP];
+  __shared__ __align__(16) T sO[F32 ? 8 : TE];     // bf16 output rows (fp32 stores directly)
+  __shared__ float sG0[CH], sG1[CH], sD0[2 * CH], sD1[2 * CH];
+  if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
+    const T z = from_f<T>(0.f);
+    sW0[threadIdx.x] = z; sQ0[threadIdx.x] = z; sK0[threadIdx.x] = z; sU0[threadIdx.x] = z;
+    sW1[threadIdx.x] = z; sQ1[threadIdx.x] = z; sK1[threadIdx.x] = z; sU1[threadIdx.x] = z;
+    sG0[threadIdx.x & 63] = 0.f; sG1[threadIdx.x & 63] = 0.f;
+  }
+  auto bufs = [&](auto bc) {
+    if constexpr (decltype(bc)::value == 0) return FusedBufs<T>{sW0, sQ0, sK0, sU0, sG0, sD0};
+    else return FusedBufs<T>{sW1, sQ1, sK1, sU1, sG1, sD1};
+  };
   // element offset of (row, col) in a staged tile
   auto tix = [](int r, int c) { return (r * NCH + ((c / VEC) ^ stage_swz<NCH>(r))) * VEC + (c % VEC); };
 
@@ -681,6 +710,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   const int c0 = s.chunk_off[n];
   const int nch = s.chunk_off[n + 1] - c0;
   if (pseg < 0 || pseg >= nseg || c0 < 0 || c0 + nch > s.NTtot) return;
+  const int seq0 = s.cu[n], seq1 = s.cu[n + 1];   // token range of the sequence
   const int L = p.seg_chunks;
   const int hk = h / (p.Hv / p.Hq);
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
@@ -724,9 +754,9 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     }
 
   // Copies of chunk jc's tiles into buffer b (rows past the chunk read as
-  // zero), in four parts (0 W, 1 U, 2 K, 3 Q and the gate cumsums) that the
-  // chunk loop issues at different points, so that no wave stalls long on a
-  // full memory queue.  The per-lane byte offsets within a tile do not
+  // zero), in four parts (0 W, 1 U, 2 K, 3 Q and the gate cumsums); the
+  // chunk loop issues W and U first and the rest after the P tiles, so that
+  // no wave stalls long on a full memory queue.  The per-lane byte offsets within a tile do not
   // depend on the chunk.
   constexpr int NCP = (NCH + FNW - 1) / FNW;   // copy instructions per wave and tile
   uint32_t off_wu[NCP], off_qk[NCP];
@@ -738,42 +768,42 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     off_wu[j] = (uint32_t)(r * KD * (int)sizeof(T) + c * 16);
     off_qk[j] = (uint32_t)(r * p.Hq * KD * (int)sizeof(T) + c * 16);
   }
-  auto copy_part = [&](int jc, int b, int part) {
-    typedef __attribute__((address_space(3))) void lds_void;
-    const int t0 = s.cu[n] + jc * CH;
-    const int len = min(CH, s.cu[n + 1] - t0);
+  auto copy_part = [&](int jc, auto bc, int part) {
+    const FusedBufs<T> bf = bufs(bc);
+    const int t0 = seq0 + jc * CH;
+    const int len = min(CH, seq1 - t0);
     const long wbytes = (long)len * KD * (long)sizeof(T), qbytes = wbytes * p.Hq;
     if (part == 0)
-      lds_copy_tile<NCP, NCH, FNW, VEC>(tile(b, 0), make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
+      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
     if (part == 1)
-      lds_copy_tile<NCP, NCH, FNW, VEC>(tile(b, 3), make_rsrc((const T*)p.U + ((long)h * s.Ttot + t0) * VD, wbytes), off_wu, w);
+      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, make_rsrc((const T*)p.U + ((long)h * s.Ttot + t0) * VD, wbytes), off_wu, w);
     if (part == 2)
-      lds_copy_tile<NCP, NCH, FNW, VEC>(tile(b, 2), make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
+      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
     if (part == 3) {
       if (jc >= cbeg)
-        lds_copy_tile<NCP, NCH, FNW, VEC>(tile(b, 1), make_rsrc((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
+        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.Q, make_rsrc((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
       if (w == 0) {
         const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (lds_void*)(sGb + b * CH), 4, (uint32_t)l * 4u, 0, 0, 0);
+        lds_copy4(rsrc_words(gr), (uint32_t)l * 4u, lds_addr(bf.G));
       }
     }
   };
-  auto copy_chunk = [&](int jc, int b) {
+  auto copy_chunk = [&](int jc, auto bc) {
 #pragma unroll
-    for (int part = 0; part < 4; ++part) copy_part(jc, b, part);
+    for (int part = 0; part < 4; ++part) copy_part(jc, bc, part);
   };
   // Waits for this wave's copies; wave 0 (which copied the gate cumsums of
   // chunk jn into buffer bn) then derives that chunk's per-row factors; the
   // barrier publishes everything.
-  auto wait_copies = [&](int jn, int bn) {
+  auto wait_copies = [&](int jn, auto bc) {
     __builtin_amdgcn_s_waitcnt(0);   // vmcnt = 0 (the LDS copies), expcnt = 0, lgkmcnt = 0
     if (w == 0 && jn < cend) {
-      const int tn = s.cu[n] + jn * CH;
-      const int ln = min(CH, s.cu[n + 1] - tn);
-      const float* g = sGb + bn * CH;
-      const float gl = g[max(ln, 1) - 1], gv = g[l];
-      sDb[(2 * bn) * CH + l] = (l < ln) ? __expf(gl - gv) : 0.f;
-      sDb[(2 * bn + 1) * CH + l] = p.scale * __expf(gv);
+      const FusedBufs<T> bf = bufs(bc);
+      const int tn = seq0 + jn * CH;
+      const int ln = min(CH, seq1 - tn);
+      const float gl = bf.G[max(ln, 1) - 1], gv = bf.G[l];
+      bf.D[l] = (l < ln) ? __expf(gl - gv) : 0.f;
+      bf.D[CH + l] = p.scale * __expf(gv);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt = 0
     }
     __builtin_amdgcn_s_barrier();
@@ -793,26 +823,32 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     }
   };
 
-  if (cstart < cend) copy_chunk(cstart, 0);
-  wait_copies(cstart, 0);
+  if (cstart < cend) copy_chunk(cstart, ic<0>());
+  wait_copies(cstart, ic<0>());
 
-  int b = 0;
   int prev_t0 = 0, prev_len = 0;
   bool prev_out = false;
-  for (int jc = cstart; jc < cend; ++jc) {
-    const int t0 = s.cu[n] + jc * CH;
-    const int len = min(CH, s.cu[n + 1] - t0);
-    if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) break;
+  // One chunk from buffer bc, copying chunk jc + 1 into the other buffer;
+  // false if the chunk tables are inconsistent (nothing is done then).
+  auto step = [&](auto bc, int jc) -> bool {
+    constexpr int b = decltype(bc)::value;
+    const int t0 = seq0 + jc * CH;
+    const int len = min(CH, seq1 - t0);
+    if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) return false;
     const bool warm = jc < cbeg;
     const bool more = jc + 1 < cend;
-    if (more) copy_part(jc + 1, b ^ 1, 0);
-    const T* sW = tile(b, 0);
-    const T* sQ = tile(b, 1);
-    const T* sK = tile(b, 2);
-    const T* sU = tile(b, 3);
-    const float* sG = sGb + b * CH;
-    const float* sD = sDb + (2 * b) * CH;
-    const float* sM = sDb + (2 * b + 1) * CH;
+    const FusedBufs<T> cur = bufs(bc);
+    if (more) {
+      copy_part(jc + 1, ic<1 - b>(), 0);
+      copy_part(jc + 1, ic<1 - b>(), 1);
+    }
+    const T* sW = cur.W;
+    const T* sQ = cur.Q;
+    const T* sK = cur.K;
+    const T* sU = cur.U;
+    const float* sG = cur.G;
+    const float* sD = cur.D;
+    const float* sM = cur.D + CH;
     const float glast = sG[len - 1];
 
     if (!warm) {  // P tiles: rows of tile ti, columns of tile tj
@@ -864,7 +900,10 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
     }
 
-    if (more) copy_part(jc + 1, b ^ 1, 1);
+    if (more) {
+      copy_part(jc + 1, ic<1 - b>(), 2);
+      copy_part(jc + 1, ic<1 - b>(), 3);
+    }
     f32x4 vn[4][CBW], oa[4][CBW];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -913,7 +952,6 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           }
         }
       }
-      if (more) copy_part(jc + 1, b ^ 1, 2);
       float uv[4][4][CBW];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -984,8 +1022,6 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
         }
       }
     }
-    if (!owner && more) copy_part(jc + 1, b ^ 1, 2);
-    if (more) copy_part(jc + 1, b ^ 1, 3);
     if (prev_out) store_o(prev_t0, prev_len);
     lds_barrier();  // P complete; the previous chunk's output rows are out of LDS
 
@@ -1044,11 +1080,14 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           }
       }
     }
-    wait_copies(jc + 1, b ^ 1);   // the next chunk's tiles have landed; the output rows are staged
+    wait_copies(jc + 1, ic<1 - b>());   // the next chunk's tiles have landed; the output rows are staged
     prev_out = !warm && !F32;
     prev_t0 = t0;
     prev_len = len;
-    b ^= 1;
+    return true;
+  };
+  for (int jc = cstart; jc < cend; jc += 2) {
+    if (!step(ic<0>(), jc) || jc + 1 >= cend || !step(ic<1>(), jc + 1)) break;
   }
   if (prev_out) store_o(prev_t0, prev_len);
 
@@ -1104,15 +1143,8 @@ static hipError_t state_impl(const StateParams& p, int total_segs, bool rows, hi
 template <typename T, int KD>
 static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t st) {
   const int total = total_segs * p.Hv;
-  constexpr int lds = FusedLds<T, KD>::BYTES;
-  static bool attr_set = false;   // dynamic LDS above 64 KB must be enabled per kernel
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_fused<T, KD>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   timing_before("chunk_fused", st);
-  hipLaunchKernelGGL((k_fused<T, KD>), dim3(padded_grid(total)), dim3(FNT), lds, st, p, total);
+  hipLaunchKernelGGL((k_fused<T, KD>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;
