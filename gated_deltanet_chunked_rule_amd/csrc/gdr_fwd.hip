@@ -91,8 +91,9 @@ __device__ __forceinline__ bool locate_chunk(const SeqTables& s, int c, int& n, 
 // Persistent: each workgroup walks a contiguous range of (chunk, value head)
 // items (value heads of one chunk adjacent, so the shared K tile is an L2
 // hit) and loads the next item's K, V, g and beta into a second register set
-// while the current one is computed.  Wave i owns row block i (tokens
-// 16i..16i+15) of A, W and U.  Per item:
+// while the current one is computed.  Each wave owns one row block (16
+// tokens) of A, W and U; "wave i" below means the owner of row block i.
+// Per item:
 //   1. K, V -> LDS with permuted columns (RowSlab); gate scan.
 //   2. L = strict_lower(diag(b)(D * K K^T)) in fp32, ten lower 16x16 tiles
 //      spread 3/2/3/2 over the waves; the diagonal of K K^T certifies
@@ -118,25 +119,18 @@ struct IntraItem {
   bool ok;
 };
 
-// acc + X Y for 16 x 16 fp32 tiles in LDS (pitch P); contraction index 4s + q
-// at step s for lane group q.
+// 16 x 16 fp32 tile products on V_MFMA_F32_16X16X4_F32 with the contraction
+// index 4q + s at step s for lane group q.  The A operand (row t of X,
+// columns 4q..4q+3) is one 16-byte LDS read; the B operand is a tile in
+// accumulator layout (lane group q holds rows 4q..4q+3 of column t), which is
+// where a product's result already is, or ld_acc() of an LDS tile.
 template <int P>
-__device__ __forceinline__ f32x4 mm_ll(f32x4 acc, const float* X, const float* Y) {
-  const int l = lane_id(), q = l >> 4, t = l & 15;
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[t * P + 4 * s + q], Y[(4 * s + q) * P + t], acc, 0, 0, 0);
-  return acc;
+__device__ __forceinline__ f32x4 ld_a(const float* X) {
+  return *reinterpret_cast<const f32x4*>(X + (lane_id() & 15) * P + 4 * (lane_id() >> 4));
 }
-// acc + X R, R a 16 x 16 accumulator tile in registers (lane group q holds
-// its rows 4q..4q+3): at step s group q contracts over index 4q + s, for
-// which it holds R's row in element s.
-template <int P>
-__device__ __forceinline__ f32x4 mm_lr(f32x4 acc, const float* X, f32x4 R) {
-  const int l = lane_id(), q = l >> 4, t = l & 15;
+__device__ __forceinline__ f32x4 mm(f32x4 acc, f32x4 a, f32x4 b) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[t * P + 4 * q + s], R[s], acc, 0, 0, 0);
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
   return acc;
 }
 // LDS tile -> accumulator layout, and back.
@@ -153,7 +147,7 @@ __device__ __forceinline__ void st_acc(float* X, f32x4 a) {
   for (int e = 0; e < 4; ++e) X[acc_row(e) * P + acc_col()] = a[e];
 }
 
-// Lower tiles (i, j) of K K^T computed by wave w (n-th of kk_count(w)).
+// Lower tiles (i, j) of K K^T computed by the owner of row block w (n-th of kk_count(w)).
 __device__ __forceinline__ int kk_count(int w) { return (w & 1) ? 2 : 3; }
 __device__ __forceinline__ void kk_tile(int w, int n, int& i, int& j) {
   // w0: (0,0) (3,0) (3,1)   w1: (1,0) (1,1)   w2: (2,0) (2,1) (2,2)   w3: (3,2) (3,3)
@@ -191,6 +185,10 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
   if (u0 >= u1) return;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
   const int q = l >> 4, t = l & 15;
+  // Row block of A, W, U owned by this wave.  The blocks differ in work (the
+  // last has the longest inverse chain and contraction), so the assignment
+  // rotates with the workgroup to spread the heavy one over the SIMDs.
+  const int rb = (w + x) & 3;
   auto tile = [&](int i, int j) { return sF + 16 * i * PF + 16 * j; };
 
   auto locate = [&](int u, IntraItem& it) {
@@ -242,13 +240,13 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
 
     // 2. L tiles.
     {
-      const int cnt = kk_count(w);
+      const int cnt = kk_count(rb);
       f32x4 acc[3];
       int ti[3], tj[3];
 #pragma unroll
       for (int n = 0; n < 3; ++n) {
         acc[n] = zero4();
-        kk_tile(w, n, ti[n], tj[n]);
+        kk_tile(rb, n, ti[n], tj[n]);
         if (n < cnt) mma_tile<T, KD, PK, 1, 1, PK>(acc[n], sK + 16 * ti[n] * PK, sK + 16 * tj[n] * PK);
       }
       int bad = 0;
@@ -277,67 +275,101 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
       p.cert[(long)h * s.NTtot + it.c] = any_bad ? INFINITY : sG[len - 1];
     }
 
-    // 3. Row block w of A into registers a0..a3 (tile j), zero above the diagonal.
+    // 3. Row block rb of A into registers a0..a3 (tile j), zero above the diagonal.
     f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4(), a3 = zero4();
     if (p.A_in) {
       const float* src = p.A_in + ((long)t0 * p.Hv + h) * CH;
       const long rs = (long)p.Hv * CH;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + acc_row(e);
+        const int r = 16 * rb + acc_row(e);
         if (r < len) {
           const float* row = src + (long)r * rs;
-          if (0 <= w && t < len) a0[e] = row[t];
-          if (1 <= w && 16 + t < len) a1[e] = row[16 + t];
-          if (2 <= w && 32 + t < len) a2[e] = row[32 + t];
-          if (3 <= w && 48 + t < len) a3[e] = row[48 + t];
+          if (0 <= rb && t < len) a0[e] = row[t];
+          if (1 <= rb && 16 + t < len) a1[e] = row[16 + t];
+          if (2 <= rb && 32 + t < len) a2[e] = row[32 + t];
+          if (3 <= rb && 48 + t < len) a3[e] = row[48 + t];
         }
       }
     } else {
-      // Diagonal block by forward substitution (lane l < 16 solves column l),
-      // written over L_ww.
-      if (l < 16) {
-        float xs[16];
+      // Diagonal block.  bf16: N = L_ii is nilpotent (N^16 = 0), so
+      //   (I + N)^-1 = (I + N^8)(I + N^4)(I + N^2)(I - N),
+      // applied right to left so that the running product is always the
+      // right factor; N^2, N^4, N^8 pass through the tile itself.  Its fp32
+      // rounding error (below 1e-3 even for nearly parallel keys) is under
+      // the bf16 rounding that A' and A'' get next.  fp32: forward
+      // substitution (lane l < 16 solves column l), exact to rounding.
+      float* D = tile(rb, rb);
+      f32x4 dg;
+      if constexpr (F32) {
+        if (l < 16) {
+          float xs[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float acc = (r == l) ? 1.f : 0.f;
-          const float* Lr = sF + (16 * w + r) * PF + 16 * w;
+          for (int r = 0; r < 16; ++r) {
+            float acc = (r == l) ? 1.f : 0.f;
+            const float* Lr = D + r * PF;
 #pragma unroll
-          for (int jj = 0; jj < r; ++jj) acc -= Lr[jj] * xs[jj];
-          xs[r] = acc;
+            for (int jj = 0; jj < r; ++jj) acc -= Lr[jj] * xs[jj];
+            xs[r] = acc;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) D[r * PF + l] = xs[r];
         }
+        wave_sync();
+        dg = ld_acc<PF>(D);
+      } else {
+        const f32x4 aN = ld_a<PF>(D), cN = ld_acc<PF>(D);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sF[(16 * w + r) * PF + 16 * w + l] = xs[r];
+        for (int e = 0; e < 4; ++e) dg[e] = (acc_row(e) == acc_col() ? 1.f : 0.f) - cN[e];
+        f32x4 pw = mm(zero4(), aN, cN);   // N^2
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {     // N^(2^(k+1))
+          wave_sync();
+          st_acc<PF>(D, pw);
+          wave_sync();
+          const f32x4 ap = ld_a<PF>(D);
+          dg = mm(dg, ap, dg);
+          if (k < 2) pw = mm(zero4(), ap, pw);
+        }
+        wave_sync();
+        st_acc<PF>(D, dg);
+        wave_sync();
       }
-      wave_sync();
-      // M_wj = A_ww L_wj over L_wj.
-      for (int j = 0; j < w; ++j) st_acc<PF>(tile(w, j), mm_ll<PF>(zero4(), tile(w, w), tile(w, j)));
+      // M_ij = A_ii L_ij over L_ij.
+      {
+        const f32x4 aA = ld_a<PF>(D);
+        for (int j = 0; j < rb; ++j) st_acc<PF>(tile(rb, j), mm(zero4(), aA, ld_acc<PF>(tile(rb, j))));
+      }
       lds_barrier();
-      const f32x4 dg = ld_acc<PF>(tile(w, w));
-      if (w == 0) {
+      if (rb == 0) {
         a0 = dg;
-      } else if (w == 1) {
-        a0 = -mm_ll<PF>(zero4(), tile(1, 0), tile(0, 0));
+      } else if (rb == 1) {
+        a0 = -mm(zero4(), ld_a<PF>(tile(1, 0)), ld_acc<PF>(tile(0, 0)));
         a1 = dg;
-      } else if (w == 2) {
-        const f32x4 t10 = mm_ll<PF>(zero4(), tile(1, 0), tile(0, 0));
-        a0 = mm_lr<PF>(-mm_ll<PF>(zero4(), tile(2, 0), tile(0, 0)), tile(2, 1), t10);
-        a1 = -mm_ll<PF>(zero4(), tile(2, 1), tile(1, 1));
+      } else if (rb == 2) {
+        const f32x4 m10 = ld_a<PF>(tile(1, 0)), m20 = ld_a<PF>(tile(2, 0)), m21 = ld_a<PF>(tile(2, 1));
+        const f32x4 d00 = ld_acc<PF>(tile(0, 0)), d11 = ld_acc<PF>(tile(1, 1));
+        const f32x4 t10 = mm(zero4(), m10, d00);
+        a0 = mm(-mm(zero4(), m20, d00), m21, t10);
+        a1 = -mm(zero4(), m21, d11);
         a2 = dg;
       } else {
-        const f32x4 t10 = mm_ll<PF>(zero4(), tile(1, 0), tile(0, 0));
-        const f32x4 t21 = mm_ll<PF>(zero4(), tile(2, 1), tile(1, 1));
-        const f32x4 a20 = mm_lr<PF>(-mm_ll<PF>(zero4(), tile(2, 0), tile(0, 0)), tile(2, 1), t10);
-        a0 = mm_lr<PF>(mm_lr<PF>(-mm_ll<PF>(zero4(), tile(3, 0), tile(0, 0)), tile(3, 1), t10), tile(3, 2), -a20);
-        a1 = mm_lr<PF>(-mm_ll<PF>(zero4(), tile(3, 1), tile(1, 1)), tile(3, 2), t21);
-        a2 = -mm_ll<PF>(zero4(), tile(3, 2), tile(2, 2));
+        const f32x4 m10 = ld_a<PF>(tile(1, 0)), m20 = ld_a<PF>(tile(2, 0)), m21 = ld_a<PF>(tile(2, 1));
+        const f32x4 m30 = ld_a<PF>(tile(3, 0)), m31 = ld_a<PF>(tile(3, 1)), m32 = ld_a<PF>(tile(3, 2));
+        const f32x4 d00 = ld_acc<PF>(tile(0, 0)), d11 = ld_acc<PF>(tile(1, 1)), d22 = ld_acc<PF>(tile(2, 2));
+        const f32x4 t10 = mm(zero4(), m10, d00);
+        const f32x4 t21 = mm(zero4(), m21, d11);
+        const f32x4 a20 = mm(-mm(zero4(), m20, d00), m21, t10);
+        a0 = mm(mm(-mm(zero4(), m30, d00), m31, t10), m32, -a20);
+        a1 = mm(-mm(zero4(), m31, d11), m32, t21);
+        a2 = -mm(zero4(), m32, d22);
         a3 = dg;
       }
     }
     if (p.A_ws || p.A_out) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * w + acc_row(e);
+        const int r = 16 * rb + acc_row(e);
         if (r < len) {
           const float v4[4] = {a0[e], a1[e], a2[e], a3[e]};
 #pragma unroll
@@ -357,33 +389,33 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
       sw[j] = su[j] * __expf(sG[16 * j + t]);
     }
     lds_barrier();
-    const int nks = F32 ? 4 * (w + 1) : (w + 2) / 2;  // contraction steps (A' is zero beyond 16(w+1))
-    const int ntile = F32 ? w + 1 : 2 * nks;          // A' tiles the steps read
+    const int nks = F32 ? 4 * (rb + 1) : (rb + 2) / 2;  // contraction steps (A' is zero beyond 16(rb+1))
+    const int ntile = F32 ? rb + 1 : 2 * nks;          // A' tiles the steps read
     {
       const f32x4 av[4] = {a0, a1, a2, a3};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (j < ntile) {
-          acc_store_t<T, PA>(sAw, 16 * w, 16 * j, av[j], sw[j]);
-          acc_store_t<T, PA>(sAu, 16 * w, 16 * j, av[j], su[j]);
+          acc_store_t<T, PA>(sAw, 16 * rb, 16 * j, av[j], sw[j]);
+          acc_store_t<T, PA>(sAu, 16 * rb, 16 * j, av[j], su[j]);
         }
       }
     }
     wave_sync();
 
-    // 5. W = A' K, U = A'' V for row block w.
+    // 5. W = A' K, U = A'' V for row block rb.
     auto gemm_store = [&](const T* sAT, const T* sX, void* dst, int D) {
       f32x4 acc[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) acc[j] = zero4();
       for (int ks = 0; ks < nks; ++ks) {
         if constexpr (F32) {
-          const float a = sAT[(4 * ks + q) * PA + 16 * w + t];
+          const float a = sAT[(4 * ks + q) * PA + 16 * rb + t];
 #pragma unroll
           for (int j = 0; j < NT; ++j)
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sX[(4 * ks + q) * PK + 16 * j + t], acc[j], 0, 0, 0);
         } else {
-          const bf16x8 a = tr_frag(sAT + 32 * ks * PA + 16 * w, PA);
+          const bf16x8 a = tr_frag(sAT + 32 * ks * PA + 16 * rb, PA);
 #pragma unroll
           for (int j = 0; j < NT; ++j)
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, tr_frag(sX + 32 * ks * PK + 16 * j, PK), acc[j], 0, 0, 0);
@@ -392,7 +424,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
       const rsrc_t rr = make_rsrc((const T*)dst + ((long)h * s.Ttot + t0) * D, (long)len * D * (long)sizeof(T));
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        store_acc_row<T, NT>(rr, (uint32_t)(((16 * w + acc_row(e)) * D + NT * t) * (int)sizeof(T)), acc, e);
+        store_acc_row<T, NT>(rr, (uint32_t)(((16 * rb + acc_row(e)) * D + NT * t) * (int)sizeof(T)), acc, e);
     };
     gemm_store(sAw, sK, p.W, KD);
     gemm_store(sAu, sV, p.U, VD);
