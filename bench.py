@@ -9,6 +9,10 @@ WY, serial state, output) through the C ABI on resident device buffers.
 Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant
 kernel (its HIP-event duration on the launch stream, against the algorithmic
 bytes or flops per launch) and the fp64 CPU oracle's throughput on the host.
+The line also carries "configs_report": the other parity configurations (tiny
+fp32, edge prefill, varlen forward and the backward), each timed per call
+with a cache flush between calls and set against the method's roofline
+(essential I/O and chunk-GEMM flops per token x value head).
 """
 from __future__ import annotations
 
@@ -22,6 +26,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_long_context.json")
 MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 MFMA
+MFMA_F32_PEAK_TFS = 157.3      # dense fp32 MFMA
 METRIC = "GDN chunked-prefill fwd tokens/s (B=1,T=64K,Hv=8) + % MFMA/HBM roofline"
 
 
@@ -68,12 +73,87 @@ def measured_traffic(kernel: str):
     return 1024.0 * (k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"])
 
 
+def method_work(K, V, G, esize, backward):
+    """The method's flops and essential bytes per token x value head (64-token
+    chunks): forward 6KV + 6CK + 4CV + C^2/3 flops and q, k (shared by the G
+    value heads), v, o, g, beta bytes; backward 16KV + 18CK + 10CV + C^2 flops
+    and q, k, v, do, dq, dk, dv, g, beta, dg, dbeta bytes."""
+    C = 64
+    if backward:
+        return (16 * K * V + 18 * C * K + 10 * C * V + C * C,
+                4 * K * esize / G + 3 * V * esize + 16)
+    return (6 * K * V + 6 * C * K + 4 * C * V + C * C / 3,
+            2 * K * esize / G + 2 * V * esize + 8)
+
+
+def config_report(torch, gdr, gi, dev):
+    """Per-call time of the other parity configurations against the method's
+    roofline; a 1 GiB buffer is rewritten between calls so that no input is
+    served from the last-level cache."""
+    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    out = {}
+    for name, backward, iters in (("tiny_fp32", False, 20), ("edge_prefill", False, 10),
+                                  ("varlen", False, 5), ("backward", True, 5)):
+        w = gi.WORKLOADS[name]
+        inp = gi.make_inputs(w)
+        d = {n: (x.to(dev) if hasattr(x, "to") and n != "cu_seqlens" else x) for n, x in inp.items()}
+        cu = inp.get("cu_seqlens")
+        h0 = d.get("initial_state")
+        if backward:
+            args = (d["q"], d["k"], d["v"], d["g"], d["beta"], None, d["do"], d["dht"], d["scale"], h0, cu)
+            call = lambda: gdr.gdr_chunk_bwd(*args)
+        else:
+            call = lambda: gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], h0, cu)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        times = []
+        gdr.timing.reset()
+        gdr.timing.enable(True)
+        for _ in range(iters):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        gdr.timing.enable(False)
+        kern = gdr.timing.collect()
+        ms = sorted(times)[len(times) // 2]
+        tokens = w.B * w.T
+        tv = tokens * w.Hv
+        esize = 4 if w.dtype == "f32" else 2
+        flops_tv, bytes_tv = method_work(w.K, w.V, w.Hv // w.Hq, esize, backward)
+        state_bytes = 0
+        nseq = len(cu) - 1 if cu is not None else w.B
+        if h0 is not None:
+            state_bytes += nseq * w.Hv * w.K * w.V * 4
+        state_bytes += nseq * w.Hv * w.K * w.V * 4 * (3 if backward else 1)  # final_state / dht, dh0
+        flops, nbytes = flops_tv * tv, bytes_tv * tv + state_bytes
+        peak = MFMA_F32_PEAK_TFS if w.dtype == "f32" else MFMA_BF16_PEAK_TFS
+        t_mfma, t_hbm = flops / (peak * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
+        t_roof = max(t_mfma, t_hbm)
+        out[name] = {
+            "pass": "bwd" if backward else "fwd", "tokens": tokens, "ms": round(ms, 4),
+            "tokens_per_s": round(tokens / (ms * 1e-3)),
+            "roof": {"bound": "mfma" if t_mfma > t_hbm else "hbm", "t_roof_us": round(t_roof * 1e6, 2),
+                     "frac": round(t_roof / (ms * 1e-3), 4), "gflop": round(flops / 1e9, 3),
+                     "mbytes": round(nbytes / 1e6, 2)},
+            "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in kern.items()},
+        }
+        del d, inp
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration report")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -159,6 +239,18 @@ def main():
                "sample": f"fp64 token recurrence over the whole workload ({t_sample} tokens x {w.Hv} "
                          f"value heads), one thread per head"}
 
+    # the method's own roofline for this workload (essential I/O, chunk-GEMM flops)
+    mf, mb = method_work(w.K, w.V, G, 2, False)
+    t_m, t_b = mf * tv / (MFMA_BF16_PEAK_TFS * 1e12), mb * tv / (HBM_PEAK_GBS * 1e9)
+    method_roof = {"bound": "mfma" if t_m > t_b else "hbm", "t_roof_us": round(max(t_m, t_b) * 1e6, 2),
+                   "frac": round(max(t_m, t_b) / (ms_per_step * 1e-3), 4)}
+
+    configs = None
+    if not args.no_configs:
+        del q, k, v, g, beta, ws
+        torch.cuda.empty_cache()
+        configs = config_report(torch, gdr, gi, dev)
+
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -168,7 +260,9 @@ def main():
                    "cp_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"]},
         "kernels_us": {n: 1e3 * t / c for n, (t, c) in kern.items()},
         "roofline": roof,
+        "method_roofline": method_roof,
         "cpu_baseline": cpu,
+        "configs_report": configs,
     }
     print(json.dumps(out))
 
