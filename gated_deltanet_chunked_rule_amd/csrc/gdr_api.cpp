@@ -38,11 +38,12 @@ struct Problem {
   // plan
   int BV = 0, nvb = 0, L = 1, W = 0, total_segs = 0;
   float log_eps = 0.f;
+  bool serial_fallback = false;   // uncertified heads run serially instead of exact segments
 };
 
 struct Layout {
   size_t cu = 0, chunk_off = 0, seg_off = 0, gcum = 0, cert = 0, W = 0, U = 0, vnew = 0, hbuf = 0;
-  size_t A = 0, dhbuf = 0, dvn = 0, total = 0;
+  size_t A = 0, dhbuf = 0, dvn = 0, segtr = 0, hstart = 0, total = 0;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -142,6 +143,9 @@ gdr_status analyze(const gdr_shape* sh, const gdr_options* op, const int32_t* cu
     else if (op->cp_warmup_chunks < 0) return fail(GDR_ERR_INVALID_ARG, "cp_warmup_chunks must be >= 0");
     if (op->cp_log_eps != 0.f) P.log_eps = op->cp_log_eps;
     if (!(P.log_eps < 0.f)) return fail(GDR_ERR_INVALID_ARG, "cp_log_eps must be negative");
+    if (op->cp_serial_fallback != 0 && op->cp_serial_fallback != 1)
+      return fail(GDR_ERR_INVALID_ARG, "cp_serial_fallback must be 0 or 1");
+    P.serial_fallback = op->cp_serial_fallback == 1;
   }
   P.BV = (P.K == 128) ? 64 : 32;
   P.nvb = P.V / P.BV;
@@ -161,6 +165,11 @@ gdr_status analyze(const gdr_shape* sh, const gdr_options* op, const int32_t* cu
   return GDR_OK;
 }
 
+// Forward with CP segments: heads that fail the warmup certificate get exact
+// segment start states (transition pass + scan) unless the caller asked for
+// the serial fallback.
+bool exact_cp(const Problem& P) { return P.L < P.NTmax && !P.serial_fallback; }
+
 Layout layout(const Problem& P, bool bwd) {
   Layout Lo;
   size_t off = 0;
@@ -177,12 +186,16 @@ Layout layout(const Problem& P, bool bwd) {
   Lo.cert = take(hv * nt * 4);
   Lo.W = take(hv * tt * P.K * P.esize);
   Lo.U = take(hv * tt * P.V * P.esize);
-  Lo.vnew = take(hv * nt * P.V * kChunk * P.esize);
-  Lo.hbuf = take(hv * nt * P.V * P.K * P.esize);
   if (bwd) {
+    Lo.vnew = take(hv * tt * P.V * P.esize);
+    Lo.hbuf = take(hv * nt * P.V * P.K * P.esize);
     Lo.A = take(hv * tt * kChunk * 4);
     Lo.dhbuf = take(hv * nt * P.V * P.K * P.esize);
     Lo.dvn = take(hv * tt * P.V * P.esize);
+  } else if (exact_cp(P)) {
+    const size_t segs = (size_t)P.total_segs, kv = (size_t)P.K * P.V * 4;
+    Lo.segtr = take(hv * segs * 2 * kv);
+    Lo.hstart = take(hv * segs * kv);
   }
   Lo.total = off;
   return Lo;
@@ -242,8 +255,22 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     fp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
     fp.cert = reinterpret_cast<const float*>(ws + Lo.cert);
     fp.h0 = h0; fp.ht = ht; fp.o = o;
-    fp.Hq = P.Hq; fp.Hv = P.Hv; fp.seg_chunks = L; fp.warmup = P.W;
+    fp.Hq = P.Hq; fp.Hv = P.Hv; fp.seg_chunks = L; fp.warmup = P.W; fp.total_segs = segs;
     fp.log_eps = P.log_eps; fp.scale = scale;
+    fp.trans = 0; fp.segtr = nullptr; fp.hstart = nullptr;
+    if (exact_cp(P)) {
+      // transitions (M, b) of the uncertified heads' segments, then their exact start states
+      gdr::FusedParams tp = fp;
+      tp.trans = 1;
+      tp.segtr = reinterpret_cast<float*>(ws + Lo.segtr);
+      if ((e = gdr::launch_fused(P.dt, P.K, tp, segs, st)) != hipSuccess) return hip_fail(e, "transition launch");
+      gdr::ScanParams sc;
+      sc.s = s; sc.cert = fp.cert; sc.segtr = tp.segtr;
+      sc.hstart = reinterpret_cast<float*>(ws + Lo.hstart);
+      sc.Hv = P.Hv; sc.seg_chunks = L; sc.warmup = P.W; sc.total_segs = segs; sc.log_eps = P.log_eps;
+      if ((e = gdr::launch_segscan(P.K, sc, P.N * P.Hv, st)) != hipSuccess) return hip_fail(e, "scan launch");
+      fp.hstart = sc.hstart;
+    }
     if ((e = gdr::launch_fused(P.dt, P.K, fp, segs, st)) != hipSuccess) return hip_fail(e, "fused launch");
   } else {
     // backward recompute: every chunk's entry state and Vnew, row layouts

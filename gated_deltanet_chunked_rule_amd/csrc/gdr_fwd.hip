@@ -642,6 +642,13 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
 // two per wave); the bf16 output is staged in LDS and written as full rows.
 // Two workgroup barriers per chunk.  Two waves per SIMD hide each other's
 // LDS and MFMA latencies.
+// Segment transitions (p.trans = 1, heads that fail the warmup certificate):
+// the map from a segment's start state to its end state is affine,
+// h_out = M h_in + b, so one workgroup per (segment, part) runs the segment's
+// chunks without output from h = I with U taken as zero (part 0: M, from the
+// second segment on) or from h = 0, the initial state for the first segment,
+// with U (part 1: b), and stores the end state.  k_segscan chains them into
+// exact start states, from which the output pass then runs every segment.
 // Row numbering: state tile rb, lane group g, element e holds K row
 // 32(rb/2) + 8g + 4(rb%2) + e, so the two tiles of a 32-row contraction step
 // give a lane K rows 32ks + 8g .. +7, and the W and Q fragments that match
@@ -724,7 +731,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     sW1[threadIdx.x] = z; sQ1[threadIdx.x] = z; sK1[threadIdx.x] = z; sU1[threadIdx.x] = z;
     sG0[threadIdx.x & 63] = 0.f; sG1[threadIdx.x & 63] = 0.f;
   }
-  auto bufs = [&](auto bc) {
+  auto bufs = [&](auto bc) __attribute__((always_inline)) {
     if constexpr (decltype(bc)::value == 0) return FusedBufs<T>{sW0, sQ0, sK0, sU0, sG0, sD0};
     else return FusedBufs<T>{sW1, sQ1, sK1, sU1, sG1, sD1};
   };
@@ -735,7 +742,9 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   const int u = xcd_remap(blockIdx.x, total_items);
   if (u >= total_items) return;
   const int h = u % p.Hv;
-  const int item = u / p.Hv;
+  const int item2 = u / p.Hv;
+  const int part = p.trans ? (item2 & 1) : 1;   // transition pass: 0 M, 1 b
+  const int item = p.trans ? (item2 >> 1) : item2;
   const int n = find_seq(s.seg_off, s.N, item);
   const int pseg = item - s.seg_off[n];
   const int nseg = s.seg_off[n + 1] - s.seg_off[n];
@@ -759,29 +768,55 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     }
   }
   const bool certified = !__syncthreads_or(!ok);
+  const int gseg = s.seg_off[n] + pseg;          // global segment index
+  const bool exact = !certified && p.hstart != nullptr;
   int cstart, cbeg, cend;
   bool write_final;
-  if (!certified) {
-    if (pseg != 0) return;             // segment 0 runs the whole head serially
-    cstart = 0; cbeg = 0; cend = nch; write_final = true;
-  } else {
+  if (p.trans) {   // uncertified heads only; the last segment's map is not needed
+    if (certified || pseg == nseg - 1 || (part == 0 && pseg == 0)) return;
+    cbeg = cstart = pseg * L;
+    cend = min(cbeg + L, nch);
+    write_final = false;
+  } else if (certified) {
     cbeg = pseg * L;
     cend = min(cbeg + L, nch);
     cstart = (pseg == 0) ? 0 : max(0, cbeg - p.warmup);
     write_final = (pseg == nseg - 1);
+  } else if (exact) {
+    cbeg = cstart = pseg * L;
+    cend = min(cbeg + L, nch);
+    write_final = (pseg == nseg - 1);
+  } else {
+    if (pseg != 0) return;             // segment 0 runs the whole head serially
+    cstart = 0; cbeg = 0; cend = nch; write_final = true;
   }
+  const bool no_u = p.trans && part == 0;         // M: the segment's map with U = 0
 
   const long hbase = ((long)n * p.Hv + h) * KD * VD;
   auto krow = [&](int rb, int e) { return 32 * (rb >> 1) + 8 * q + 4 * (rb & 1) + e; };
+  // Initial state: h0 at a sequence start, an exact start state, the identity
+  // (transition part 0) or zero.
+  const float* hinit = nullptr;
+  if (p.trans) {
+    if (part == 1 && pseg == 0 && p.h0) hinit = p.h0 + hbase;
+  } else if (cstart == 0) {
+    if (p.h0) hinit = p.h0 + hbase;
+  } else if (exact) {
+    hinit = p.hstart + ((long)h * p.total_segs + gseg) * KD * VD;
+  }
   f32x4 hs[NKB][CBW];
 #pragma unroll
   for (int rb = 0; rb < NKB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CBW; ++cb) {
       hs[rb][cb] = zero4();
-      if (owner && cstart == 0 && p.h0) {
+      if (owner) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hs[rb][cb][e] = p.h0[hbase + (long)(F32 ? 16 * rb + acc_row(e) : krow(rb, e)) * VD + vcol(cb)];
+        for (int e = 0; e < 4; ++e) {
+          const int row = F32 ? 16 * rb + acc_row(e) : krow(rb, e), col = vcol(cb);
+          if (no_u) hs[rb][cb][e] = (row == col) ? 1.f : 0.f;
+          else if (hinit) hs[rb][cb][e] = hinit[(long)row * VD + col];
+        }
       }
     }
 
@@ -800,19 +835,19 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     off_wu[j] = (uint32_t)(r * KD * (int)sizeof(T) + c * 16);
     off_qk[j] = (uint32_t)(r * p.Hq * KD * (int)sizeof(T) + c * 16);
   }
-  auto copy_part = [&](int jc, auto bc, int part) {
+  auto copy_part = [&](int jc, auto bc, int piece) __attribute__((always_inline)) {
     const FusedBufs<T> bf = bufs(bc);
     const int t0 = seq0 + jc * CH;
     const int len = min(CH, seq1 - t0);
     const long wbytes = (long)len * KD * (long)sizeof(T), qbytes = wbytes * p.Hq;
-    if (part == 0)
+    if (piece == 0)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
-    if (part == 1)
+    if (piece == 1 && !no_u)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, make_rsrc((const T*)p.U + ((long)h * s.Ttot + t0) * VD, wbytes), off_wu, w);
-    if (part == 2)
+    if (piece == 2)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
-    if (part == 3) {
-      if (jc >= cbeg)
+    if (piece == 3) {
+      if (jc >= cbeg && !p.trans)
         lds_copy_tile<NCP, NCH, FNW, VEC>(bf.Q, make_rsrc((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
       if (w == 0) {
         const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
@@ -820,14 +855,14 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
     }
   };
-  auto copy_chunk = [&](int jc, auto bc) {
+  auto copy_chunk = [&](int jc, auto bc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int part = 0; part < 4; ++part) copy_part(jc, bc, part);
+    for (int piece = 0; piece < 4; ++piece) copy_part(jc, bc, piece);
   };
   // Waits for this wave's copies; wave 0 (which copied the gate cumsums of
   // chunk jn into buffer bn) then derives that chunk's per-row factors; the
   // barrier publishes everything.
-  auto wait_copies = [&](int jn, auto bc) {
+  auto wait_copies = [&](int jn, auto bc) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);   // vmcnt = 0 (the LDS copies), expcnt = 0, lgkmcnt = 0
     if (w == 0 && jn < cend) {
       const FusedBufs<T> bf = bufs(bc);
@@ -842,7 +877,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
   // bf16 output rows of a chunk from sO to global memory.
-  auto store_o = [&](int ot0, int olen) {
+  auto store_o = [&](int ot0, int olen) __attribute__((always_inline)) {
     if constexpr (!F32) {
       const rsrc_t rr = make_rsrc((T*)p.o + ((long)ot0 * p.Hv + h) * VD, (long)olen * p.Hv * VD * (long)sizeof(T));
       const uint32_t rs = (uint32_t)(p.Hv * VD * (int)sizeof(T));
@@ -862,12 +897,12 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   bool prev_out = false;
   // One chunk from buffer bc, copying chunk jc + 1 into the other buffer;
   // false if the chunk tables are inconsistent (nothing is done then).
-  auto step = [&](auto bc, int jc) -> bool {
+  auto step = [&](auto bc, int jc) __attribute__((always_inline)) -> bool {
     constexpr int b = decltype(bc)::value;
     const int t0 = seq0 + jc * CH;
     const int len = min(CH, seq1 - t0);
     if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) return false;
-    const bool warm = jc < cbeg;
+    const bool warm = jc < cbeg || p.trans;   // no output for this chunk
     const bool more = jc + 1 < cend;
     const FusedBufs<T> cur = bufs(bc);
     if (more) {
@@ -998,6 +1033,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 #pragma unroll
             for (int cb = 0; cb < CBW; ++cb) uv[tt][e][cb] = to_f(sU[tix(r, vcol(cb))]);
           }
+#pragma unroll
+          for (int cb = 0; cb < CBW; ++cb) uv[tt][e][cb] = no_u ? 0.f : uv[tt][e][cb];  // U tile not copied for M
         }
       f32x4 vd[4][CBW];
 #pragma unroll
@@ -1123,6 +1160,15 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   }
   if (prev_out) store_o(prev_t0, prev_len);
 
+  if (p.trans && owner) {
+    float* dst = p.segtr + (((long)h * p.total_segs + gseg) * 2 + part) * KD * VD;
+#pragma unroll
+    for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(long)(F32 ? 16 * rb + acc_row(e) : krow(rb, e)) * VD + vcol(cb)] = hs[rb][cb][e];
+  }
   if (write_final && p.ht && owner) {
 #pragma unroll
     for (int rb = 0; rb < NKB; ++rb)
@@ -1130,6 +1176,77 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       for (int cb = 0; cb < CBW; ++cb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) p.ht[hbase + (long)(F32 ? 16 * rb + acc_row(e) : krow(rb, e)) * VD + vcol(cb)] = hs[rb][cb][e];
+  }
+}
+
+// -------------------------------------------------------------- k_segscan --
+// Exact start states of the CP segments of heads that fail the warmup
+// certificate: h_1 = b_0 (the first segment's end state from the initial
+// state), h_{s+1} = M_s h_s + b_s.  One 8-wave workgroup per (sequence,
+// value head); wave w owns state columns 16w..16w+15 in fp32 accumulators,
+// which are the B operand of the next M_s product; M_s is staged in LDS.
+template <int KD>
+__global__ __launch_bounds__(FNT) void k_segscan(ScanParams p, int total_items) {
+  constexpr int VD = KD, NKB = KD / 16, NCB = VD / 16, PM = KD + 4;
+  __shared__ __align__(16) float sM[KD * PM];
+  const SeqTables& s = p.s;
+  const int u = xcd_remap(blockIdx.x, total_items);
+  if (u >= total_items) return;
+  const int h = u % p.Hv, n = u / p.Hv;
+  if (n >= s.N) return;
+  const int nseg = s.seg_off[n + 1] - s.seg_off[n];
+  const int c0 = s.chunk_off[n];
+  const int L = p.seg_chunks;
+  if (nseg <= 1 || c0 < 0) return;
+  int ok = 1;
+  for (int qq = 1 + (int)threadIdx.x; qq < nseg; qq += FNT) {
+    const int ws = qq * L - p.warmup;
+    if (ws > 0) {
+      float sum = 0.f;
+      for (int cc = ws; cc < qq * L; ++cc) sum += p.cert[(long)h * s.NTtot + c0 + cc];
+      if (!(sum <= p.log_eps)) ok = 0;
+    }
+  }
+  if (!__syncthreads_or(!ok)) return;   // certified: the warmup path needs no start states
+  const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
+  const bool owner = w < NCB;
+  const int col = 16 * w + t;
+  const long head = (long)h * p.total_segs + s.seg_off[n];
+  auto tr = [&](int sg, int part) { return p.segtr + ((head + sg) * 2 + part) * KD * VD; };
+  f32x4 hs[NKB];
+#pragma unroll
+  for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hs[rb][e] = owner ? tr(0, 1)[(long)(16 * rb + acc_row(e)) * VD + col] : 0.f;
+  for (int sg = 1; sg < nseg; ++sg) {
+    if (owner) {
+      float* dst = p.hstart + (head + sg) * KD * VD;
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(long)(16 * rb + acc_row(e)) * VD + col] = hs[rb][e];
+    }
+    if (sg == nseg - 1) break;
+    const float* M = tr(sg, 0);
+    for (int i = threadIdx.x; i < KD * KD / 4; i += FNT) {
+      const int r = i / (KD / 4), c4 = (i % (KD / 4)) * 4;
+      *reinterpret_cast<float4*>(sM + r * PM + c4) = *reinterpret_cast<const float4*>(M + (long)r * KD + c4);
+    }
+    __syncthreads();
+    if (owner) {
+      const float* bsg = tr(sg, 1);
+      f32x4 acc[NKB];
+#pragma unroll
+      for (int ot = 0; ot < NKB; ++ot) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[ot][e] = bsg[(long)(16 * ot + acc_row(e)) * VD + col];
+#pragma unroll
+        for (int rb = 0; rb < NKB; ++rb) acc[ot] = mm(acc[ot], ld_a<PM>(sM + 16 * ot * PM + 16 * rb), hs[rb]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb) hs[rb] = acc[rb];
+    }
+    __syncthreads();
   }
 }
 
@@ -1174,9 +1291,20 @@ static hipError_t state_impl(const StateParams& p, int total_segs, bool rows, hi
 
 template <typename T, int KD>
 static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t st) {
-  const int total = total_segs * p.Hv;
-  timing_before("chunk_fused", st);
+  const int total = total_segs * p.Hv * (p.trans ? 2 : 1);
+  timing_before(p.trans ? "cp_transition" : "chunk_fused", st);
   hipLaunchKernelGGL((k_fused<T, KD>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  hipError_t err = hipGetLastError();
+  timing_after(st);
+  return err;
+}
+
+hipError_t launch_segscan(int KD, const ScanParams& p, int total_items, hipStream_t st) {
+  timing_before("cp_scan", st);
+  const dim3 grid(padded_grid(total_items)), block(FNT);
+  if (KD == 32) hipLaunchKernelGGL(k_segscan<32>, grid, block, 0, st, p, total_items);
+  else if (KD == 64) hipLaunchKernelGGL(k_segscan<64>, grid, block, 0, st, p, total_items);
+  else hipLaunchKernelGGL(k_segscan<128>, grid, block, 0, st, p, total_items);
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;

@@ -5,13 +5,13 @@
 //   gcum  fp32 [Hv][Ttot]          chunk-local inclusive cumsum of g
 //   cert  fp32 [Hv][NTtot]         chunk gate sum, +inf if some beta|k|^2 is outside [0, 2]
 //   W, U  T    [Hv][Ttot][K|V]     W = A diag(beta*Gamma) K,  U = A diag(beta) V
-//   vnew  T    forward: [Hv][NTtot][V][64]  Vnew = U - W h per chunk, transposed
-//              backward: [Hv][Ttot][V]     the same values as token rows
-//   hbuf  T    forward: [Hv][NTtot][V][K]  state entering each chunk, transposed
-//              backward: [Hv][NTtot][K][V] the same states, row-major
+//   vnew  T    [Hv][Ttot][V]       Vnew = U - W h (token rows; backward only)
+//   hbuf  T    [Hv][NTtot][K][V]   state entering each chunk (backward only)
 //   A     fp32 [Hv][Ttot][64]      rows of the chunk's A (backward only)
 //   dhbuf T    [Hv][NTtot][K][V]   gradient of the state leaving each chunk
 //   dvn   T    [Hv][Ttot][V]       gradient of Vnew (token rows)
+//   segtr fp32 [Hv][segs][2][K][V] per CP segment: M (start -> end state map) and b
+//   hstart fp32 [Hv][segs][K][V]   exact start state of each CP segment
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,8 +73,19 @@ struct FusedParams {         // forward state recurrence fused with the output
   float* ht;                 // nullable [N][Hv][K][V]
   void* o;                   // [Ttot][Hv][V]
   int Hq, Hv;
-  int seg_chunks, warmup;
+  int seg_chunks, warmup, total_segs;
   float log_eps, scale;
+  int trans;                 // 1: segment-transition pass (no output), 0: output pass
+  float* segtr;              // transition pass: [Hv][total_segs][2][K][V] {M, b}
+  const float* hstart;       // nullable: exact segment start states [Hv][total_segs][K][V]
+};
+
+struct ScanParams {          // exact segment start states from the segment transitions
+  SeqTables s;
+  const float *cert, *segtr;
+  float* hstart;
+  int Hv, seg_chunks, warmup, total_segs;
+  float log_eps;
 };
 
 struct DStateParams {        // reverse state pass
@@ -106,6 +117,7 @@ hipError_t launch_intra(DType dt, int KD, const IntraParams& p, hipStream_t st);
 hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int total_segs, bool rows,
                         hipStream_t st);
 hipError_t launch_fused(DType dt, int KD, const FusedParams& p, int total_segs, hipStream_t st);
+hipError_t launch_segscan(int KD, const ScanParams& p, int total_items, hipStream_t st);
 hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, int total_items, hipStream_t st);
 hipError_t launch_grads(DType dt, int KD, const GradParams& p, hipStream_t st);
 

@@ -84,8 +84,14 @@ typedef struct {
  * the `cp_warmup_chunks` chunks before it, which is exact up to a factor
  * exp(sum of g over those chunks).  A head whose every warmup window has
  * sum(g) <= cp_log_eps (and beta |k|^2 in [0, 2]) is certified and uses the
- * segments; any other head is computed serially, so results never depend on
- * an uncertified warmup.  Pass NULL for the defaults. */
+ * segments.  Any other head (for example one with g = 0) gets its segment
+ * start states exactly instead: the map from a segment's start state to its
+ * end state is affine, h_out = M h_in + b (the correction matrix the Tongyi
+ * page describes for CP), so every segment's (M, b) is computed in parallel,
+ * the start states follow from a short scan, and the segments then run from
+ * them; with cp_serial_fallback = 1 such heads run serially instead.  Results
+ * never depend on an uncertified warmup.  Pass NULL for the defaults; a
+ * zero-initialised struct also gives the defaults. */
 typedef enum { GDR_CP_AUTO = 0, GDR_CP_OFF = 1, GDR_CP_FORCE = 2 } gdr_cp_mode;
 
 typedef struct {
@@ -93,6 +99,7 @@ typedef struct {
   int32_t cp_segment_chunks; /* GDR_CP_FORCE: chunks per segment (>= 1) */
   int32_t cp_warmup_chunks;  /* warmup chunks before each segment; default 8 */
   float cp_log_eps;          /* certificate threshold on sum(g); default ln(1e-6) */
+  int32_t cp_serial_fallback;/* 1: uncertified heads run serially; 0 (default): exact segment states */
 } gdr_options;
 
 /* What the planner chose for a forward call (for tests and reporting). */

@@ -179,3 +179,30 @@ def test_nearly_parallel_keys_without_decay(dtype, K, spread):
     inp["beta"] = torch.ones_like(inp["beta"])
     inp["g"] = torch.zeros_like(inp["g"])
     check_fwd(inp, label=f"nearly parallel keys {dtype}")
+
+
+@pytest.mark.parametrize("dtype,K,seg", [("bf16", 128, 3), ("bf16", 64, 1), ("f32", 32, 2)])
+def test_exact_segments_for_uncertified_heads(dtype, K, seg):
+    # g = 0 on every head: no warmup window is certified, so every head takes
+    # the exact path (segment transitions, scan, then the segments from their
+    # exact start states), here with an initial state and a ragged tail.
+    w = gi.custom(B=2, T=64 * 11 + 23, Hq=2, Hv=4, K=K, V=K, dtype=dtype, seed=80, initial_state=True,
+                  zero_gate_frac=1.0)
+    check_fwd(gi.make_inputs(w), gdr.Options(gdr.CP_FORCE, seg, 2), label=f"exact segments L={seg}")
+
+
+def test_serial_fallback_option_for_uncertified_heads():
+    w = gi.custom(B=1, T=64 * 24 + 5, Hq=2, Hv=8, K=128, V=128, dtype="bf16", seed=81, initial_state=True,
+                  gate=(0.9, 0.999), zero_gate_frac=0.5)
+    inp = gi.make_inputs(w)
+    o1, h1 = check_fwd(inp, gdr.Options(gdr.CP_FORCE, 4, 2, 0.0, 1), label="serial fallback")
+    o2, h2 = check_fwd(inp, gdr.Options(gdr.CP_FORCE, 4, 2, 0.0, 0), label="exact segments")
+    # both reach the same recurrence; they differ only by rounding order
+    assert rel_err(o1, f64(o2)) <= 2e-2 and rel_err(h1, f64(h2)) <= 1e-2
+
+
+def test_exact_segments_varlen():
+    w = gi.custom(B=1, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=82, initial_state=True,
+                  gate=(0.9, 0.999), zero_gate_frac=0.5)
+    inp = gi.packed_from_lengths(w, [64 * 9 + 7, 1, 64 * 3, 0, 64 * 6 + 40])
+    check_fwd(inp, gdr.Options(gdr.CP_FORCE, 2, 1), label="varlen exact segments")
