@@ -1182,24 +1182,27 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 // -------------------------------------------------------------- k_segscan --
 // Exact start states of the CP segments of heads that fail the warmup
 // certificate: h_1 = b_0 (the first segment's end state from the initial
-// state), h_{s+1} = M_s h_s + b_s.  One 8-wave workgroup per (sequence,
-// value head); wave w owns state columns 16w..16w+15 in fp32 accumulators,
-// which are the B operand of the next M_s product; M_s is staged in LDS.
+// state), h_{s+1} = M_s h_s + b_s.  State columns are independent, so one
+// workgroup per (sequence, value head, 16-column block) with KD/16 waves;
+// wave w produces rows 16w..16w+15.  The A operand (rows of M_s) comes
+// straight from memory into registers, one step ahead; the state slice
+// lives in LDS transposed (column-major), double-buffered, so each lane's B
+// operand is one 16-byte read and each step needs one barrier.
 template <int KD>
-__global__ __launch_bounds__(FNT) void k_segscan(ScanParams p, int total_items) {
-  constexpr int VD = KD, NKB = KD / 16, NCB = VD / 16, PM = KD + 4;
-  __shared__ __align__(16) float sM[KD * PM];
+__global__ __launch_bounds__(KD * 4) void k_segscan(ScanParams p, int total_items) {
+  constexpr int VD = KD, NKB = KD / 16, NCB = VD / 16, PH = KD + 4;
+  __shared__ __align__(16) float sH[2][16 * PH];
   const SeqTables& s = p.s;
   const int u = xcd_remap(blockIdx.x, total_items);
   if (u >= total_items) return;
-  const int h = u % p.Hv, n = u / p.Hv;
+  const int cb = u % NCB, h = (u / NCB) % p.Hv, n = u / (NCB * p.Hv);
   if (n >= s.N) return;
   const int nseg = s.seg_off[n + 1] - s.seg_off[n];
   const int c0 = s.chunk_off[n];
   const int L = p.seg_chunks;
   if (nseg <= 1 || c0 < 0) return;
   int ok = 1;
-  for (int qq = 1 + (int)threadIdx.x; qq < nseg; qq += FNT) {
+  for (int qq = 1 + (int)threadIdx.x; qq < nseg; qq += KD * 4) {
     const int ws = qq * L - p.warmup;
     if (ws > 0) {
       float sum = 0.f;
@@ -1209,44 +1212,46 @@ __global__ __launch_bounds__(FNT) void k_segscan(ScanParams p, int total_items) 
   }
   if (!__syncthreads_or(!ok)) return;   // certified: the warmup path needs no start states
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
-  const bool owner = w < NCB;
-  const int col = 16 * w + t;
+  const int col = 16 * cb + t, row0 = 16 * w + 4 * q;
   const long head = (long)h * p.total_segs + s.seg_off[n];
   auto tr = [&](int sg, int part) { return p.segtr + ((head + sg) * 2 + part) * KD * VD; };
-  f32x4 hs[NKB];
+  auto load_m = [&](int sg, f32x4 (&a)[NKB]) {
+    const float* M = tr(sg, 0) + (long)(16 * w + t) * KD + 4 * q;
 #pragma unroll
-  for (int rb = 0; rb < NKB; ++rb)
+    for (int rb = 0; rb < NKB; ++rb) a[rb] = *reinterpret_cast<const f32x4*>(M + 16 * rb);
+  };
+  auto load_b = [&](int sg, f32x4& b) {
+    const float* B = tr(sg, 1) + (long)row0 * VD + col;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) hs[rb][e] = owner ? tr(0, 1)[(long)(16 * rb + acc_row(e)) * VD + col] : 0.f;
+    for (int e = 0; e < 4; ++e) b[e] = B[(long)e * VD];
+  };
+  f32x4 hs, bn, a[NKB];
+  load_b(0, hs);
+  if (nseg > 2) { load_m(1, a); load_b(1, bn); }
   for (int sg = 1; sg < nseg; ++sg) {
-    if (owner) {
-      float* dst = p.hstart + (head + sg) * KD * VD;
+    float* dst = p.hstart + (head + sg) * KD * VD + (long)row0 * VD + col;
 #pragma unroll
-      for (int rb = 0; rb < NKB; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(long)(16 * rb + acc_row(e)) * VD + col] = hs[rb][e];
-    }
+    for (int e = 0; e < 4; ++e) dst[(long)e * VD] = hs[e];
     if (sg == nseg - 1) break;
-    const float* M = tr(sg, 0);
-    for (int i = threadIdx.x; i < KD * KD / 4; i += FNT) {
-      const int r = i / (KD / 4), c4 = (i % (KD / 4)) * 4;
-      *reinterpret_cast<float4*>(sM + r * PM + c4) = *reinterpret_cast<const float4*>(M + (long)r * KD + c4);
-    }
+    float* buf = sH[sg & 1];
+    *reinterpret_cast<f32x4*>(buf + t * PH + row0) = hs;
     __syncthreads();
-    if (owner) {
-      const float* bsg = tr(sg, 1);
-      f32x4 acc[NKB];
+    f32x4 an[NKB], bnn = bn;
+    const bool more = sg + 1 < nseg - 1;
+    if (more) { load_m(sg + 1, an); load_b(sg + 1, bnn); }
+    f32x4 acc0 = bn, acc1 = zero4();
 #pragma unroll
-      for (int ot = 0; ot < NKB; ++ot) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[ot][e] = bsg[(long)(16 * ot + acc_row(e)) * VD + col];
-#pragma unroll
-        for (int rb = 0; rb < NKB; ++rb) acc[ot] = mm(acc[ot], ld_a<PM>(sM + 16 * ot * PM + 16 * rb), hs[rb]);
-      }
-#pragma unroll
-      for (int rb = 0; rb < NKB; ++rb) hs[rb] = acc[rb];
+    for (int rb = 0; rb < NKB; rb += 2) {
+      acc0 = mm(acc0, a[rb], *reinterpret_cast<const f32x4*>(buf + t * PH + 16 * rb + 4 * q));
+      if (rb + 1 < NKB) acc1 = mm(acc1, a[rb + 1], *reinterpret_cast<const f32x4*>(buf + t * PH + 16 * (rb + 1) + 4 * q));
     }
-    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hs[e] = acc0[e] + acc1[e];
+    if (more) {
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb) a[rb] = an[rb];
+      bn = bnn;
+    }
   }
 }
 
@@ -1301,7 +1306,8 @@ static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t s
 
 hipError_t launch_segscan(int KD, const ScanParams& p, int total_items, hipStream_t st) {
   timing_before("cp_scan", st);
-  const dim3 grid(padded_grid(total_items)), block(FNT);
+  total_items *= KD / 16;   // one workgroup per 16-column block
+  const dim3 grid(padded_grid(total_items)), block(KD * 4);
   if (KD == 32) hipLaunchKernelGGL(k_segscan<32>, grid, block, 0, st, p, total_items);
   else if (KD == 64) hipLaunchKernelGGL(k_segscan<64>, grid, block, 0, st, p, total_items);
   else hipLaunchKernelGGL(k_segscan<128>, grid, block, 0, st, p, total_items);
