@@ -165,10 +165,13 @@ gdr_status analyze(const gdr_shape* sh, const gdr_options* op, const int32_t* cu
   return GDR_OK;
 }
 
-// Forward with CP segments: heads that fail the warmup certificate get exact
-// segment start states (transition pass + scan) unless the caller asked for
-// the serial fallback.
-bool exact_cp(const Problem& P) { return P.L < P.NTmax && !P.serial_fallback; }
+// CP segments (forward, and the bf16 backward): heads that fail the warmup
+// certificate get exact segment start states (transition pass + scan) unless
+// the caller asked for the serial fallback.
+bool exact_cp(const Problem& P, int L) { return L < P.NTmax && !P.serial_fallback; }
+bool exact_cp(const Problem& P) { return exact_cp(P, P.L); }
+// The bf16 backward runs its serial passes in CP segments; fp32 runs them whole.
+bool bwd_segmented(const Problem& P) { return P.dt == gdr::DType::BF16; }
 
 Layout layout(const Problem& P, bool bwd) {
   Layout Lo;
@@ -192,7 +195,8 @@ Layout layout(const Problem& P, bool bwd) {
     Lo.A = take(hv * tt * kChunk * 4);
     Lo.dhbuf = take(hv * nt * P.V * P.K * P.esize);
     Lo.dvn = take(hv * tt * P.V * P.esize);
-  } else if (exact_cp(P)) {
+  }
+  if (exact_cp(P) && (!bwd || bwd_segmented(P))) {
     const size_t segs = (size_t)P.total_segs, kv = (size_t)P.K * P.V * 4;
     Lo.segtr = take(hv * segs * 2 * kv);
     Lo.hstart = take(hv * segs * kv);
@@ -248,8 +252,9 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
   }
   int segs = 0;
   for (int c : P.chunks) segs += std::max(1, (c + L - 1) / L);
-  if (!bwd) {
-    // forward: state recurrence fused with the output
+  if (!bwd || bwd_segmented(P)) {
+    // forward: state recurrence fused with the output; backward recompute:
+    // the same pass storing every chunk's entry state and Vnew instead
     gdr::FusedParams fp;
     fp.s = s; fp.q = q; fp.k = k; fp.W = ws + Lo.W; fp.U = ws + Lo.U;
     fp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
@@ -258,7 +263,10 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     fp.Hq = P.Hq; fp.Hv = P.Hv; fp.seg_chunks = L; fp.warmup = P.W; fp.total_segs = segs;
     fp.log_eps = P.log_eps; fp.scale = scale;
     fp.trans = 0; fp.segtr = nullptr; fp.hstart = nullptr;
-    if (exact_cp(P)) {
+    fp.rev_cert = bwd ? 1 : 0;
+    fp.hbuf = bwd ? ws + Lo.hbuf : nullptr;
+    fp.vnew = bwd ? ws + Lo.vnew : nullptr;
+    if (exact_cp(P, L)) {
       // transitions (M, b) of the uncertified heads' segments, then their exact start states
       gdr::FusedParams tp = fp;
       tp.trans = 1;
@@ -268,6 +276,7 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
       sc.s = s; sc.cert = fp.cert; sc.segtr = tp.segtr;
       sc.hstart = reinterpret_cast<float*>(ws + Lo.hstart);
       sc.Hv = P.Hv; sc.seg_chunks = L; sc.warmup = P.W; sc.total_segs = segs; sc.log_eps = P.log_eps;
+      sc.rev = 0; sc.rev_cert = fp.rev_cert;
       if ((e = gdr::launch_segscan(P.K, sc, P.N * P.Hv, st)) != hipSuccess) return hip_fail(e, "scan launch");
       fp.hstart = sc.hstart;
     }
@@ -378,22 +387,54 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
     return fail(GDR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(Lo.total) + " bytes");
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // Recompute g_cum, A, W, U and the chunk states (no context parallelism in
-  // the backward: the reverse pass needs every chunk's exact state).
-  const int Lfull = std::max(P.NTmax, 1);
+  // Recompute g_cum, A, W, U and every chunk's entry state and Vnew.  bf16
+  // runs both serial passes in CP segments: the states from warmup or exact
+  // segment starts, and the reverse pass the same way from segment ends
+  // (exact end gradients from the reverse offsets, the transposed segment
+  // transitions and a reverse scan).  fp32 runs each head whole.
+  const int L = bwd_segmented(P) ? P.L : std::max(P.NTmax, 1);
   st = run_forward_chain(P, Lo, ws, q, k, v, g, beta, scale, initial_state, cu_seqlens, nullptr,
-                         nullptr, nullptr, nullptr, reinterpret_cast<float*>(ws + Lo.A), A, Lfull, true, hs);
+                         nullptr, nullptr, nullptr, reinterpret_cast<float*>(ws + Lo.A), A, L, true, hs);
   if (st != GDR_OK) return st;
   if (P.NTtot == 0 && !dh0) return GDR_OK;
   const gdr::SeqTables s = tables(P, Lo, ws);
   hipError_t e;
-  gdr::DStateParams dp;
-  dp.s = s; dp.q = q; dp.k = k; dp.W = ws + Lo.W; dp.d_o = d_o;
-  dp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
-  dp.dht = dht; dp.dh0 = dh0; dp.dhbuf = ws + Lo.dhbuf; dp.dvn = ws + Lo.dvn;
-  dp.Hq = P.Hq; dp.Hv = P.Hv; dp.scale = scale; dp.nvb = P.nvb;
-  if ((e = gdr::launch_dstate(P.dt, P.K, P.BV, dp, P.N * P.Hv * P.nvb, hs)) != hipSuccess)
-    return hip_fail(e, "dstate launch");
+  if (bwd_segmented(P)) {
+    gdr::DFusedParams dp;
+    dp.s = s; dp.q = q; dp.k = k; dp.W = ws + Lo.W; dp.d_o = d_o;
+    dp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
+    dp.cert = reinterpret_cast<const float*>(ws + Lo.cert);
+    dp.dht = dht; dp.dh0 = dh0; dp.dhbuf = ws + Lo.dhbuf; dp.dvn = ws + Lo.dvn;
+    dp.Hq = P.Hq; dp.Hv = P.Hv; dp.seg_chunks = L; dp.warmup = P.W; dp.total_segs = P.total_segs;
+    dp.log_eps = P.log_eps; dp.scale = scale;
+    dp.trans = 0; dp.segtr = nullptr; dp.dhstart = nullptr;
+    if (exact_cp(P, L)) {
+      // reverse offsets d_s (into segtr part 1, whose b_s are spent), then
+      // the exact end gradients (into hstart, whose start states are spent)
+      gdr::DFusedParams tp = dp;
+      tp.trans = 1;
+      tp.segtr = reinterpret_cast<float*>(ws + Lo.segtr);
+      if ((e = gdr::launch_dfused(P.dt, P.K, tp, P.total_segs, hs)) != hipSuccess)
+        return hip_fail(e, "reverse transition launch");
+      gdr::ScanParams sc;
+      sc.s = s; sc.cert = dp.cert; sc.segtr = tp.segtr;
+      sc.hstart = reinterpret_cast<float*>(ws + Lo.hstart);
+      sc.Hv = P.Hv; sc.seg_chunks = L; sc.warmup = P.W; sc.total_segs = P.total_segs;
+      sc.log_eps = P.log_eps; sc.rev = 1; sc.rev_cert = 1;
+      if ((e = gdr::launch_segscan(P.K, sc, P.N * P.Hv, hs)) != hipSuccess) return hip_fail(e, "reverse scan launch");
+      dp.dhstart = sc.hstart;
+    }
+    if ((e = gdr::launch_dfused(P.dt, P.K, dp, P.total_segs, hs)) != hipSuccess)
+      return hip_fail(e, "reverse pass launch");
+  } else {
+    gdr::DStateParams dp;
+    dp.s = s; dp.q = q; dp.k = k; dp.W = ws + Lo.W; dp.d_o = d_o;
+    dp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
+    dp.dht = dht; dp.dh0 = dh0; dp.dhbuf = ws + Lo.dhbuf; dp.dvn = ws + Lo.dvn;
+    dp.Hq = P.Hq; dp.Hv = P.Hv; dp.scale = scale; dp.nvb = P.nvb;
+    if ((e = gdr::launch_dstate(P.dt, P.K, P.BV, dp, P.N * P.Hv * P.nvb, hs)) != hipSuccess)
+      return hip_fail(e, "dstate launch");
+  }
   if (P.NTtot > 0) {
     gdr::GradParams gp;
     gp.s = s; gp.q = q; gp.k = k; gp.v = v; gp.d_o = d_o; gp.hbuf = ws + Lo.hbuf;

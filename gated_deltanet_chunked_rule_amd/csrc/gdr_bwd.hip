@@ -210,6 +210,329 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
   }
 }
 
+// -------------------------------------------------------------- k_dfused --
+// The reverse state pass of the backward, cut into CP segments like the
+// forward's fused pass: one 8-wave workgroup per (sequence, value head,
+// segment), chunks in reverse order.  Wave w owns state-gradient columns
+// 16w..16w+15 over all K rows in fp32 accumulators, rows numbered as in
+// k_fused.  Per chunk, with dh the gradient of the state leaving it:
+//   kd  = K dh                             (dh as the MFMA B operand)
+//   dh <- Gamma_n dh + s (Gamma Q)^T dO    (Q^T by transposing LDS reads)
+//   dVn = s P^T dO + dec * kd,  dec_t = e^{gamma_n - gamma_t},  P = lower(D * Q K^T)
+//   dh <- dh - W^T dVn
+// and dh entering the chunk (before the update) and dVn are stored for the
+// per-chunk gradients.  The dO terms do not depend on dh, so the map from a
+// segment's end gradient to its start gradient is affine with the forward
+// transition transposed: dh_in = M^T dh_out + d.  A certified head runs each
+// segment from up to W warmup chunks after its end, from zero (or from the
+// final-state gradient when the window reaches the sequence end); other
+// heads run from exact end gradients (k_segscan, reverse mode), and with
+// trans = 1 compute the offsets d of their segments from a zero end
+// gradient (the last from the final-state gradient).  Q, K, W, dO and the
+// gate cumsums are copied into LDS one chunk ahead as in k_fused; P^T is
+// stored with its token columns permuted as k_fused permutes P.
+template <typename T>
+struct DFusedBufs {   // one buffer of staged chunk inputs
+  T *W, *Q, *K, *O;
+  float *G, *D;       // gate cumsums; per-row factors {e^{gamma_n - gamma_t}, s e^{gamma_t}}
+};
+
+template <int KD>
+__global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items) {
+  using T = bf16;
+  constexpr int VD = KD;
+  constexpr int VEC = 8;
+  constexpr int NCH = KD / VEC;
+  constexpr int PP = Pitch<T, CH>::value;
+  constexpr int TE = CH * KD;
+  constexpr int NKB = KD / 16, NCB = VD / 16;
+  constexpr int NWV = NCB < FNW ? NCB : FNW;
+  static_assert(NCB <= FNW && NKB % 2 == 0, "one column tile per wave, paired row tiles");
+  __shared__ __align__(16) T sW0[TE], sQ0[TE], sK0[TE], sO0[TE], sW1[TE], sQ1[TE], sK1[TE], sO1[TE];
+  __shared__ __align__(16) T sP[CH * PP];
+  __shared__ float sG0[CH], sG1[CH], sD0[2 * CH], sD1[2 * CH];
+  if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
+    const T z = from_f<T>(0.f);
+    sW0[threadIdx.x] = z; sQ0[threadIdx.x] = z; sK0[threadIdx.x] = z; sO0[threadIdx.x] = z;
+    sW1[threadIdx.x] = z; sQ1[threadIdx.x] = z; sK1[threadIdx.x] = z; sO1[threadIdx.x] = z;
+    sG0[threadIdx.x & 63] = 0.f; sG1[threadIdx.x & 63] = 0.f;
+  }
+  auto bufs = [&](auto bc) __attribute__((always_inline)) {
+    if constexpr (decltype(bc)::value == 0) return DFusedBufs<T>{sW0, sQ0, sK0, sO0, sG0, sD0};
+    else return DFusedBufs<T>{sW1, sQ1, sK1, sO1, sG1, sD1};
+  };
+  auto tix = [](int r, int c) { return (r * NCH + ((c / VEC) ^ stage_swz<NCH>(r))) * VEC + (c % VEC); };
+
+  const SeqTables& s = p.s;
+  const int u = xcd_remap(blockIdx.x, total_items);
+  if (u >= total_items) return;
+  const int h = u % p.Hv;
+  const int item = u / p.Hv;
+  const int n = find_seq(s.seg_off, s.N, item);
+  const int pseg = item - s.seg_off[n];
+  const int nseg = s.seg_off[n + 1] - s.seg_off[n];
+  const int c0 = s.chunk_off[n];
+  const int nch = s.chunk_off[n + 1] - c0;
+  if (pseg < 0 || pseg >= nseg || c0 < 0 || c0 + nch > s.NTtot) return;
+  const int seq0 = s.cu[n], seq1 = s.cu[n + 1];
+  const int L = p.seg_chunks;
+  const int hk = h / (p.Hv / p.Hq);
+  const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15, sl = l & 15;
+  const bool owner = w < NWV;
+  const int col = 16 * w + t;
+  const bool certified =
+      head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, true);
+  const int gseg = s.seg_off[n] + pseg;
+  const long hbase = ((long)n * p.Hv + h) * KD * VD;
+  // chunks crs down to cbeg; those below cend are the segment's own
+  int cbeg = pseg * L, cend = min(cbeg + L, nch), crs;
+  const float* ginit = nullptr;   // end gradient (null: zero)
+  if (p.trans) {
+    if (certified || pseg == 0) return;
+    crs = cend - 1;
+    if (pseg == nseg - 1) ginit = p.dht ? p.dht + hbase : nullptr;
+  } else if (certified) {
+    crs = min(cend + p.warmup, nch) - 1;
+    if (crs == nch - 1) ginit = p.dht ? p.dht + hbase : nullptr;
+  } else if (p.dhstart) {
+    crs = cend - 1;
+    if (pseg == nseg - 1) ginit = p.dht ? p.dht + hbase : nullptr;
+    else ginit = p.dhstart + ((long)h * p.total_segs + gseg) * KD * VD;
+  } else {
+    if (pseg != 0) return;             // segment 0 runs the whole head serially
+    cbeg = 0; cend = nch; crs = nch - 1;
+    ginit = p.dht ? p.dht + hbase : nullptr;
+  }
+  auto krow = [&](int rb, int e) { return 32 * (rb >> 1) + 8 * q + 4 * (rb & 1) + e; };
+  f32x4 ds[NKB];
+#pragma unroll
+  for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ds[rb][e] = (owner && ginit) ? ginit[(long)krow(rb, e) * VD + col] : 0.f;
+
+  // Copies of chunk jc's tiles into buffer bc in four parts (0 W, 1 dO, 2 K,
+  // 3 Q and the gate cumsums); rows past the chunk read as zero.
+  constexpr int NCP = (NCH + FNW - 1) / FNW;
+  uint32_t off_w[NCP], off_qk[NCP], off_o[NCP];
+#pragma unroll
+  for (int j = 0; j < NCP; ++j) {
+    const int i = w + FNW * j;
+    const int pidx = 64 * i + l;
+    const int r = pidx / NCH, c = (pidx % NCH) ^ stage_swz<NCH>(r);
+    off_w[j] = (uint32_t)(r * KD * (int)sizeof(T) + c * 16);
+    off_qk[j] = (uint32_t)(r * p.Hq * KD * (int)sizeof(T) + c * 16);
+    off_o[j] = (uint32_t)(r * p.Hv * VD * (int)sizeof(T) + c * 16);
+  }
+  auto copy_part = [&](int jc, auto bc, int piece) __attribute__((always_inline)) {
+    const DFusedBufs<T> bf = bufs(bc);
+    const int t0 = seq0 + jc * CH;
+    const int len = min(CH, seq1 - t0);
+    const long rbytes = (long)len * KD * (long)sizeof(T);
+    if (piece == 0)
+      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, rbytes), off_w, w);
+    if (piece == 1)
+      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.O, make_rsrc((const T*)p.d_o + ((long)t0 * p.Hv + h) * VD, rbytes * p.Hv), off_o, w);
+    if (piece == 2)
+      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, rbytes * p.Hq), off_qk, w);
+    if (piece == 3) {
+      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.Q, make_rsrc((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, rbytes * p.Hq), off_qk, w);
+      if (w == 0) {
+        const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
+        lds_copy4(rsrc_words(gr), (uint32_t)l * 4u, lds_addr(bf.G));
+      }
+    }
+  };
+  auto copy_chunk = [&](int jc, auto bc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int piece = 0; piece < 4; ++piece) copy_part(jc, bc, piece);
+  };
+  // Waits for this wave's copies; wave 0 derives chunk jn's per-row factors;
+  // the barrier publishes everything.
+  auto wait_copies = [&](int jn, auto bc) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (w == 0 && jn >= cbeg) {
+      const DFusedBufs<T> bf = bufs(bc);
+      const int tn = seq0 + jn * CH;
+      const int ln = min(CH, seq1 - tn);
+      const float gl = bf.G[max(ln, 1) - 1], gv = bf.G[l];
+      bf.D[l] = (l < ln) ? __expf(gl - gv) : 0.f;
+      bf.D[CH + l] = p.scale * __expf(gv);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  auto trd = [](const T* a) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
+  };
+
+  if (crs >= cbeg) copy_chunk(crs, ic<0>());
+  wait_copies(crs, ic<0>());
+
+  auto step = [&](auto bc, int jc) __attribute__((always_inline)) -> bool {
+    constexpr int b = decltype(bc)::value;
+    const int t0 = seq0 + jc * CH;
+    const int len = min(CH, seq1 - t0);
+    if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) return false;
+    const bool keep = !p.trans && jc < cend;   // a chunk of the segment itself
+    const bool more = jc - 1 >= cbeg;
+    const DFusedBufs<T> cur = bufs(bc);
+    if (more) {
+      copy_part(jc - 1, ic<1 - b>(), 0);
+      copy_part(jc - 1, ic<1 - b>(), 1);
+    }
+    const T* sW = cur.W;
+    const T* sQ = cur.Q;
+    const T* sK = cur.K;
+    const T* sO = cur.O;
+    const float* sG = cur.G;
+    const float* sD = cur.D;
+    const float* sM = cur.D + CH;
+    const float glast = sG[len - 1];
+    if (keep && owner) {   // gradient of the state leaving the chunk, [K][V] rows
+      T* db = (T*)p.dhbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD + col;
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) db[(long)krow(rb, e) * VD] = from_f<T>(ds[rb][e]);
+    }
+    {  // P tiles (the ten lower ones and the masked (0,1), (2,3)), stored transposed
+      constexpr int TI[12] = {3, 3, 2, 2, 3, 3, 2, 1, 1, 0, 0, 2};
+      constexpr int TJ[12] = {0, 1, 0, 1, 2, 3, 2, 0, 1, 0, 1, 3};
+      const int cnt = w < 4 ? 2 : 1;
+      int ti[2], tj[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int idx = w < 4 ? 2 * w + m : 8 + (w - 4);
+        ti[m] = TI[idx];
+        tj[m] = TJ[idx];
+      }
+      f32x4 pa[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int k0 = 0; k0 < KD; k0 += 32) {
+        bf16x8 fa[2], fb[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          fa[m] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * ti[m] + t, k0 + 8 * q));
+          fb[m] = *reinterpret_cast<const bf16x8*>(sK + tix(16 * tj[m] + t, k0 + 8 * q));
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[m], pa[m], 0, 0, 0);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m < cnt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ti[m] + acc_row(e), c = 16 * tj[m] + acc_col();
+            const float v = (r >= c && r < len) ? p.scale * __expf(sG[r] - sG[c]) * pa[m][e] : 0.f;
+            const int pr = (r & ~31) + 8 * ((r >> 2) & 3) + 4 * ((r >> 4) & 1) + (r & 3);
+            sP[c * PP + pr] = from_f<T>(v);
+          }
+        }
+      }
+    }
+    if (more) {
+      copy_part(jc - 1, ic<1 - b>(), 2);
+      copy_part(jc - 1, ic<1 - b>(), 3);
+    }
+    f32x4 kd[4];
+    bf16x8 bo[2];   // dO[32ks + {4q .. 4q+3, 16+4q .. 16+4q+3}][col]
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) kd[tt] = zero4();
+    if (owner) {
+#pragma unroll
+      for (int ks = 0; ks < KD / 32; ++ks) {   // kd = K dh
+        bf16x8 ak[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) ak[tt] = *reinterpret_cast<const bf16x8*>(sK + tix(16 * tt + t, 32 * ks + 8 * q));
+        const bf16x8 hb = pack_b(ds[2 * ks], ds[2 * ks + 1]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) kd[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[tt], hb, kd[tt], 0, 0, 0);
+      }
+      const float gn = __expf(glast);
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb) ds[rb] *= gn;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {   // dh += s (Gamma Q)^T dO
+        const int ra = 32 * ks + 4 * q + (sl >> 2);
+        bo[ks] = cat4(trd(sO + tix(ra, 16 * w + 4 * (sl & 3))), trd(sO + tix(ra + 16, 16 * w + 4 * (sl & 3))));
+        const f32x4 mlo = *reinterpret_cast<const f32x4*>(sM + 32 * ks + 4 * q);
+        const f32x4 mhi = *reinterpret_cast<const f32x4*>(sM + 32 * ks + 16 + 4 * q);
+        bf16x8 by;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16 xl = bo[ks][i], xh = bo[ks][4 + i];
+          by[i] = from_f<T>(to_f(xl) * mlo[i]);
+          by[4 + i] = from_f<T>(to_f(xh) * mhi[i]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < NKB; ++rb) {
+          const int cc = 32 * (rb >> 1) + 8 * (sl & 3) + 4 * (rb & 1);
+          const bf16x8 aq = cat4(trd(sQ + tix(ra, cc)), trd(sQ + tix(ra + 16, cc)));
+          ds[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, by, ds[rb], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();   // P^T complete
+    if (owner) {
+      f32x4 dv[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) dv[tt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)   // s P^T dO: row tile tt needs tokens >= 16 tt
+#pragma unroll
+        for (int tt = 0; tt <= 2 * ks + 1; ++tt) {
+          const bf16x8 ap = *reinterpret_cast<const bf16x8*>(sP + (16 * tt + t) * PP + 32 * ks + 8 * q);
+          dv[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bo[ks], dv[tt], 0, 0, 0);
+        }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dv[tt][e] += sD[16 * tt + acc_row(e)] * kd[tt][e];
+      if (keep) {   // dVn token rows
+        T* vb = (T*)p.dvn + ((long)h * s.Ttot + t0) * VD + col;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tt + acc_row(e);
+            if (r < len) vb[(long)r * VD] = from_f<T>(dv[tt][e]);
+          }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {   // dh -= W^T dVn
+        const int ra = 32 * ks + 4 * q + (sl >> 2);
+        const bf16x8 bv = pack_b(-dv[2 * ks], -dv[2 * ks + 1]);
+#pragma unroll
+        for (int rb = 0; rb < NKB; ++rb) {
+          const int cc = 32 * (rb >> 1) + 8 * (sl & 3) + 4 * (rb & 1);
+          const bf16x8 aw = cat4(trd(sW + tix(ra, cc)), trd(sW + tix(ra + 16, cc)));
+          ds[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bv, ds[rb], 0, 0, 0);
+        }
+      }
+    }
+    wait_copies(jc - 1, ic<1 - b>());   // the next chunk's tiles have landed; P^T is free again
+    return true;
+  };
+  for (int jc = crs; jc >= cbeg; jc -= 2) {
+    if (!step(ic<0>(), jc) || jc - 1 < cbeg || !step(ic<1>(), jc - 1)) break;
+  }
+
+  if (owner) {
+    float* dst = nullptr;
+    if (p.trans) dst = p.segtr + (((long)h * p.total_segs + gseg) * 2 + 1) * KD * VD;
+    else if (cbeg == 0 && p.dh0) dst = p.dh0 + hbase;
+    if (dst) {
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(long)krow(rb, e) * VD + col] = ds[rb][e];
+    }
+  }
+}
+
 // --------------------------------------------------------------- k_grads --
 // LDS: permanent K rows, K^T and Q^T; three 64-row regions R1..R3 and four
 // 64x64 tiles S0..S3 whose contents change phase by phase (see comments).
@@ -643,6 +966,24 @@ hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, int to
     if (KD == 32 && BV == 32) return dstate_impl<float, 32, 32>(p, total, st);
     if (KD == 64 && BV == 32) return dstate_impl<float, 64, 32>(p, total, st);
   }
+  return hipErrorInvalidValue;
+}
+
+template <int KD>
+static hipError_t dfused_impl(const DFusedParams& p, int total_segs, hipStream_t st) {
+  const int total = total_segs * p.Hv;
+  timing_before(p.trans ? "cp_rev_transition" : "chunk_dfused", st);
+  hipLaunchKernelGGL((k_dfused<KD>), dim3(padded_grid_b(total)), dim3(FNT), 0, st, p, total);
+  hipError_t err = hipGetLastError();
+  timing_after(st);
+  return err;
+}
+
+hipError_t launch_dfused(DType dt, int KD, const DFusedParams& p, int total_segs, hipStream_t st) {
+  if (dt != DType::BF16) return hipErrorInvalidValue;
+  if (KD == 32) return dfused_impl<32>(p, total_segs, st);
+  if (KD == 64) return dfused_impl<64>(p, total_segs, st);
+  if (KD == 128) return dfused_impl<128>(p, total_segs, st);
   return hipErrorInvalidValue;
 }
 

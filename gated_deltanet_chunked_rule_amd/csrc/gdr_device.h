@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gdr {
 
 typedef __bf16 bf16;
@@ -449,6 +451,86 @@ __device__ __forceinline__ int find_seq(const int32_t* off, int N, int c) {
     if (off[mid] <= c) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// ---- staged chunk tiles (the fused state kernels) ----
+// Staged tiles are unpadded: row r holds NCH 16-byte pieces, piece c stored
+// at position c ^ stage_swz(r), which keeps 8-byte fragment reads and the
+// transposing reads free of bank conflicts.
+template <int NCH>
+__device__ __forceinline__ int stage_swz(int r) {
+  if constexpr (NCH == 16) return 2 * (r & 7) + ((r >> 3) & 1);
+  else if constexpr (NCH == 8) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  else return (r >> 2) & (NCH - 1);
+}
+
+// Global -> LDS copy of 16 (or 4) bytes per lane: BUFFER_LOAD with the LDS
+// bit, lane l's bytes landing at lds + 16 l (4 l).  Issued through inline
+// assembly on purpose: the compiler's wait-count pass treats every later LDS
+// access as possibly aliasing a copy in flight and would wait for all
+// copies before it, serialising the copies with the chunk's compute.  The
+// kernels that use these wait for the copies themselves (vmcnt(0)) before
+// the barrier that publishes the data; nothing else in them uses M0.
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4v rsrc_words(rsrc_t r) {   // wave-uniform, in SGPRs
+  i32x4v v;
+  __builtin_memcpy(&v, &r, 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+__device__ __forceinline__ void lds_copy16(i32x4v rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_copy4(i32x4v rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+
+// One wave's share of copying a staged tile from global memory into LDS:
+// instruction j fills the 1 KB block w + 8j of the tile; off[j] is this
+// lane's byte offset in the source (rows past the descriptor range read 0).
+template <int NCP, int NCH, int FNWV, int VEC, typename T>
+__device__ __forceinline__ void lds_copy_tile(T* dst, rsrc_t rr, const uint32_t* off, int w) {
+  const i32x4v rv = rsrc_words(rr);
+#pragma unroll
+  for (int j = 0; j < NCP; ++j) {
+    const int i = w + FNWV * j;
+    if (NCH % FNWV == 0 || i < NCH) lds_copy16(rv, off[j], lds_addr(dst + 64 * i * VEC));
+  }
+}
+
+template <int V> using ic = std::integral_constant<int, V>;
+
+constexpr int FNW = 8, FNT = 64 * FNW;   // waves / threads of the fused state kernels
+
+// CP certificate of one head, called by every thread of the workgroup; cert
+// points at the head's first chunk of the sequence.  Each warmup window must
+// carry a gate mass of at most log_eps (and keys inside the contraction
+// range, which the per-chunk value encodes as +inf otherwise): forward
+// windows are the W chunks before a segment start that does not reach back
+// to the sequence start; with rev, also the W chunks after each segment end
+// that do not reach the sequence end (the reverse pass of the backward starts
+// there from zero).
+__device__ __forceinline__ bool head_certified(const float* cert, int nseg, int nch, int L, int W,
+                                               float log_eps, bool rev) {
+  int ok = 1;
+  for (int qq = 1 + (int)threadIdx.x; qq < nseg; qq += (int)blockDim.x) {
+    const int ws = qq * L - W;
+    if (ws > 0) {
+      float sum = 0.f;
+      for (int cc = ws; cc < qq * L; ++cc) sum += cert[cc];
+      if (!(sum <= log_eps)) ok = 0;
+    }
+    if (rev && qq * L + W < nch) {
+      float sum = 0.f;
+      for (int cc = qq * L; cc < qq * L + W; ++cc) sum += cert[cc];
+      if (!(sum <= log_eps)) ok = 0;
+    }
+  }
+  return !__syncthreads_or(!ok);
 }
 
 // Inclusive prefix sum across a wave64 (lane i gets x_0 + ... + x_i).

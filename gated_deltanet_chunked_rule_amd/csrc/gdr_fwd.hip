@@ -491,16 +491,7 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
 
   // A head is certified when every warmup window's gate mass is small enough
   // (all segments of the head evaluate the same test, so they agree).
-  int ok = 1;
-  for (int q = 1 + (int)threadIdx.x; q < nseg; q += NTHR) {
-    const int ws = q * L - p.warmup;
-    if (ws > 0) {
-      float sum = 0.f;
-      for (int cc = ws; cc < q * L; ++cc) sum += p.cert[(long)h * s.NTtot + c0 + cc];
-      if (!(sum <= p.log_eps)) ok = 0;
-    }
-  }
-  const bool certified = !__syncthreads_or(!ok);
+  const bool certified = head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, false);
   int cstart, cbeg, cend;
   bool write_final;
   if (!certified) {
@@ -655,61 +646,13 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
 // them are single 16-byte LDS reads.  P is stored with its token columns
 // permuted the same way (32-token block, group g, half hh: column
 // 32ks + 16hh + 4g + e at position 32ks + 8g + 4hh + e) for P Vnew.
-template <int NCH>
-__device__ __forceinline__ int stage_swz(int r) {
-  if constexpr (NCH == 16) return 2 * (r & 7) + ((r >> 3) & 1);
-  else if constexpr (NCH == 8) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-  else return (r >> 2) & (NCH - 1);
-}
-
-// Global -> LDS copy of 16 (or 4) bytes per lane: BUFFER_LOAD with the LDS
-// bit, lane l's bytes landing at lds + 16 l (4 l).  Issued through inline
-// assembly on purpose: the compiler's wait-count pass treats every later LDS
-// access as possibly aliasing a copy in flight and would wait for all
-// copies before it, serialising the copies with the chunk's compute.  The
-// kernels that use these wait for the copies themselves (vmcnt(0)) before
-// the barrier that publishes the data; nothing else in them uses M0.
-typedef int i32x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4v rsrc_words(rsrc_t r) {   // wave-uniform, in SGPRs
-  i32x4v v;
-  __builtin_memcpy(&v, &r, 16);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
-  return v;
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
-}
-__device__ __forceinline__ void lds_copy16(i32x4v rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
-}
-__device__ __forceinline__ void lds_copy4(i32x4v rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
-}
-
-// One wave's share of copying a staged tile from global memory into LDS:
-// instruction j fills the 1 KB block w + 8j of the tile; off[j] is this
-// lane's byte offset in the source (rows past the descriptor range read 0).
-template <int NCP, int NCH, int FNWV, int VEC, typename T>
-__device__ __forceinline__ void lds_copy_tile(T* dst, rsrc_t rr, const uint32_t* off, int w) {
-  const i32x4v rv = rsrc_words(rr);
-#pragma unroll
-  for (int j = 0; j < NCP; ++j) {
-    const int i = w + FNWV * j;
-    if (NCH % FNWV == 0 || i < NCH) lds_copy16(rv, off[j], lds_addr(dst + 64 * i * VEC));
-  }
-}
-
 template <typename T>
 struct FusedBufs {   // one buffer of staged chunk inputs
   T *W, *Q, *K, *U;
   float *G, *D;      // gate cumsums; per-row factors {e^{gamma_n - gamma_t}, s e^{gamma_t}}
 };
-template <int V> using ic = std::integral_constant<int, V>;
 
-constexpr int FNW = 8, FNT = 64 * FNW;   // waves / threads of k_fused
-
-template <typename T, int KD>
+template <typename T, int KD, bool ST>
 __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
@@ -758,16 +701,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   const bool owner = w < NWV;
   auto vcol = [&](int cb) { return CBW == 2 ? 32 * w + 2 * t + cb : 16 * w + t; };
 
-  int ok = 1;
-  for (int qq = 1 + (int)threadIdx.x; qq < nseg; qq += FNT) {
-    const int ws = qq * L - p.warmup;
-    if (ws > 0) {
-      float sum = 0.f;
-      for (int cc = ws; cc < qq * L; ++cc) sum += p.cert[(long)h * s.NTtot + c0 + cc];
-      if (!(sum <= p.log_eps)) ok = 0;
-    }
-  }
-  const bool certified = !__syncthreads_or(!ok);
+  const bool certified =
+      head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0);
   const int gseg = s.seg_off[n] + pseg;          // global segment index
   const bool exact = !certified && p.hstart != nullptr;
   int cstart, cbeg, cend;
@@ -791,6 +726,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     cstart = 0; cbeg = 0; cend = nch; write_final = true;
   }
   const bool no_u = p.trans && part == 0;         // M: the segment's map with U = 0
+  const bool st_mode = ST && !p.trans;   // backward recompute: states, no output
 
   const long hbase = ((long)n * p.Hv + h) * KD * VD;
   auto krow = [&](int rb, int e) { return 32 * (rb >> 1) + 8 * q + 4 * (rb & 1) + e; };
@@ -847,7 +783,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     if (piece == 2)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
     if (piece == 3) {
-      if (jc >= cbeg && !p.trans)
+      if (jc >= cbeg && !p.trans && !st_mode)
         lds_copy_tile<NCP, NCH, FNW, VEC>(bf.Q, make_rsrc((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
       if (w == 0) {
         const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
@@ -902,7 +838,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const int t0 = seq0 + jc * CH;
     const int len = min(CH, seq1 - t0);
     if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) return false;
-    const bool warm = jc < cbeg || p.trans;   // no output for this chunk
+    const bool warm = jc < cbeg || p.trans || st_mode;   // no output for this chunk
+    const bool keep = st_mode && jc >= cbeg;             // store the entry state and Vnew
     const bool more = jc + 1 < cend;
     const FusedBufs<T> cur = bufs(bc);
     if (more) {
@@ -917,6 +854,13 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const float* sD = cur.D;
     const float* sM = cur.D + CH;
     const float glast = sG[len - 1];
+    if (keep && owner) {   // entry state of the chunk, [K][V] rows
+      T* hb = (T*)p.hbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD + vcol(0);
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hb[(long)(F32 ? 16 * rb + acc_row(e) : krow(rb, e)) * VD] = from_f<T>(hs[rb][0][e]);
+    }
 
     if (!warm) {  // P tiles: rows of tile ti, columns of tile tj
       // The ten lower tiles and the upper tiles (0,1), (2,3) that the
@@ -1051,6 +995,16 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
             oa[tt][cb][e] *= gm;
           }
         }
+      if (keep) {   // Vnew token rows
+        T* vb = (T*)p.vnew + ((long)h * s.Ttot + t0) * VD + vcol(0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tt + acc_row(e);
+            if (r < len) vb[(long)r * VD] = from_f<T>(vn[tt][0][e]);
+          }
+      }
       // h' = Gamma_n h + K^T (d * Vnew).
       const float gn = __expf(glast);
 #pragma unroll
@@ -1182,7 +1136,10 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 // -------------------------------------------------------------- k_segscan --
 // Exact start states of the CP segments of heads that fail the warmup
 // certificate: h_1 = b_0 (the first segment's end state from the initial
-// state), h_{s+1} = M_s h_s + b_s.  State columns are independent, so one
+// state), h_{s+1} = M_s h_s + b_s.  Reverse mode (backward): the state
+// gradient entering segment s from its end is g_s = M_{s+1}^T g_{s+1} + d_{s+1},
+// g_{nseg-2} = d_{nseg-1} (the last segment run from the final-state gradient),
+// where d_s is the reverse pass over segment s from a zero gradient.  State columns are independent, so one
 // workgroup per (sequence, value head, 16-column block) with KD/16 waves;
 // wave w produces rows 16w..16w+15.  The A operand (rows of M_s) comes
 // straight from memory into registers, one step ahead; the state slice
@@ -1201,35 +1158,39 @@ __global__ __launch_bounds__(KD * 4) void k_segscan(ScanParams p, int total_item
   const int c0 = s.chunk_off[n];
   const int L = p.seg_chunks;
   if (nseg <= 1 || c0 < 0) return;
-  int ok = 1;
-  for (int qq = 1 + (int)threadIdx.x; qq < nseg; qq += KD * 4) {
-    const int ws = qq * L - p.warmup;
-    if (ws > 0) {
-      float sum = 0.f;
-      for (int cc = ws; cc < qq * L; ++cc) sum += p.cert[(long)h * s.NTtot + c0 + cc];
-      if (!(sum <= p.log_eps)) ok = 0;
-    }
-  }
-  if (!__syncthreads_or(!ok)) return;   // certified: the warmup path needs no start states
+  const int nch = s.chunk_off[n + 1] - c0;
+  if (head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0))
+    return;   // certified: the warmup path needs no start states
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
   const int col = 16 * cb + t, row0 = 16 * w + 4 * q;
   const long head = (long)h * p.total_segs + s.seg_off[n];
   auto tr = [&](int sg, int part) { return p.segtr + ((head + sg) * 2 + part) * KD * VD; };
   auto load_m = [&](int sg, f32x4 (&a)[NKB]) {
-    const float* M = tr(sg, 0) + (long)(16 * w + t) * KD + 4 * q;
+    if (p.rev) {   // M^T: lane reads column 16w + t of M, rows 16rb + 4q .. +3
+      const float* M = tr(sg, 0) + (long)(4 * q) * KD + 16 * w + t;
 #pragma unroll
-    for (int rb = 0; rb < NKB; ++rb) a[rb] = *reinterpret_cast<const f32x4*>(M + 16 * rb);
+      for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[rb][e] = M[(long)(16 * rb + e) * KD];
+    } else {
+      const float* M = tr(sg, 0) + (long)(16 * w + t) * KD + 4 * q;
+#pragma unroll
+      for (int rb = 0; rb < NKB; ++rb) a[rb] = *reinterpret_cast<const f32x4*>(M + 16 * rb);
+    }
   };
   auto load_b = [&](int sg, f32x4& b) {
     const float* B = tr(sg, 1) + (long)row0 * VD + col;
 #pragma unroll
     for (int e = 0; e < 4; ++e) b[e] = B[(long)e * VD];
   };
+  // Step i stores slot sx(i) and then applies transition sx(i): forward
+  // slots 1 .. nseg-1 from b_0; reverse slots nseg-2 .. 0 from d_{nseg-1}.
+  auto sx = [&](int i) { return p.rev ? nseg - 1 - i : i; };
   f32x4 hs, bn, a[NKB];
-  load_b(0, hs);
-  if (nseg > 2) { load_m(1, a); load_b(1, bn); }
+  load_b(p.rev ? nseg - 1 : 0, hs);
+  if (nseg > 2) { load_m(sx(1), a); load_b(sx(1), bn); }
   for (int sg = 1; sg < nseg; ++sg) {
-    float* dst = p.hstart + (head + sg) * KD * VD + (long)row0 * VD + col;
+    float* dst = p.hstart + (head + sx(sg)) * KD * VD + (long)row0 * VD + col;
 #pragma unroll
     for (int e = 0; e < 4; ++e) dst[(long)e * VD] = hs[e];
     if (sg == nseg - 1) break;
@@ -1238,7 +1199,7 @@ __global__ __launch_bounds__(KD * 4) void k_segscan(ScanParams p, int total_item
     __syncthreads();
     f32x4 an[NKB], bnn = bn;
     const bool more = sg + 1 < nseg - 1;
-    if (more) { load_m(sg + 1, an); load_b(sg + 1, bnn); }
+    if (more) { load_m(sx(sg + 1), an); load_b(sx(sg + 1), bnn); }
     f32x4 acc0 = bn, acc1 = zero4();
 #pragma unroll
     for (int rb = 0; rb < NKB; rb += 2) {
@@ -1297,8 +1258,10 @@ static hipError_t state_impl(const StateParams& p, int total_segs, bool rows, hi
 template <typename T, int KD>
 static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t st) {
   const int total = total_segs * p.Hv * (p.trans ? 2 : 1);
-  timing_before(p.trans ? "cp_transition" : "chunk_fused", st);
-  hipLaunchKernelGGL((k_fused<T, KD>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  const bool states = p.hbuf != nullptr && !p.trans;
+  timing_before(p.trans ? "cp_transition" : states ? "chunk_states" : "chunk_fused", st);
+  if (states) hipLaunchKernelGGL((k_fused<T, KD, true>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  else hipLaunchKernelGGL((k_fused<T, KD, false>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;

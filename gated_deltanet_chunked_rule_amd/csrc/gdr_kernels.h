@@ -10,8 +10,10 @@
 //   A     fp32 [Hv][Ttot][64]      rows of the chunk's A (backward only)
 //   dhbuf T    [Hv][NTtot][K][V]   gradient of the state leaving each chunk
 //   dvn   T    [Hv][Ttot][V]       gradient of Vnew (token rows)
-//   segtr fp32 [Hv][segs][2][K][V] per CP segment: M (start -> end state map) and b
-//   hstart fp32 [Hv][segs][K][V]   exact start state of each CP segment
+//   segtr fp32 [Hv][segs][2][K][V] per CP segment: M (start -> end state map) and b;
+//                                  the backward then reuses part 1 for the reverse offsets d
+//   hstart fp32 [Hv][segs][K][V]   exact start state of each CP segment; the backward then
+//                                  reuses it for the exact state gradients at segment ends
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -78,6 +80,25 @@ struct FusedParams {         // forward state recurrence fused with the output
   int trans;                 // 1: segment-transition pass (no output), 0: output pass
   float* segtr;              // transition pass: [Hv][total_segs][2][K][V] {M, b}
   const float* hstart;       // nullable: exact segment start states [Hv][total_segs][K][V]
+  int rev_cert;              // 1 (backward): a head certifies only if its reverse windows do too
+  void* hbuf;                // non-null (backward recompute): store each chunk's entry state
+  void* vnew;                //   and Vnew instead of the output
+};
+
+struct DFusedParams {        // reverse state pass with CP segments (backward)
+  SeqTables s;
+  const void *q, *k, *W, *d_o;
+  const float *gcum, *cert;
+  const float* dht;          // nullable [N][Hv][K][V]
+  float* dh0;                // nullable [N][Hv][K][V]
+  void* dhbuf;               // [Hv][NTtot][K][V] gradient of the state leaving each chunk
+  void* dvn;                 // [Hv][Ttot][V]
+  int Hq, Hv;
+  int seg_chunks, warmup, total_segs;
+  float log_eps, scale;
+  int trans;                 // 1: reverse segment offsets d_s into segtr part 1
+  float* segtr;
+  const float* dhstart;      // nullable: exact state gradients at the segment ends [Hv][total_segs][K][V]
 };
 
 struct ScanParams {          // exact segment start states from the segment transitions
@@ -86,6 +107,8 @@ struct ScanParams {          // exact segment start states from the segment tran
   float* hstart;
   int Hv, seg_chunks, warmup, total_segs;
   float log_eps;
+  int rev;                   // 1: reverse scan g_{s-1} = M_s^T g_s + d_s (state gradients)
+  int rev_cert;
 };
 
 struct DStateParams {        // reverse state pass
@@ -119,6 +142,7 @@ hipError_t launch_state(DType dt, int KD, int BV, const StateParams& p, int tota
 hipError_t launch_fused(DType dt, int KD, const FusedParams& p, int total_segs, hipStream_t st);
 hipError_t launch_segscan(int KD, const ScanParams& p, int total_items, hipStream_t st);
 hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, int total_items, hipStream_t st);
+hipError_t launch_dfused(DType dt, int KD, const DFusedParams& p, int total_segs, hipStream_t st);
 hipError_t launch_grads(DType dt, int KD, const GradParams& p, hipStream_t st);
 
 // Kernel timing hooks (gdr_timing.cpp).

@@ -90,8 +90,14 @@ typedef struct {
  * page describes for CP), so every segment's (M, b) is computed in parallel,
  * the start states follow from a short scan, and the segments then run from
  * them; with cp_serial_fallback = 1 such heads run serially instead.  Results
- * never depend on an uncertified warmup.  Pass NULL for the defaults; a
- * zero-initialised struct also gives the defaults. */
+ * never depend on an uncertified warmup.  The bf16 backward uses the same
+ * segments for both of its serial passes: the recomputed chunk states as
+ * above, and the reverse pass over the state gradient, whose segments start
+ * at their ends after up to cp_warmup_chunks chunks of warmup (the reverse
+ * map is the transposed M plus an offset); its certificate also covers the
+ * windows after every segment end.  The fp32 backward runs each head whole.
+ * Pass NULL for the defaults; a zero-initialised struct also gives the
+ * defaults. */
 typedef enum { GDR_CP_AUTO = 0, GDR_CP_OFF = 1, GDR_CP_FORCE = 2 } gdr_cp_mode;
 
 typedef struct {

@@ -15,11 +15,11 @@ pytestmark = pytest.mark.gpu
 NAMES = ["dq", "dk", "dv", "dbeta", "dg", "dh0"]
 
 
-def check_bwd(inp, qk_heads=None, label="", A=None):
+def check_bwd(inp, qk_heads=None, label="", A=None, options=None):
     w = inp["workload"]
     print(f"[bwd] {label or w.name} B={w.B} T={inp['q'].shape[1]} Hq={w.Hq} Hv={w.Hv} K={w.K} {w.dtype}",
           flush=True)
-    grads = gpu_bwd(inp, A=A)
+    grads = gpu_bwd(inp, A=A, options=options)
     torch.cuda.synchronize()
     ref = oracle_bwd(inp, qk_heads=qk_heads)
     tol = TOL[w.dtype]
@@ -117,3 +117,40 @@ def test_deterministic():
 def test_backward_workload_full_size_sampled_heads():
     inp = gi.make_inputs(gi.WORKLOADS["backward"])
     check_bwd(inp, qk_heads=(0, 1), label="backward heads 0-1")
+
+
+# CP segments in the backward (bf16): both serial passes (the recomputed
+# chunk states and the reverse pass over the state gradient) run per segment.
+
+@pytest.mark.parametrize("K", [64, 128])
+def test_cp_segments_mixed_heads(K):
+    # Half the heads decay fast enough for a 2-chunk warmup to certify, both
+    # before each segment start and after each segment end; the g = 0 heads
+    # take the exact path in both passes (transitions, scans, exact starts).
+    w = gi.custom(B=2, T=64 * 11 + 23, Hq=2, Hv=4, K=K, V=K, dtype="bf16", seed=90, initial_state=True,
+                  backward=True, gate=(0.5, 0.8), zero_gate_frac=0.5)
+    check_bwd(gi.make_inputs(w), options=gdr.Options(gdr.CP_FORCE, 3, 2), label=f"CP mixed heads K={K}")
+
+
+@pytest.mark.parametrize("seg", [1, 4])
+def test_cp_exact_segments_all_uncertified(seg):
+    w = gi.custom(B=1, T=64 * 9 + 5, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=91, initial_state=True,
+                  backward=True, zero_gate_frac=1.0)
+    check_bwd(gi.make_inputs(w), options=gdr.Options(gdr.CP_FORCE, seg, 2), label=f"CP exact L={seg}")
+
+
+def test_cp_serial_fallback_backward():
+    w = gi.custom(B=1, T=64 * 14 + 5, Hq=2, Hv=8, K=128, V=128, dtype="bf16", seed=92, initial_state=True,
+                  backward=True, gate=(0.9, 0.999), zero_gate_frac=0.5)
+    inp = gi.make_inputs(w)
+    g1 = check_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 4, 2, 0.0, 1), label="CP serial fallback")
+    g2 = check_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 4, 2, 0.0, 0), label="CP exact segments")
+    for a, b in zip(g1, g2):   # the same recurrence up to rounding order
+        assert rel_err(a, f64(b)) <= 2e-2
+
+
+def test_cp_backward_varlen():
+    w = gi.custom(B=1, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=93, initial_state=True, backward=True,
+                  gate=(0.5, 0.8), zero_gate_frac=0.5)
+    inp = gi.packed_from_lengths(w, [64 * 9 + 7, 1, 64 * 3, 0, 64 * 6 + 40])
+    check_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 2, 1), label="CP varlen")
