@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
-SOURCES = ["gdr_api.cpp", "gdr_timing.cpp", "gdr_fwd.hip", "gdr_bwd.hip"]
+SOURCES = ["gdr_api.cpp", "gdr_timing.cpp", "gdr_fwd.hip", "gdr_bwd.hip", "gdr_grads.hip"]
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 

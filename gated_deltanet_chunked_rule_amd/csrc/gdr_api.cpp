@@ -227,7 +227,7 @@ gdr_status hip_fail(hipError_t e, const char* what) {
 gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const void* q,
                              const void* k, const void* v, const float* g, const float* beta,
                              float scale, const float* h0, const int32_t* cu_dev, void* o,
-                             float* ht, float* g_cum_out, float* A_out, float* A_ws,
+                             float* ht, float* g_cum_out, float* A_out, float* A_ws, void* A_bf,
                              const float* A_in, int L, bool bwd, hipStream_t st) {
   hipError_t e;
   gdr::PlanParams pp;
@@ -247,7 +247,7 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     ip.g_cum_out = g_cum_out;
     ip.cert = reinterpret_cast<float*>(ws + Lo.cert);
     ip.W = ws + Lo.W; ip.U = ws + Lo.U;
-    ip.A_ws = A_ws; ip.A_out = A_out; ip.A_in = A_in;
+    ip.A_ws = A_ws; ip.A_bf = A_bf; ip.A_out = A_out; ip.A_in = A_in;
     if ((e = gdr::launch_intra(P.dt, P.K, ip, st)) != hipSuccess) return hip_fail(e, "intra launch");
   }
   int segs = 0;
@@ -358,7 +358,7 @@ gdr_status gdr_chunk_fwd(const gdr_shape* shape, const gdr_options* opts, const 
     return fail(GDR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(Lo.total) + " bytes");
   char* ws = static_cast<char*>(workspace);
   return run_forward_chain(P, Lo, ws, q, k, v, g, beta, scale, initial_state, cu_seqlens, o,
-                           final_state, g_cum_out, A_out, nullptr, nullptr, P.L, false,
+                           final_state, g_cum_out, A_out, nullptr, nullptr, nullptr, P.L, false,
                            static_cast<hipStream_t>(stream));
 }
 
@@ -393,8 +393,12 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
   // (exact end gradients from the reverse offsets, the transposed segment
   // transitions and a reverse scan).  fp32 runs each head whole.
   const int L = bwd_segmented(P) ? P.L : std::max(P.NTmax, 1);
+  // The K = 128 bf16 gradient kernel reads A as bf16; the others as fp32.
+  const bool grads_f = P.dt == gdr::DType::BF16 && P.K == 128;
+  float* A_ws = grads_f ? nullptr : reinterpret_cast<float*>(ws + Lo.A);
+  void* A_bf = grads_f ? static_cast<void*>(ws + Lo.A) : nullptr;
   st = run_forward_chain(P, Lo, ws, q, k, v, g, beta, scale, initial_state, cu_seqlens, nullptr,
-                         nullptr, nullptr, nullptr, reinterpret_cast<float*>(ws + Lo.A), A, L, true, hs);
+                         nullptr, nullptr, nullptr, A_ws, A_bf, A, L, true, hs);
   if (st != GDR_OK) return st;
   if (P.NTtot == 0 && !dh0) return GDR_OK;
   const gdr::SeqTables s = tables(P, Lo, ws);
@@ -440,10 +444,11 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
     gp.s = s; gp.q = q; gp.k = k; gp.v = v; gp.d_o = d_o; gp.hbuf = ws + Lo.hbuf;
     gp.vnew = ws + Lo.vnew; gp.dhbuf = ws + Lo.dhbuf; gp.dvn = ws + Lo.dvn;
     gp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
-    gp.beta = beta; gp.A_ws = reinterpret_cast<const float*>(ws + Lo.A);
+    gp.beta = beta; gp.A_ws = A_ws; gp.A_bf = A_bf;
     gp.dq = dq; gp.dk = dk; gp.dv = dv; gp.dbeta = dbeta; gp.dg = dg;
     gp.Hq = P.Hq; gp.Hv = P.Hv; gp.scale = scale;
-    if ((e = gdr::launch_grads(P.dt, P.K, gp, hs)) != hipSuccess) return hip_fail(e, "grads launch");
+    e = grads_f ? gdr::launch_gradsf(gp, hs) : gdr::launch_grads(P.dt, P.K, gp, hs);
+    if (e != hipSuccess) return hip_fail(e, "grads launch");
   }
   return GDR_OK;
 }

@@ -31,35 +31,6 @@
 
 namespace gdr {
 
-__device__ __forceinline__ bool locate_chunk_b(const SeqTables& s, int c, int& n, int& t0, int& len) {
-  if (c >= s.NTtot) return false;
-  n = find_seq(s.chunk_off, s.N, c);
-  t0 = s.cu[n] + (c - s.chunk_off[n]) * CH;
-  len = min(CH, s.cu[n + 1] - t0);
-  return len > 0 && t0 >= 0 && (long)t0 + len <= s.Ttot;
-}
-
-// Sum over the 16 lanes that share a row of an accumulator tile (lanes with
-// equal lane/16); every lane of the group receives the sum.
-__device__ __forceinline__ float row_group_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
-// Sum over the four lane groups that share a column (lane % 16).
-__device__ __forceinline__ float col_group_sum(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
 // -------------------------------------------------------------- k_dstate --
 template <typename T, int KD, int BV>
 __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items) {

@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
         a3 = dg;
       }
     }
-    if (p.A_ws || p.A_out) {
+    if (p.A_ws || p.A_out || p.A_bf) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + acc_row(e);
@@ -375,6 +375,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (p.A_ws) p.A_ws[((long)h * s.Ttot + t0 + r) * CH + 16 * j + t] = v4[j];
+            if (p.A_bf) ((bf16*)p.A_bf)[((long)h * s.Ttot + t0 + r) * CH + 16 * j + t] = from_f<bf16>(v4[j]);
             if (p.A_out) p.A_out[((long)(t0 + r) * p.Hv + h) * CH + 16 * j + t] = v4[j];
           }
         }

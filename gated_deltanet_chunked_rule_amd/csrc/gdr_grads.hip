@@ -1,0 +1,512 @@
+// gdr_grads.hip -- per-chunk gradients of the chunked gated delta rule for
+// K = V = 128 in bf16 on gfx950 (the other shapes use k_grads).
+//
+// Given the recomputed chunk states h, the state gradients dh leaving each
+// chunk, Vnew and dVnew (the two serial passes of the backward), every
+// (chunk, value head) is independent.  Its products, with P-like masks
+// D_ts = e^{gamma_t - gamma_s} for t >= s and s the scale:
+//   dPD = s D * lower(dO Vnew^T)
+//   dQ  = dPD K + s diag(Gamma) dO h^T
+//   dW  = -dVnew h^T,  dA = strict_lower(dW (b Gamma K)^T + dVnew (b V)^T)
+//   dKb = A^T dW,  dVb = A^T dVnew,  dL = strict_lower(-A^T dA A^T)
+//   dK  = dPD^T Q + (E + E^T) K + diag(b Gamma) dKb + diag(dec) Vnew dh^T,
+//         E = dL * diag(b) D,  dec_t = e^{gamma_n - gamma_t}
+//   dV  = diag(b) dVb,  and dbeta, dgamma from row and column sums of the
+//   same terms; dg is the reverse cumulative sum of dgamma over the chunk
+// (the backward listing the FlashQLA pages describe: FlashQLA curated
+// summary, section "使用方式與需求").
+//
+// Design: a persistent grid (one 8-wave workgroup per CU) walks a contiguous
+// range of (chunk, query/key head) items; each item loops over its group's
+// value heads ("units") so that dq and dk are summed in registers.  Wave w
+// owns feature columns 16w..16w+15 of every 64 x 128 product (h and dh rows
+// 16w..16w+15 are its MFMA B operands, read once from memory straight into
+// registers); 64 x 64 products are split two tiles per wave.  The token-row
+// tiles (dO, Vnew, dVnew, V, Q, K) and A are copied into LDS with
+// buffer-to-LDS loads; the next unit's copies are issued as soon as the
+// current unit is done with each region, so the copies of one unit overlap
+// the compute of the previous one.  Transposed operands come from
+// transposing LDS reads; no transposed copy is stored.  Row and column sums
+// go through per-wave partial arrays added in a fixed order (deterministic).
+#include <math.h>
+
+#include "gdr_device.h"
+#include "gdr_kernels.h"
+
+namespace gdr {
+
+template <int KD>
+__global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, int per_wg) {
+  using T = bf16;
+  constexpr int VD = KD;
+  constexpr int TE = CH * KD, TE8 = CH * CH;
+  static_assert(KD == 128, "one 16-column block per wave");
+  __shared__ __align__(16) T sQ[TE], sK[TE], sdO[TE], sVn[TE], sdVn[TE], sV[TE], sW[TE];
+  __shared__ __align__(16) T sA2[2][TE8], sPD[TE8];
+  __shared__ __align__(16) float sGc[2][CH], sBe[2][CH];
+  __shared__ float sGam[CH], sGm[CH], sDec[CH], sBt[CH];
+  __shared__ float sRowP[FNW][CH], sColP[FNW][CH], sDbP[FNW][CH], sRed[2][FNW];
+  if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
+    const T z = from_f<T>(0.f);
+    sQ[threadIdx.x] = z; sK[threadIdx.x] = z; sdO[threadIdx.x] = z; sVn[threadIdx.x] = z;
+    sdVn[threadIdx.x] = z; sV[threadIdx.x] = z; sA2[0][threadIdx.x] = z; sA2[1][threadIdx.x] = z;
+    sGc[threadIdx.x >> 8][threadIdx.x & 63] = 0.f;
+    sBe[threadIdx.x >> 8][threadIdx.x & 63] = 0.f;
+  }
+  const SeqTables& s = p.s;
+  const int G = p.Hv / p.Hq;
+  const int i0 = (int)blockIdx.x * per_wg;
+  const int i1 = min(total_items, i0 + per_wg);
+  if (i0 >= i1) return;
+  const int nunits = (i1 - i0) * G;
+  const int w = wave_id(), l = lane_id();
+  // Lane coordinates; re-materialised opaquely at every unit so that the
+  // compiler does not hoist hundreds of loop-invariant LDS addresses out of
+  // the unit loop (and spill them).
+  int q = l >> 4, t = l & 15;
+  int dcol = 16 * w + t;                       // this wave's feature column
+  const int ti = w >> 1, tj0 = 2 * (w & 1);    // this wave's 64 x 64 tiles (ti, tj0), (ti, tj0 + 1)
+
+  // staged-tile element offsets: 128-wide (16 pieces a row) and 64-wide (8)
+  auto t16 = [](int r, int c) __attribute__((always_inline)) { return (r * 16 + ((c >> 3) ^ stage_swz<16>(r))) * 8 + (c & 7); };
+  auto t8 = [](int r, int c) __attribute__((always_inline)) { return (r * 8 + ((c >> 3) ^ stage_swz<8>(r))) * 8 + (c & 7); };
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  auto trd = [](const T* a) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
+  };
+  // Fragments of V_MFMA_F32_16X16X32_BF16.  ra: row m of X, contraction
+  // 32ks + 8q + j.  rb: contraction 32ks + {4q, 16 + 4q} + i over the rows of
+  // X at column c0 + t (the row set of accumulator tiles 2ks, 2ks + 1).
+  // rt: contraction 32ks + 8q + j over the rows of X at column c0 + t.
+  auto ra16 = [&](const T* X, int m, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(X + t16(m, 32 * ks + 8 * q));
+  };
+  auto ra8 = [&](const T* X, int m, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(X + t8(m, 32 * ks + 8 * q));
+  };
+  auto rb16 = [&](const T* X, int ks, int c0) __attribute__((always_inline)) {
+    const int r = 32 * ks + 4 * q + (t >> 2), c = c0 + 4 * (t & 3);
+    return cat4(trd(X + t16(r, c)), trd(X + t16(r + 16, c)));
+  };
+  auto rb8 = [&](const T* X, int ks, int c0) __attribute__((always_inline)) {
+    const int r = 32 * ks + 4 * q + (t >> 2), c = c0 + 4 * (t & 3);
+    return cat4(trd(X + t8(r, c)), trd(X + t8(r + 16, c)));
+  };
+  auto rt16 = [&](const T* X, int ks, int c0) __attribute__((always_inline)) {
+    const int r = 32 * ks + 8 * q + (t >> 2), c = c0 + 4 * (t & 3);
+    return cat4(trd(X + t16(r, c)), trd(X + t16(r + 4, c)));
+  };
+  auto mf = [](bf16x8 a, bf16x8 b, f32x4 c) __attribute__((always_inline)) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  };
+
+  // per-lane byte offsets of the tile copies (rows past the chunk read as 0)
+  uint32_t off_qk[2], off_hv[2], off_ws[2], off_a[1];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int pidx = 64 * (w + FNW * j) + l;
+    const int r = pidx >> 4, c = (pidx & 15) ^ stage_swz<16>(r);
+    off_qk[j] = (uint32_t)(r * p.Hq * KD * 2 + c * 16);
+    off_hv[j] = (uint32_t)(r * p.Hv * VD * 2 + c * 16);
+    off_ws[j] = (uint32_t)(r * VD * 2 + c * 16);
+  }
+  {
+    const int pidx = 64 * w + l;
+    const int r = pidx >> 3, c = (pidx & 7) ^ stage_swz<8>(r);
+    off_a[0] = (uint32_t)(r * CH * 2 + c * 16);
+  }
+  struct Unit { int c, hk, h, gi, t0, len; };
+  auto unit = [&](int j, Unit& u) __attribute__((always_inline)) -> bool {
+    const int it = i0 + j / G;
+    u.gi = j % G;
+    u.c = it / p.Hq;
+    u.hk = it % p.Hq;
+    u.h = u.hk * G + u.gi;
+    int n;
+    return locate_chunk_b(s, u.c, n, u.t0, u.len);
+  };
+  auto tile = [&](T* dst, const void* base, long elem0, long row_elems, int len, const uint32_t* off)
+      __attribute__((always_inline)) {
+    lds_copy_tile<2, 16, FNW, 8>(dst, make_rsrc((const T*)base + elem0, (long)len * row_elems * 2), off, w);
+  };
+  auto copy_dO_Vn = [&](const Unit& u) __attribute__((always_inline)) {
+    tile(sdO, p.d_o, ((long)u.t0 * p.Hv + u.h) * VD, (long)p.Hv * VD, u.len, off_hv);
+    tile(sVn, p.vnew, ((long)u.h * s.Ttot + u.t0) * VD, VD, u.len, off_ws);
+  };
+  auto copy_Q = [&](const Unit& u) __attribute__((always_inline)) {
+    tile(sQ, p.q, ((long)u.t0 * p.Hq + u.hk) * KD, (long)p.Hq * KD, u.len, off_qk);
+  };
+  auto copy_K = [&](const Unit& u) __attribute__((always_inline)) {
+    tile(sK, p.k, ((long)u.t0 * p.Hq + u.hk) * KD, (long)p.Hq * KD, u.len, off_qk);
+  };
+  auto copy_rest = [&](const Unit& u, auto abc) __attribute__((always_inline)) {   // dVnew, V, A, gates
+    constexpr int ab = decltype(abc)::value;
+    tile(sdVn, p.dvn, ((long)u.h * s.Ttot + u.t0) * VD, VD, u.len, off_ws);
+    tile(sV, p.v, ((long)u.t0 * p.Hv + u.h) * VD, (long)p.Hv * VD, u.len, off_hv);
+    lds_copy_tile<1, 8, FNW, 8>(&sA2[ab][0],
+                                make_rsrc((const T*)p.A_bf + ((long)u.h * s.Ttot + u.t0) * CH, (long)u.len * CH * 2),
+                                off_a, w);
+    if (w == 0) {
+      const rsrc_t gr = make_rsrc(p.gcum + (long)u.h * s.Ttot + u.t0, (long)u.len * 4);
+      lds_copy4(rsrc_words(gr), (uint32_t)l * 4u, lds_addr(&sGc[ab][0]));
+      const rsrc_t br = make_rsrc(p.beta + (long)u.t0 * p.Hv + u.h, ((long)(u.len - 1) * p.Hv + 1) * 4);
+      lds_copy4(rsrc_words(br), (uint32_t)(l * p.Hv * 4), lds_addr(&sBe[ab][0]));
+    }
+  };
+  // rows 16w..16w+15 of h and dh as B fragments (contraction over V)
+  auto load_hd = [&](const Unit& u, bf16x8 (&hf)[4], bf16x8 (&df)[4]) __attribute__((always_inline)) {
+    const long base = (((long)u.h * s.NTtot + u.c) * KD + dcol) * VD + 8 * q;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      hf[ks] = *reinterpret_cast<const bf16x8*>((const T*)p.hbuf + base + 32 * ks);
+      df[ks] = *reinterpret_cast<const bf16x8*>((const T*)p.dhbuf + base + 32 * ks);
+    }
+  };
+
+  Unit cu;
+  if (!unit(0, cu)) return;
+  copy_Q(cu);
+  copy_K(cu);
+  copy_dO_Vn(cu);
+  copy_rest(cu, ic<0>());
+  f32x4 dq[4], dk[4], Sqk[2], Skk[2];
+  bf16x8 kt1[2], kt2[2];   // K fragments at column block w: rt (for dPD K, E K) and rb (for E^T K)
+
+  // One unit with its A and gate buffers ab (a compile-time index: the loop
+  // is unrolled by two); false when there is no next unit.
+  auto body = [&](auto abc, int j) __attribute__((always_inline)) -> bool {
+    constexpr int ab = decltype(abc)::value;
+    asm volatile("" : "+v"(q), "+v"(t), "+v"(dcol));
+    Unit nu;
+    const bool has_next = j + 1 < nunits && unit(j + 1, nu);
+    const bool new_item = cu.gi == 0;
+    const bool next_new = has_next && nu.gi == 0;
+    const T* sA = &sA2[ab][0];
+    const float* gcb = &sGc[ab][0];
+    const float* beb = &sBe[ab][0];
+    const int len = cu.len, t0 = cu.t0, h = cu.h;
+    bf16x8 Hf[4], Df[4];   // issued first, needed only after the dPD tiles
+    load_hd(cu, Hf, Df);
+
+    // ---- unit start: this unit's copies have landed (waited at the end of
+    // the previous unit); gate factors and zeroed per-wave partial sums
+    if (w == 0) {
+      const float gl = gcb[len - 1], gv = gcb[l];
+      const float gam = l < len ? gv : gl;
+      sGam[l] = gam;
+      sGm[l] = l < len ? __expf(gam) : 0.f;
+      sDec[l] = l < len ? __expf(gl - gam) : 0.f;
+      sBt[l] = l < len ? beb[l] : 0.f;
+    }
+    sRowP[w][l] = 0.f;
+    sColP[w][l] = 0.f;
+    sDbP[w][l] = 0.f;
+    lds_barrier();
+    if (new_item) {   // raw Q K^T and K K^T tiles, cached K fragments, zero dq and dk
+#pragma unroll
+      for (int m = 0; m < 2; ++m) { Sqk[m] = zero4(); Skk[m] = zero4(); }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 aq = ra16(sQ, 16 * ti + t, ks), ak = ra16(sK, 16 * ti + t, ks);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const bf16x8 bk = ra16(sK, 16 * (tj0 + m) + t, ks);
+          Sqk[m] = mf(aq, bk, Sqk[m]);
+          Skk[m] = mf(ak, bk, Skk[m]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        kt1[ks] = rt16(sK, ks, 16 * w);
+        kt2[ks] = rb16(sK, ks, 16 * w);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) { dq[tt] = zero4(); dk[tt] = zero4(); }
+    }
+
+    // ---- phase 1: dPD tiles; dO h^T, dVnew h^T, Vnew dh^T (column split)
+    {
+      f32x4 dP[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = ra16(sdO, 16 * ti + t, ks);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) dP[m] = mf(a, ra16(sVn, 16 * (tj0 + m) + t, ks), dP[m]);
+      }
+      float rx[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float cx = 0.f;
+        const int c = 16 * (tj0 + m) + t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * ti + 4 * q + e;
+          const float v = (r >= c && r < len) ? p.scale * __expf(sGam[r] - sGam[c]) * dP[m][e] : 0.f;
+          const float x = v * Sqk[m][e];
+          rx[e] += x;
+          cx += x;
+          sPD[t8(r, c)] = from_f<T>(v);
+        }
+        cx = col_group_sum(cx);
+        if (q == 0) sColP[w][c] -= cx;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float rs = row_group_sum(rx[e]);
+        if (t == 0) sRowP[w][16 * ti + 4 * q + e] += rs;
+      }
+    }
+    // Three passes over h and dh (rows 16w..16w+15 as B fragments), each
+    // folded right away: s Gamma_t dO h^T into dq, -dVnew h^T (dW) into LDS
+    // rows, dec_t Vnew dh^T into dk; with the row sums they feed.
+    float hdp = 0.f, rsum = 0.f;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const T* X = pass == 0 ? sdO : pass == 1 ? sdVn : sVn;
+      f32x4 acc[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 b = pass == 2 ? Df[ks] : Hf[ks];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = mf(ra16(X, 16 * tt + t, ks), b, acc[tt]);
+        if (pass == 2) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const bf16 hv = Hf[ks][i], dv = Df[ks][i];
+            hdp += to_f(hv) * to_f(dv);
+          }
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tt + 4 * q + e;
+          if (pass == 0) {
+            const float vq = p.scale * sGm[r] * acc[tt][e];
+            dq[tt][e] += vq;
+            const float rr = row_group_sum(vq * to_f(sQ[t16(r, dcol)]));
+            if (t == 0) sRowP[w][r] += rr;
+          } else if (pass == 1) {
+            sW[t16(r, dcol)] = from_f<T>(-acc[tt][e]);
+          } else {
+            const float vk = sDec[r] * acc[tt][e];
+            dk[tt][e] += vk;
+            const float rk = vk * to_f(sK[t16(r, dcol)]);
+            rsum += rk;
+            const float rr = row_group_sum(rk);
+            if (t == 0) sRowP[w][r] -= rr;
+          }
+        }
+      }
+    }
+    rsum = wave_sum(rsum);
+    hdp = wave_sum(hdp);
+    if (l == 0) { sRed[0][w] = rsum; sRed[1][w] = hdp; }
+    lds_barrier();   // dPD and dW rows complete; dO and Vnew are no longer read
+    if (has_next) copy_dO_Vn(nu);
+    {  // dQ += dPD K;  dK += dPD^T Q
+      bf16x8 bq[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) bq[ks] = rb16(sQ, ks, 16 * w);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dq[tt] = mf(ra8(sPD, 16 * tt + t, ks), kt1[ks], dq[tt]);
+          dk[tt] = mf(rb8(sPD, ks, 16 * tt), bq[ks], dk[tt]);
+        }
+    }
+    lds_barrier();   // Q and dPD are no longer read
+    if (next_new) copy_Q(nu);
+
+    // ---- phase 2: dA tiles; dKb = A^T dW and dVb = A^T dVnew (column split)
+    T* sdA = sPD;
+    {
+      f32x4 ta[2] = {zero4(), zero4()}, tb[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a1 = ra16(sW, 16 * ti + t, ks), a2 = ra16(sdVn, 16 * ti + t, ks);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          ta[m] = mf(a1, ra16(sK, 16 * (tj0 + m) + t, ks), ta[m]);
+          tb[m] = mf(a2, ra16(sV, 16 * (tj0 + m) + t, ks), tb[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int c = 16 * (tj0 + m) + t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * ti + 4 * q + e;
+          const float v = (r > c) ? sBt[c] * (sGm[c] * ta[m][e] + tb[m][e]) : 0.f;
+          sdA[t8(r, c)] = from_f<T>(v);
+        }
+      }
+    }
+    {  // dKb = A^T dW and dVb = A^T dVnew, rows s of A^T in blocks st
+      f32x4 kb[4], vb[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) { kb[st] = zero4(); vb[st] = zero4(); }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bw = rb16(sW, ks, 16 * w), bd = rb16(sdVn, ks, 16 * w);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const bf16x8 aA = rb8(sA, ks, 16 * st);
+          kb[st] = mf(aA, bw, kb[st]);
+          vb[st] = mf(aA, bd, vb[st]);
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * st + 4 * q + e;
+          const float bt = sBt[r], gm = sGm[r];
+          dk[st][e] += bt * gm * kb[st][e];
+          const float kk = row_group_sum(kb[st][e] * to_f(sK[t16(r, dcol)]));
+          const float vv = row_group_sum(vb[st][e] * to_f(sV[t16(r, dcol)]));
+          if (t == 0) {
+            sRowP[w][r] += bt * gm * kk;
+            sDbP[w][r] += gm * kk + vv;
+          }
+          if (r < len) ((T*)p.dv)[((long)(t0 + r) * p.Hv + h) * VD + dcol] = from_f<T>(bt * vb[st][e]);
+        }
+      }
+    }
+    lds_barrier();   // dA complete; dW, dVnew, V and K are no longer read from LDS
+    if (has_next) {
+      copy_rest(nu, ic<1 - ab>());
+      if (next_new) copy_K(nu);
+    }
+
+    // ---- phase 3: M1 = A^T dA; dL = -M1 A^T -> E; dK += E K + E^T K
+    T* sM1 = sW;
+    T* sE = sW + TE8;
+    {
+      f32x4 m1[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = rb8(sA, ks, 16 * ti);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) m1[m] = mf(a, rb8(sdA, ks, 16 * (tj0 + m)), m1[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sM1[t8(16 * ti + 4 * q + e, 16 * (tj0 + m) + t)] = from_f<T>(m1[m][e]);
+    }
+    lds_barrier();
+    {
+      f32x4 dl[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = ra8(sM1, 16 * ti + t, ks);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) dl[m] = mf(a, ra8(sA, 16 * (tj0 + m) + t, ks), dl[m]);
+      }
+      float rx[4] = {0.f, 0.f, 0.f, 0.f}, bs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int c = 16 * (tj0 + m) + t;
+        float cx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * ti + 4 * q + e;
+          float ev = 0.f;
+          if (r > c) {
+            const float D = __expf(sGam[r] - sGam[c]);
+            const float dlv = -dl[m][e];
+            const float y = dlv * D * Skk[m][e];
+            bs[e] += y;
+            ev = dlv * sBt[r] * D;
+            const float x = sBt[r] * y;
+            rx[e] += x;
+            cx += x;
+          }
+          sE[t8(r, c)] = from_f<T>(ev);
+        }
+        cx = col_group_sum(cx);
+        if (q == 0) sColP[w][c] -= cx;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float rs = row_group_sum(rx[e]), bsum = row_group_sum(bs[e]);
+        if (t == 0) {
+          sRowP[w][16 * ti + 4 * q + e] += rs;
+          sDbP[w][16 * ti + 4 * q + e] += bsum;
+        }
+      }
+    }
+    lds_barrier();   // E complete; every partial sum is in
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dk[tt] = mf(ra8(sE, 16 * tt + t, ks), kt1[ks], dk[tt]);
+        dk[tt] = mf(rb8(sE, ks, 16 * tt), kt2[ks], dk[tt]);
+      }
+    if (w == 0) {   // dgamma row sums, dg as its reverse cumulative sum, dbeta
+      float dgm = 0.f, db = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < FNW; ++ww) {
+        dgm += sRowP[ww][l] + sColP[ww][l];
+        db += sDbP[ww][l];
+      }
+      if (l == len - 1) {
+        float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < FNW; ++ww) { r0 += sRed[0][ww]; r1 += sRed[1][ww]; }
+        dgm += r0 + __expf(sGam[CH - 1]) * r1;
+      }
+      dgm = (l < len) ? dgm : 0.f;
+      const float rev = __shfl(dgm, 63 - l, 64);
+      const float sc = wave_inclusive_scan(rev);
+      const float dgv = __shfl(sc, 63 - l, 64);
+      if (l < len) {
+        p.dg[(long)(t0 + l) * p.Hv + h] = dgv;
+        p.dbeta[(long)(t0 + l) * p.Hv + h] = db;
+      }
+    }
+    if (cu.gi == G - 1) {   // the group's dq and dk rows
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tt + 4 * q + e;
+          if (r < len) {
+            const long o = ((long)(t0 + r) * p.Hq + cu.hk) * KD + dcol;
+            ((T*)p.dq)[o] = from_f<T>(dq[tt][e]);
+            ((T*)p.dk)[o] = from_f<T>(dk[tt][e]);
+          }
+        }
+    }
+    // the next unit's copies have landed; every wave is done with this unit
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (!has_next) return false;
+    cu = nu;
+    return true;
+  };
+  for (int j = 0; j < nunits; j += 2) {
+    if (!body(ic<0>(), j) || !body(ic<1>(), j + 1)) break;
+  }
+}
+
+hipError_t launch_gradsf(const GradParams& p, hipStream_t st) {
+  const int total = p.s.NTtot * p.Hq;
+  if (total <= 0) return hipSuccess;
+  const int nwg = std::min(total, 256);
+  const int per_wg = (total + nwg - 1) / nwg;
+  timing_before("chunk_grads", st);
+  hipLaunchKernelGGL((k_gradsf<128>), dim3(nwg), dim3(FNT), 0, st, p, total, per_wg);
+  hipError_t err = hipGetLastError();
+  timing_after(st);
+  return err;
+}
+
+}  // namespace gdr

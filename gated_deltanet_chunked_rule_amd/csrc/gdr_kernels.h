@@ -7,7 +7,7 @@
 //   W, U  T    [Hv][Ttot][K|V]     W = A diag(beta*Gamma) K,  U = A diag(beta) V
 //   vnew  T    [Hv][Ttot][V]       Vnew = U - W h (token rows; backward only)
 //   hbuf  T    [Hv][NTtot][K][V]   state entering each chunk (backward only)
-//   A     fp32 [Hv][Ttot][64]      rows of the chunk's A (backward only)
+//   A     fp32 [Hv][Ttot][64]      rows of the chunk's A (backward only; bf16 for K = 128)
 //   dhbuf T    [Hv][NTtot][K][V]   gradient of the state leaving each chunk
 //   dvn   T    [Hv][Ttot][V]       gradient of Vnew (token rows)
 //   segtr fp32 [Hv][segs][2][K][V] per CP segment: M (start -> end state map) and b;
@@ -49,6 +49,7 @@ struct IntraParams {
   float* cert;
   void *W, *U;
   float* A_ws;               // nullable, [Hv][Ttot][64]
+  void* A_bf;                // nullable, bf16 [Hv][Ttot][64] (the per-chunk gradient kernel's copy)
   float* A_out;              // nullable, [Ttot][Hv][64]
   const float* A_in;         // nullable: use this A ([Ttot][Hv][64]) instead of inverting
 };
@@ -128,6 +129,7 @@ struct GradParams {          // per-chunk gradients
   SeqTables s;
   const void *q, *k, *v, *d_o, *hbuf, *vnew, *dhbuf, *dvn;
   const float *gcum, *beta, *A_ws;
+  const void* A_bf;          // bf16 copy of A (K = 128 kernel)
   void *dq, *dk, *dv;
   float *dbeta, *dg;
   int Hq, Hv;
@@ -144,6 +146,7 @@ hipError_t launch_segscan(int KD, const ScanParams& p, int total_items, hipStrea
 hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, int total_items, hipStream_t st);
 hipError_t launch_dfused(DType dt, int KD, const DFusedParams& p, int total_segs, hipStream_t st);
 hipError_t launch_grads(DType dt, int KD, const GradParams& p, hipStream_t st);
+hipError_t launch_gradsf(const GradParams& p, hipStream_t st);   // bf16, K = V = 128, A_bf set
 
 // Kernel timing hooks (gdr_timing.cpp).
 void timing_before(const char* name, hipStream_t st);
