@@ -35,6 +35,50 @@
 
 namespace gdr {
 
+// Sum over the 16 lanes of a DPP row (the lanes sharing lane / 16), on the
+// VALU: quad swaps, then the mirrored half-row, then the mirrored row.
+template <int C>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), C, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x141>(x);   // row_half_mirror
+  x += dpp_f<0x140>(x);   // row_mirror
+  return x;
+}
+
+// 4 x 4 transpose within each quad of lanes: on entry lane 4k + i holds
+// x[e] = M[e][i]; on exit x[c] = M[i][c].  Accumulator tiles then give each
+// lane four consecutive columns of one row (8-byte bf16 stores).
+__device__ __forceinline__ f32x4 quad_t(f32x4 x) {
+  const int i = lane_id() & 3;
+  {
+    const bool odd = (i & 1) != 0;
+    float s0 = odd ? x[0] : x[1], s1 = odd ? x[2] : x[3];
+    s0 = dpp_f<0xB1>(s0);
+    s1 = dpp_f<0xB1>(s1);
+    if (odd) { x[0] = s0; x[2] = s1; } else { x[1] = s0; x[3] = s1; }
+  }
+  {
+    const bool hi = (i & 2) != 0;
+    float s0 = hi ? x[0] : x[2], s1 = hi ? x[1] : x[3];
+    s0 = dpp_f<0x4E>(s0);
+    s1 = dpp_f<0x4E>(s1);
+    if (hi) { x[0] = s0; x[1] = s1; } else { x[2] = s0; x[3] = s1; }
+  }
+  return x;
+}
+__device__ __forceinline__ uint2 pack4_bf16(f32x4 x) {
+  bf16x4 b;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) b[c] = static_cast<bf16>(x[c]);
+  uint2 u;
+  __builtin_memcpy(&u, &b, 8);
+  return u;
+}
+
 template <int KD>
 __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, int per_wg) {
   using T = bf16;
@@ -96,6 +140,34 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     const int r = 32 * ks + 8 * q + (t >> 2), c = c0 + 4 * (t & 3);
     return cat4(trd(X + t16(r, c)), trd(X + t16(r + 4, c)));
   };
+  // X[16tt + 4q + i][dcol], i < 4 (the rows of this lane's accumulator entries)
+  auto rows4 = [&](const T* X, int tt) __attribute__((always_inline)) {
+    const i16x4 v = trd(X + t16(16 * tt + 4 * q + (t >> 2), 16 * w + 4 * (t & 3)));
+    f32x4 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float((uint32_t)(uint16_t)v[i] << 16);
+    return f;
+  };
+  auto fac4 = [&](const float* F, int tt) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(F + 16 * tt + 4 * q);
+  };
+  // Row sums of per-lane partials x[tt][e] (rows 16tt + 4q + e); lane t
+  // receives the sum for tt = t / 4, e = t % 4, i.e. row 16(t/4) + 4q + t%4.
+  auto own_rows = [&](const f32x4 (&x)[4]) __attribute__((always_inline)) {
+    float own = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = row16_sum(x[tt][e]);
+        own = (t == 4 * tt + e) ? v : own;
+      }
+    return own;
+  };
+  // accumulator tile (row block rb, column block cb) of a 64 x 64 LDS matrix, 8-byte writes
+  auto st_tile8 = [&](T* X, int rb, int cb, f32x4 v) __attribute__((always_inline)) {
+    *reinterpret_cast<uint2*>(X + t8(16 * rb + 4 * q + (t & 3), 16 * cb + 4 * (t >> 2))) = pack4_bf16(quad_t(v));
+  };
   auto mf = [](bf16x8 a, bf16x8 b, f32x4 c) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   };
@@ -116,14 +188,21 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     off_a[0] = (uint32_t)(r * CH * 2 + c * 16);
   }
   struct Unit { int c, hk, h, gi, t0, len; };
+  int cc = -1, ct0 = 0, clen = 0;   // the last chunk looked up (the chunk changes every Hq items)
   auto unit = [&](int j, Unit& u) __attribute__((always_inline)) -> bool {
     const int it = i0 + j / G;
     u.gi = j % G;
     u.c = it / p.Hq;
     u.hk = it % p.Hq;
     u.h = u.hk * G + u.gi;
-    int n;
-    return locate_chunk_b(s, u.c, n, u.t0, u.len);
+    if (u.c != cc) {
+      int n;
+      if (!locate_chunk_b(s, u.c, n, ct0, clen)) return false;
+      cc = u.c;
+    }
+    u.t0 = ct0;
+    u.len = clen;
+    return true;
   };
   auto tile = [&](T* dst, const void* base, long elem0, long row_elems, int len, const uint32_t* off)
       __attribute__((always_inline)) {
@@ -139,10 +218,12 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   auto copy_K = [&](const Unit& u) __attribute__((always_inline)) {
     tile(sK, p.k, ((long)u.t0 * p.Hq + u.hk) * KD, (long)p.Hq * KD, u.len, off_qk);
   };
-  auto copy_rest = [&](const Unit& u, auto abc) __attribute__((always_inline)) {   // dVnew, V, A, gates
-    constexpr int ab = decltype(abc)::value;
+  auto copy_dVn_V = [&](const Unit& u) __attribute__((always_inline)) {
     tile(sdVn, p.dvn, ((long)u.h * s.Ttot + u.t0) * VD, VD, u.len, off_ws);
     tile(sV, p.v, ((long)u.t0 * p.Hv + u.h) * VD, (long)p.Hv * VD, u.len, off_hv);
+  };
+  auto copy_A_gates = [&](const Unit& u, auto abc) __attribute__((always_inline)) {   // into buffer ab
+    constexpr int ab = decltype(abc)::value;
     lds_copy_tile<1, 8, FNW, 8>(&sA2[ab][0],
                                 make_rsrc((const T*)p.A_bf + ((long)u.h * s.Ttot + u.t0) * CH, (long)u.len * CH * 2),
                                 off_a, w);
@@ -168,8 +249,13 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   copy_Q(cu);
   copy_K(cu);
   copy_dO_Vn(cu);
-  copy_rest(cu, ic<0>());
-  f32x4 dq[4], dk[4], Sqk[2], Skk[2];
+  copy_dVn_V(cu);
+  copy_A_gates(cu, ic<0>());
+  // the first unit's copies have landed (later units wait at the end of the previous one)
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  f32x4 dq[4], dk[4];
   bf16x8 kt1[2], kt2[2];   // K fragments at column block w: rt (for dPD K, E K) and rb (for E^T K)
 
   // One unit with its A and gate buffers ab (a compile-time index: the loop
@@ -185,7 +271,8 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     const float* gcb = &sGc[ab][0];
     const float* beb = &sBe[ab][0];
     const int len = cu.len, t0 = cu.t0, h = cu.h;
-    bf16x8 Hf[4], Df[4];   // issued first, needed only after the dPD tiles
+    // this unit's h and dh fragments: issued first, needed after the dPD tiles
+    bf16x8 Hf[4], Df[4];
     load_hd(cu, Hf, Df);
 
     // ---- unit start: this unit's copies have landed (waited at the end of
@@ -202,19 +289,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     sColP[w][l] = 0.f;
     sDbP[w][l] = 0.f;
     lds_barrier();
-    if (new_item) {   // raw Q K^T and K K^T tiles, cached K fragments, zero dq and dk
-#pragma unroll
-      for (int m = 0; m < 2; ++m) { Sqk[m] = zero4(); Skk[m] = zero4(); }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 aq = ra16(sQ, 16 * ti + t, ks), ak = ra16(sK, 16 * ti + t, ks);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 bk = ra16(sK, 16 * (tj0 + m) + t, ks);
-          Sqk[m] = mf(aq, bk, Sqk[m]);
-          Skk[m] = mf(ak, bk, Skk[m]);
-        }
-      }
+    if (new_item) {   // cached K fragments, zero dq and dk
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         kt1[ks] = rt16(sK, ks, 16 * w);
@@ -226,18 +301,22 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 
     // ---- phase 1: dPD tiles; dO h^T, dVnew h^T, Vnew dh^T (column split)
     {
-      f32x4 dP[2] = {zero4(), zero4()};
+      f32x4 dP[2] = {zero4(), zero4()}, Sqk[2] = {zero4(), zero4()};   // dO Vnew^T and raw Q K^T
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = ra16(sdO, 16 * ti + t, ks);
+        const bf16x8 a = ra16(sdO, 16 * ti + t, ks), aq = ra16(sQ, 16 * ti + t, ks);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) dP[m] = mf(a, ra16(sVn, 16 * (tj0 + m) + t, ks), dP[m]);
+        for (int m = 0; m < 2; ++m) {
+          dP[m] = mf(a, ra16(sVn, 16 * (tj0 + m) + t, ks), dP[m]);
+          Sqk[m] = mf(aq, ra16(sK, 16 * (tj0 + m) + t, ks), Sqk[m]);
+        }
       }
       float rx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         float cx = 0.f;
         const int c = 16 * (tj0 + m) + t;
+        f32x4 pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * ti + 4 * q + e;
@@ -245,21 +324,53 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
           const float x = v * Sqk[m][e];
           rx[e] += x;
           cx += x;
-          sPD[t8(r, c)] = from_f<T>(v);
+          pv[e] = v;
         }
+        st_tile8(sPD, ti, tj0 + m, pv);
         cx = col_group_sum(cx);
         if (q == 0) sColP[w][c] -= cx;
       }
+      float own = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float rs = row_group_sum(rx[e]);
-        if (t == 0) sRowP[w][16 * ti + 4 * q + e] += rs;
+        const float v = row16_sum(rx[e]);
+        own = (t == e) ? v : own;
       }
+      if (t < 4) sRowP[w][16 * ti + 4 * q + t] += own;
     }
     // Three passes over h and dh (rows 16w..16w+15 as B fragments), each
     // folded right away: s Gamma_t dO h^T into dq, -dVnew h^T (dW) into LDS
     // rows, dec_t Vnew dh^T into dk; with the row sums they feed.
+    {  // dVb = A^T dVnew (needs neither h nor dh): dv and its dbeta terms
+      f32x4 vb[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) vb[st] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bd = rb16(sdVn, ks, 16 * w);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) vb[st] = mf(rb8(sA, ks, 16 * st), bd, vb[st]);
+      }
+      f32x4 dbL[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const f32x4 bt = fac4(sBt, st), ve = rows4(sV, st);
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dbL[st][e] = vb[st][e] * ve[e];
+          o[e] = bt[e] * vb[st][e];
+        }
+        const int r = 16 * st + 4 * q + (t & 3);   // after the transpose: row r, columns 16w + 4(t/4) ..
+        const uint2 u = pack4_bf16(quad_t(o));
+        if (r < len) *reinterpret_cast<uint2*>((T*)p.dv + ((long)(t0 + r) * p.Hv + h) * VD + 16 * w + 4 * (t >> 2)) = u;
+      }
+      sDbP[w][16 * (t >> 2) + 4 * q + (t & 3)] += own_rows(dbL);
+    }
     float hdp = 0.f, rsum = 0.f;
+    f32x4 rowL[4];   // per-lane row partials (rows 16tt + 4q + e)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) rowL[tt] = zero4();
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
       const T* X = pass == 0 ? sdO : pass == 1 ? sdVn : sVn;
@@ -281,32 +392,39 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
+        if (pass == 0) {
+          const f32x4 gm = fac4(sGm, tt), qe = rows4(sQ, tt);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tt + 4 * q + e;
-          if (pass == 0) {
-            const float vq = p.scale * sGm[r] * acc[tt][e];
+          for (int e = 0; e < 4; ++e) {
+            const float vq = p.scale * gm[e] * acc[tt][e];   // s Gamma_t (dO h^T)
             dq[tt][e] += vq;
-            const float rr = row_group_sum(vq * to_f(sQ[t16(r, dcol)]));
-            if (t == 0) sRowP[w][r] += rr;
-          } else if (pass == 1) {
-            sW[t16(r, dcol)] = from_f<T>(-acc[tt][e]);
-          } else {
-            const float vk = sDec[r] * acc[tt][e];
+            rowL[tt][e] += vq * qe[e];
+          }
+        } else if (pass == 1) {   // dW rows
+          const uint2 u = pack4_bf16(quad_t(-acc[tt]));
+          *reinterpret_cast<uint2*>(sW + t16(16 * tt + 4 * q + (t & 3), 16 * w + 4 * (t >> 2))) = u;
+        } else {
+          const f32x4 dc = fac4(sDec, tt), ke = rows4(sK, tt);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float vk = dc[e] * acc[tt][e];             // dec_t (Vnew dh^T)
             dk[tt][e] += vk;
-            const float rk = vk * to_f(sK[t16(r, dcol)]);
+            const float rk = vk * ke[e];
             rsum += rk;
-            const float rr = row_group_sum(rk);
-            if (t == 0) sRowP[w][r] -= rr;
+            rowL[tt][e] -= rk;
           }
         }
       }
     }
+    sRowP[w][16 * (t >> 2) + 4 * q + (t & 3)] += own_rows(rowL);
     rsum = wave_sum(rsum);
     hdp = wave_sum(hdp);
     if (l == 0) { sRed[0][w] = rsum; sRed[1][w] = hdp; }
     lds_barrier();   // dPD and dW rows complete; dO and Vnew are no longer read
-    if (has_next) copy_dO_Vn(nu);
+    if (has_next) {
+      copy_dO_Vn(nu);
+      copy_A_gates(nu, ic<1 - ab>());
+    }
     {  // dQ += dPD K;  dK += dPD^T Q
       bf16x8 bq[2];
 #pragma unroll
@@ -324,62 +442,62 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 
     // ---- phase 2: dA tiles; dKb = A^T dW and dVb = A^T dVnew (column split)
     T* sdA = sPD;
+    f32x4 Skk[2] = {zero4(), zero4()};   // raw K K^T tiles (for phase 3)
     {
       f32x4 ta[2] = {zero4(), zero4()}, tb[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 a1 = ra16(sW, 16 * ti + t, ks), a2 = ra16(sdVn, 16 * ti + t, ks);
+        const bf16x8 ak = ra16(sK, 16 * ti + t, ks);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          ta[m] = mf(a1, ra16(sK, 16 * (tj0 + m) + t, ks), ta[m]);
+          const bf16x8 bk = ra16(sK, 16 * (tj0 + m) + t, ks);
+          ta[m] = mf(a1, bk, ta[m]);
+          Skk[m] = mf(ak, bk, Skk[m]);
           tb[m] = mf(a2, ra16(sV, 16 * (tj0 + m) + t, ks), tb[m]);
         }
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int c = 16 * (tj0 + m) + t;
+        f32x4 av;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * ti + 4 * q + e;
-          const float v = (r > c) ? sBt[c] * (sGm[c] * ta[m][e] + tb[m][e]) : 0.f;
-          sdA[t8(r, c)] = from_f<T>(v);
+          av[e] = (r > c) ? sBt[c] * (sGm[c] * ta[m][e] + tb[m][e]) : 0.f;
         }
+        st_tile8(sdA, ti, tj0 + m, av);
       }
     }
-    {  // dKb = A^T dW and dVb = A^T dVnew, rows s of A^T in blocks st
-      f32x4 kb[4], vb[4];
+    {  // dKb = A^T dW, rows s of A^T in blocks st
+      f32x4 kb[4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) { kb[st] = zero4(); vb[st] = zero4(); }
+      for (int st = 0; st < 4; ++st) kb[st] = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bw = rb16(sW, ks, 16 * w), bd = rb16(sdVn, ks, 16 * w);
+        const bf16x8 bw = rb16(sW, ks, 16 * w);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const bf16x8 aA = rb8(sA, ks, 16 * st);
-          kb[st] = mf(aA, bw, kb[st]);
-          vb[st] = mf(aA, bd, vb[st]);
-        }
+        for (int st = 0; st < 4; ++st) kb[st] = mf(rb8(sA, ks, 16 * st), bw, kb[st]);
       }
+      f32x4 rowK[4], dbL[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
+        const f32x4 bt = fac4(sBt, st), gm = fac4(sGm, st), ke = rows4(sK, st);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * st + 4 * q + e;
-          const float bt = sBt[r], gm = sGm[r];
-          dk[st][e] += bt * gm * kb[st][e];
-          const float kk = row_group_sum(kb[st][e] * to_f(sK[t16(r, dcol)]));
-          const float vv = row_group_sum(vb[st][e] * to_f(sV[t16(r, dcol)]));
-          if (t == 0) {
-            sRowP[w][r] += bt * gm * kk;
-            sDbP[w][r] += gm * kk + vv;
-          }
-          if (r < len) ((T*)p.dv)[((long)(t0 + r) * p.Hv + h) * VD + dcol] = from_f<T>(bt * vb[st][e]);
+          dk[st][e] += bt[e] * gm[e] * kb[st][e];
+          const float kk = kb[st][e] * ke[e];
+          rowK[st][e] = bt[e] * gm[e] * kk;
+          dbL[st][e] = gm[e] * kk;
         }
       }
+      const int rown = 16 * (t >> 2) + 4 * q + (t & 3);
+      sRowP[w][rown] += own_rows(rowK);
+      sDbP[w][rown] += own_rows(dbL);
     }
     lds_barrier();   // dA complete; dW, dVnew, V and K are no longer read from LDS
     if (has_next) {
-      copy_rest(nu, ic<1 - ab>());
+      copy_dVn_V(nu);
       if (next_new) copy_K(nu);
     }
 
@@ -395,9 +513,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
         for (int m = 0; m < 2; ++m) m1[m] = mf(a, rb8(sdA, ks, 16 * (tj0 + m)), m1[m]);
       }
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sM1[t8(16 * ti + 4 * q + e, 16 * (tj0 + m) + t)] = from_f<T>(m1[m][e]);
+      for (int m = 0; m < 2; ++m) st_tile8(sM1, ti, tj0 + m, m1[m]);
     }
     lds_barrier();
     {
@@ -413,6 +529,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int m = 0; m < 2; ++m) {
         const int c = 16 * (tj0 + m) + t;
         float cx = 0.f;
+        f32x4 evv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * ti + 4 * q + e;
@@ -427,18 +544,22 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
             rx[e] += x;
             cx += x;
           }
-          sE[t8(r, c)] = from_f<T>(ev);
+          evv[e] = ev;
         }
+        st_tile8(sE, ti, tj0 + m, evv);
         cx = col_group_sum(cx);
         if (q == 0) sColP[w][c] -= cx;
       }
+      float orow = 0.f, odb = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float rs = row_group_sum(rx[e]), bsum = row_group_sum(bs[e]);
-        if (t == 0) {
-          sRowP[w][16 * ti + 4 * q + e] += rs;
-          sDbP[w][16 * ti + 4 * q + e] += bsum;
-        }
+        const float vr = row16_sum(rx[e]), vb = row16_sum(bs[e]);
+        orow = (t == e) ? vr : orow;
+        odb = (t == e) ? vb : odb;
+      }
+      if (t < 4) {
+        sRowP[w][16 * ti + 4 * q + t] += orow;
+        sDbP[w][16 * ti + 4 * q + t] += odb;
       }
     }
     lds_barrier();   // E complete; every partial sum is in
@@ -473,16 +594,15 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     }
     if (cu.gi == G - 1) {   // the group's dq and dk rows
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tt + 4 * q + e;
-          if (r < len) {
-            const long o = ((long)(t0 + r) * p.Hq + cu.hk) * KD + dcol;
-            ((T*)p.dq)[o] = from_f<T>(dq[tt][e]);
-            ((T*)p.dk)[o] = from_f<T>(dk[tt][e]);
-          }
+      for (int tt = 0; tt < 4; ++tt) {
+        const int r = 16 * tt + 4 * q + (t & 3);
+        const uint2 uq = pack4_bf16(quad_t(dq[tt])), uk = pack4_bf16(quad_t(dk[tt]));
+        if (r < len) {
+          const long o = ((long)(t0 + r) * p.Hq + cu.hk) * KD + 16 * w + 4 * (t >> 2);
+          *reinterpret_cast<uint2*>((T*)p.dq + o) = uq;
+          *reinterpret_cast<uint2*>((T*)p.dk + o) = uk;
         }
+      }
     }
     // the next unit's copies have landed; every wave is done with this unit
     __builtin_amdgcn_s_waitcnt(0);

@@ -154,3 +154,12 @@ def test_cp_backward_varlen():
                   gate=(0.5, 0.8), zero_gate_frac=0.5)
     inp = gi.packed_from_lengths(w, [64 * 9 + 7, 1, 64 * 3, 0, 64 * 6 + 40])
     check_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 2, 1), label="CP varlen")
+
+
+def test_many_chunks_per_workgroup():
+    # Enough (chunk, query/key head) items that each workgroup of the
+    # persistent per-chunk gradient kernel walks several of them, crossing
+    # chunk and head boundaries; sampled heads keep the oracle fast.
+    w = gi.custom(B=1, T=64 * 600 + 17, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=94, initial_state=True,
+                  backward=True, gate=(0.9, 0.999))
+    check_bwd(gi.make_inputs(w), qk_heads=(1, 2), label="many chunks per workgroup")
