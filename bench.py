@@ -12,7 +12,10 @@ bytes or flops per launch) and the fp64 CPU oracle's throughput on the host.
 The line also carries "configs_report": the other parity configurations (tiny
 fp32, edge prefill, varlen forward and the backward), each timed per call
 with a cache flush between calls and set against the method's roofline
-(essential I/O and chunk-GEMM flops per token x value head).
+(essential I/O and chunk-GEMM flops per token x value head); and
+"train_step_sweep": training-step (forward + backward) and backward latency
+against tokens per update step for value-head counts 64, 48, 32, 24, 16, 8
+(the head configurations the pages benchmark the backward on).
 """
 from __future__ import annotations
 
@@ -147,6 +150,73 @@ def config_report(torch, gdr, gi, dev):
     return out
 
 
+SWEEP_HV = (64, 48, 32, 24, 16, 8)          # value heads per GPU (TP1 .. TP8 shares)
+SWEEP_TOKENS = (8192, 16384, 32768, 65536)   # tokens per update step, as 8192-token sequences
+
+
+def train_step_sweep(torch, gdr, dev):
+    """Training-step latency against tokens per update step for each value-head
+    count: one forward + backward through the autograd wrapper (the forward's
+    A reused by the backward), and the backward entry point alone.  Hq = Hv/2,
+    K = V = 128, bf16; inputs drawn on the device (q, k L2-normalised N(0,1),
+    v and do N(0,1), g = log U(0.85, 1), beta = sigmoid(N(0,1)), no initial
+    state), median of 5 calls with a cache flush before each."""
+    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    K = V = 128
+    rows = []
+    for hv in SWEEP_HV:
+        hq = hv // 2
+        for tokens in SWEEP_TOKENS:
+            B, T = tokens // 8192, 8192
+            nrm = lambda x: x / x.norm(dim=-1, keepdim=True)
+            q = nrm(torch.randn(B, T, hq, K, device=dev, generator=gen)).to(torch.bfloat16)
+            k = nrm(torch.randn(B, T, hq, K, device=dev, generator=gen)).to(torch.bfloat16)
+            v = torch.randn(B, T, hv, V, device=dev, generator=gen).to(torch.bfloat16)
+            do = torch.randn(B, T, hv, V, device=dev, generator=gen).to(torch.bfloat16)
+            g = torch.log(0.85 + 0.15 * torch.rand(B, T, hv, device=dev, generator=gen))
+            beta = torch.sigmoid(torch.randn(B, T, hv, device=dev, generator=gen))
+            scale = K ** -0.5
+            leaves = [x.detach().requires_grad_(True) for x in (q, k, v, g, beta)]
+
+            def step():
+                o, _ = gdr.chunk_gated_delta_rule(*leaves, scale)
+                return torch.autograd.grad(o, leaves, do)
+
+            _, _, _, A = gdr.gdr_chunk_fwd(q, k, v, g, beta, scale, output_A=True)
+            bwd = lambda: gdr.gdr_chunk_bwd(q, k, v, g, beta, A, do, None, scale, None, None)
+
+            def timed(fn, iters=5):
+                for _ in range(2):
+                    fn()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(iters):
+                    flush.zero_()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+                return sorted(ts)[len(ts) // 2]
+
+            ms_step, ms_bwd = timed(step), timed(bwd)
+            tv = tokens * hv
+            ff, fb = method_work(K, V, 2, 2, False)
+            bf, bb = method_work(K, V, 2, 2, True)
+            roof = lambda fl, by: max(fl * tv / (MFMA_BF16_PEAK_TFS * 1e12), by * tv / (HBM_PEAK_GBS * 1e9))
+            rows.append({"hv": hv, "hq": hq, "tokens": tokens, "ms_step": round(ms_step, 3),
+                         "ms_bwd": round(ms_bwd, 3),
+                         "step_tokens_per_s": round(tokens / (ms_step * 1e-3)),
+                         "step_roof_frac": round(roof(ff + bf, fb + bb) / (ms_step * 1e-3), 4),
+                         "bwd_roof_frac": round(roof(bf, bb) / (ms_bwd * 1e-3), 4)})
+            del q, k, v, do, g, beta, leaves, A
+            torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +224,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration report")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the training-step sweep")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -250,6 +321,9 @@ def main():
         del q, k, v, g, beta, ws
         torch.cuda.empty_cache()
         configs = config_report(torch, gdr, gi, dev)
+    sweep = None
+    if not args.no_sweep:
+        sweep = train_step_sweep(torch, gdr, dev)
 
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -263,6 +337,7 @@ def main():
         "method_roofline": method_roof,
         "cpu_baseline": cpu,
         "configs_report": configs,
+        "train_step_sweep": sweep,
     }
     print(json.dumps(out))
 

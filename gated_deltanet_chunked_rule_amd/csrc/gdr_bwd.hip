@@ -208,7 +208,7 @@ struct DFusedBufs {   // one buffer of staged chunk inputs
   float *G, *D;       // gate cumsums; per-row factors {e^{gamma_n - gamma_t}, s e^{gamma_t}}
 };
 
-template <int KD>
+template <int KD, bool TRANS>
 __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items) {
   using T = bf16;
   constexpr int VD = KD;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   // chunks crs down to cbeg; those below cend are the segment's own
   int cbeg = pseg * L, cend = min(cbeg + L, nch), crs;
   const float* ginit = nullptr;   // end gradient (null: zero)
-  if (p.trans) {
+  if (TRANS) {
     if (certified || pseg == 0) return;
     crs = cend - 1;
     if (pseg == nseg - 1) ginit = p.dht ? p.dht + hbase : nullptr;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
     const int t0 = seq0 + jc * CH;
     const int len = min(CH, seq1 - t0);
     if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) return false;
-    const bool keep = !p.trans && jc < cend;   // a chunk of the segment itself
+    const bool keep = !TRANS && jc < cend;   // a chunk of the segment itself
     const bool more = jc - 1 >= cbeg;
     const DFusedBufs<T> cur = bufs(bc);
     if (more) {
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
 
   if (owner) {
     float* dst = nullptr;
-    if (p.trans) dst = p.segtr + (((long)h * p.total_segs + gseg) * 2 + 1) * KD * VD;
+    if (TRANS) dst = p.segtr + (((long)h * p.total_segs + gseg) * 2 + 1) * KD * VD;
     else if (cbeg == 0 && p.dh0) dst = p.dh0 + hbase;
     if (dst) {
 #pragma unroll
@@ -944,7 +944,8 @@ template <int KD>
 static hipError_t dfused_impl(const DFusedParams& p, int total_segs, hipStream_t st) {
   const int total = total_segs * p.Hv;
   timing_before(p.trans ? "cp_rev_transition" : "chunk_dfused", st);
-  hipLaunchKernelGGL((k_dfused<KD>), dim3(padded_grid_b(total)), dim3(FNT), 0, st, p, total);
+  if (p.trans) hipLaunchKernelGGL((k_dfused<KD, true>), dim3(padded_grid_b(total)), dim3(FNT), 0, st, p, total);
+  else hipLaunchKernelGGL((k_dfused<KD, false>), dim3(padded_grid_b(total)), dim3(FNT), 0, st, p, total);
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;

@@ -634,7 +634,7 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
 // two per wave); the bf16 output is staged in LDS and written as full rows.
 // Two workgroup barriers per chunk.  Two waves per SIMD hide each other's
 // LDS and MFMA latencies.
-// Segment transitions (p.trans = 1, heads that fail the warmup certificate):
+// Segment transitions (MODE 2, heads that fail the warmup certificate):
 // the map from a segment's start state to its end state is affine,
 // h_out = M h_in + b, so one workgroup per (segment, part) runs the segment's
 // chunks without output from h = I with U taken as zero (part 0: M, from the
@@ -653,8 +653,11 @@ struct FusedBufs {   // one buffer of staged chunk inputs
   float *G, *D;      // gate cumsums; per-row factors {e^{gamma_n - gamma_t}, s e^{gamma_t}}
 };
 
-template <typename T, int KD, bool ST>
+// MODE: 0 the output pass, 1 the backward's states pass, 2 the segment
+// transitions (separate instantiations, so each keeps only its own paths).
+template <typename T, int KD, int MODE>
 __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
+  constexpr bool TRANS = MODE == 2;
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
   constexpr int VEC = 16 / (int)sizeof(T);
@@ -687,8 +690,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   if (u >= total_items) return;
   const int h = u % p.Hv;
   const int item2 = u / p.Hv;
-  const int part = p.trans ? (item2 & 1) : 1;   // transition pass: 0 M, 1 b
-  const int item = p.trans ? (item2 >> 1) : item2;
+  const int part = TRANS ? (item2 & 1) : 1;   // transition pass: 0 M, 1 b
+  const int item = TRANS ? (item2 >> 1) : item2;
   const int n = find_seq(s.seg_off, s.N, item);
   const int pseg = item - s.seg_off[n];
   const int nseg = s.seg_off[n + 1] - s.seg_off[n];
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   const bool exact = !certified && p.hstart != nullptr;
   int cstart, cbeg, cend;
   bool write_final;
-  if (p.trans) {   // uncertified heads only; the last segment's map is not needed
+  if (TRANS) {   // uncertified heads only; the last segment's map is not needed
     if (certified || pseg == nseg - 1 || (part == 0 && pseg == 0)) return;
     cbeg = cstart = pseg * L;
     cend = min(cbeg + L, nch);
@@ -726,15 +729,15 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     if (pseg != 0) return;             // segment 0 runs the whole head serially
     cstart = 0; cbeg = 0; cend = nch; write_final = true;
   }
-  const bool no_u = p.trans && part == 0;         // M: the segment's map with U = 0
-  const bool st_mode = ST && !p.trans;   // backward recompute: states, no output
+  const bool no_u = TRANS && part == 0;         // M: the segment's map with U = 0
+  const bool st_mode = MODE == 1;   // backward recompute: states, no output
 
   const long hbase = ((long)n * p.Hv + h) * KD * VD;
   auto krow = [&](int rb, int e) { return 32 * (rb >> 1) + 8 * q + 4 * (rb & 1) + e; };
   // Initial state: h0 at a sequence start, an exact start state, the identity
   // (transition part 0) or zero.
   const float* hinit = nullptr;
-  if (p.trans) {
+  if (TRANS) {
     if (part == 1 && pseg == 0 && p.h0) hinit = p.h0 + hbase;
   } else if (cstart == 0) {
     if (p.h0) hinit = p.h0 + hbase;
@@ -784,7 +787,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     if (piece == 2)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
     if (piece == 3) {
-      if (jc >= cbeg && !p.trans && !st_mode)
+      if (jc >= cbeg && !TRANS && !st_mode)
         lds_copy_tile<NCP, NCH, FNW, VEC>(bf.Q, make_rsrc((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
       if (w == 0) {
         const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
@@ -839,7 +842,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const int t0 = seq0 + jc * CH;
     const int len = min(CH, seq1 - t0);
     if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) return false;
-    const bool warm = jc < cbeg || p.trans || st_mode;   // no output for this chunk
+    const bool warm = jc < cbeg || TRANS || st_mode;   // no output for this chunk
     const bool keep = st_mode && jc >= cbeg;             // store the entry state and Vnew
     const bool more = jc + 1 < cend;
     const FusedBufs<T> cur = bufs(bc);
@@ -1115,7 +1118,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   }
   if (prev_out) store_o(prev_t0, prev_len);
 
-  if (p.trans && owner) {
+  if (TRANS && owner) {
     float* dst = p.segtr + (((long)h * p.total_segs + gseg) * 2 + part) * KD * VD;
 #pragma unroll
     for (int rb = 0; rb < NKB; ++rb)
@@ -1261,8 +1264,9 @@ static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t s
   const int total = total_segs * p.Hv * (p.trans ? 2 : 1);
   const bool states = p.hbuf != nullptr && !p.trans;
   timing_before(p.trans ? "cp_transition" : states ? "chunk_states" : "chunk_fused", st);
-  if (states) hipLaunchKernelGGL((k_fused<T, KD, true>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
-  else hipLaunchKernelGGL((k_fused<T, KD, false>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  if (p.trans) hipLaunchKernelGGL((k_fused<T, KD, 2>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  else if (states) hipLaunchKernelGGL((k_fused<T, KD, 1>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  else hipLaunchKernelGGL((k_fused<T, KD, 0>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;
