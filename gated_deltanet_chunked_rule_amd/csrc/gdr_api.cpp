@@ -43,8 +43,12 @@ struct Problem {
 
 struct Layout {
   size_t cu = 0, chunk_off = 0, seg_off = 0, gcum = 0, cert = 0, W = 0, U = 0, vnew = 0, hbuf = 0;
-  size_t A = 0, dhbuf = 0, dvn = 0, segtr = 0, hstart = 0, total = 0;
+  size_t A = 0, dhbuf = 0, dvn = 0, segtr = 0, hstart = 0, Au = 0, total = 0;
 };
+
+// The bf16 forward stages A diag(beta) per chunk and V, and forms Vnew from
+// them inside the fused pass, instead of a W and U round trip through HBM.
+bool forward_apath(const Problem& P, bool bwd) { return !bwd && P.dt == gdr::DType::BF16; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -187,8 +191,12 @@ Layout layout(const Problem& P, bool bwd) {
   Lo.seg_off = take(nn * 4);
   Lo.gcum = take(hv * tt * 4);
   Lo.cert = take(hv * nt * 4);
-  Lo.W = take(hv * tt * P.K * P.esize);
-  Lo.U = take(hv * tt * P.V * P.esize);
+  if (forward_apath(P, bwd)) {
+    Lo.Au = take(hv * tt * kChunk * 2);
+  } else {
+    Lo.W = take(hv * tt * P.K * P.esize);
+    Lo.U = take(hv * tt * P.V * P.esize);
+  }
   if (bwd) {
     Lo.vnew = take(hv * tt * P.V * P.esize);
     Lo.hbuf = take(hv * nt * P.V * P.K * P.esize);
@@ -246,7 +254,9 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     ip.gcum = reinterpret_cast<float*>(ws + Lo.gcum);
     ip.g_cum_out = g_cum_out;
     ip.cert = reinterpret_cast<float*>(ws + Lo.cert);
-    ip.W = ws + Lo.W; ip.U = ws + Lo.U;
+    const bool ap = forward_apath(P, bwd);
+    ip.W = ap ? nullptr : ws + Lo.W; ip.U = ap ? nullptr : ws + Lo.U;
+    ip.Au = ap ? ws + Lo.Au : nullptr;
     ip.A_ws = A_ws; ip.A_bf = A_bf; ip.A_out = A_out; ip.A_in = A_in;
     if ((e = gdr::launch_intra(P.dt, P.K, ip, st)) != hipSuccess) return hip_fail(e, "intra launch");
   }
@@ -257,6 +267,7 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     // the same pass storing every chunk's entry state and Vnew instead
     gdr::FusedParams fp;
     fp.s = s; fp.q = q; fp.k = k; fp.W = ws + Lo.W; fp.U = ws + Lo.U;
+    fp.v = v; fp.Au = forward_apath(P, bwd) ? ws + Lo.Au : nullptr;
     fp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
     fp.cert = reinterpret_cast<const float*>(ws + Lo.cert);
     fp.h0 = h0; fp.ht = ht; fp.o = o;

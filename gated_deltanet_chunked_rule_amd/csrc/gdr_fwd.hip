@@ -213,7 +213,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
     const int len = it.ok ? it.len : 0;
     const int t0 = it.ok ? it.t0 : 0;
     rk.load((const T*)p.k + ((long)t0 * p.Hq + it.hk) * KD, (long)p.Hq * KD, len);
-    rv.load((const T*)p.v + ((long)t0 * p.Hv + it.h) * VD, (long)p.Hv * VD, len);
+    rv.load((const T*)p.v + ((long)t0 * p.Hv + it.h) * VD, (long)p.Hv * VD, p.Au ? 0 : len);
     const rsrc_t gr = make_rsrc(p.g + (long)t0 * p.Hv + it.h, (long)len * p.Hv * 4);
     const rsrc_t br = make_rsrc(p.beta + (long)t0 * p.Hv + it.h, (long)len * p.Hv * 4);
     gv = buf_load_f32(gr, (uint32_t)(l * p.Hv) * 4u);
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
       }
     }
     rk.template store_perm<PK>(sK);
-    rv.template store_perm<PK>(sV);
+    if (!p.Au) rv.template store_perm<PK>(sV);
     lds_barrier();
     fetch(nx, rkn, rvn, gvn, bvn);
 
@@ -388,6 +388,21 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
     for (int j = 0; j < 4; ++j) {
       su[j] = sB[16 * j + t];
       sw[j] = su[j] * __expf(sG[16 * j + t]);
+    }
+    if (p.Au) {   // A'' rows (bf16) for the fused pass, which forms Vnew = A''(V - Gamma K h) itself
+      if constexpr (!F32) {
+        const f32x4 av[4] = {a0, a1, a2, a3};
+        const int r = 16 * rb + 4 * q + (t & 3);   // after the in-quad transpose: row r, columns 16j + 4(t/4) ..
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 v = av[j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= su[j];
+          const uint2 u = pack4_bf16(quad_t(v));
+          if (r < len) *reinterpret_cast<uint2*>((bf16*)p.Au + ((long)h * s.Ttot + t0 + r) * CH + 16 * j + 4 * (t >> 2)) = u;
+        }
+      }
+      return;
     }
     lds_barrier();
     const int nks = F32 ? 4 * (rb + 1) : (rb + 2) / 2;  // contraction steps (A' is zero beyond 16(rb+1))
@@ -653,11 +668,12 @@ struct FusedBufs {   // one buffer of staged chunk inputs
   float *G, *D;      // gate cumsums; per-row factors {e^{gamma_n - gamma_t}, s e^{gamma_t}}
 };
 
-// MODE: 0 the output pass, 1 the backward's states pass, 2 the segment
-// transitions (separate instantiations, so each keeps only its own paths).
+// MODE: 0 the output pass, 1 the backward's states pass, 2 the forward's
+// segment transitions, 3 the backward's (separate instantiations, so each
+// keeps only its own paths).
 template <typename T, int KD, int MODE>
 __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
-  constexpr bool TRANS = MODE == 2;
+  constexpr bool TRANS = MODE >= 2;
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
   constexpr int VEC = 16 / (int)sizeof(T);
@@ -668,10 +684,14 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   constexpr int NWV = NCB < FNW ? NCB : FNW;       // waves owning state columns
   constexpr int CBW = NCB / NWV;                   // column tiles per owning wave
   static_assert(CBW == 1, "one column tile per wave");
-  __shared__ __align__(16) T sW0[TE], sQ0[TE], sK0[TE], sU0[TE], sW1[TE], sQ1[TE], sK1[TE], sU1[TE];
+  // bf16 output and transition passes stage A'' = A diag(beta) (64 x 64) and
+  // V instead of W and U, and form Vnew = A''(V - Gamma * K h) themselves.
+  constexpr bool AP = !F32 && (MODE == 0 || MODE == 2);
+  constexpr int TW = AP ? CH * CH : TE;
+  __shared__ __align__(16) T sW0[TW], sQ0[TE], sK0[TE], sU0[TE], sW1[TW], sQ1[TE], sK1[TE], sU1[TE];
   __shared__ __align__(16) T sP[CH * PP];
   __shared__ __align__(16) T sO[F32 ? 8 : TE];     // bf16 output rows (fp32 stores directly)
-  __shared__ float sG0[CH], sG1[CH], sD0[2 * CH], sD1[2 * CH];
+  __shared__ __align__(16) float sG0[CH], sG1[CH], sD0[3 * CH], sD1[3 * CH];
   if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
     const T z = from_f<T>(0.f);
     sW0[threadIdx.x] = z; sQ0[threadIdx.x] = z; sK0[threadIdx.x] = z; sU0[threadIdx.x] = z;
@@ -766,7 +786,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   // no wave stalls long on a full memory queue.  The per-lane byte offsets within a tile do not
   // depend on the chunk.
   constexpr int NCP = (NCH + FNW - 1) / FNW;   // copy instructions per wave and tile
-  uint32_t off_wu[NCP], off_qk[NCP];
+  uint32_t off_wu[NCP], off_qk[NCP], off_v[NCP], off_a[1];
 #pragma unroll
   for (int j = 0; j < NCP; ++j) {
     const int i = w + FNW * j;
@@ -774,16 +794,30 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const int r = pidx / NCH, c = (pidx % NCH) ^ stage_swz<NCH>(r);
     off_wu[j] = (uint32_t)(r * KD * (int)sizeof(T) + c * 16);
     off_qk[j] = (uint32_t)(r * p.Hq * KD * (int)sizeof(T) + c * 16);
+    off_v[j] = (uint32_t)(r * p.Hv * VD * (int)sizeof(T) + c * 16);
   }
+  {  // the 64-wide A'' tile: eight 1 KB blocks, one per wave
+    const int pidx = 64 * w + l;
+    const int r = pidx >> 3, c = (pidx & 7) ^ stage_swz<8>(r);
+    off_a[0] = (uint32_t)(r * CH * 2 + c * 16);
+  }
+  auto tix8 = [](int r, int c) { return (r * 8 + ((c >> 3) ^ stage_swz<8>(r))) * 8 + (c & 7); };
   auto copy_part = [&](int jc, auto bc, int piece) __attribute__((always_inline)) {
     const FusedBufs<T> bf = bufs(bc);
     const int t0 = seq0 + jc * CH;
     const int len = min(CH, seq1 - t0);
     const long wbytes = (long)len * KD * (long)sizeof(T), qbytes = wbytes * p.Hq;
-    if (piece == 0)
-      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
-    if (piece == 1 && !no_u)
-      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, make_rsrc((const T*)p.U + ((long)h * s.Ttot + t0) * VD, wbytes), off_wu, w);
+    if constexpr (AP) {
+      if (piece == 0)
+        lds_copy_tile<1, 8, FNW, 8>(bf.W, make_rsrc((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, (long)len * CH * 2), off_a, w);
+      if (piece == 1 && !no_u)
+        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, make_rsrc((const T*)p.v + ((long)t0 * p.Hv + h) * VD, wbytes * p.Hv), off_v, w);
+    } else {
+      if (piece == 0)
+        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
+      if (piece == 1 && !no_u)
+        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, make_rsrc((const T*)p.U + ((long)h * s.Ttot + t0) * VD, wbytes), off_wu, w);
+    }
     if (piece == 2)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
     if (piece == 3) {
@@ -811,6 +845,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       const float gl = bf.G[max(ln, 1) - 1], gv = bf.G[l];
       bf.D[l] = (l < ln) ? __expf(gl - gv) : 0.f;
       bf.D[CH + l] = p.scale * __expf(gv);
+      bf.D[2 * CH + l] = __expf(gv);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt = 0
     }
     __builtin_amdgcn_s_barrier();
@@ -948,7 +983,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
         for (int ks = 0; ks < KD / 32; ++ks) {
           bf16x8 aw[4], aq[4], hb[CBW];
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) aw[tt] = *reinterpret_cast<const bf16x8*>(sW + tix(16 * tt + t, 32 * ks + 8 * q));
+          for (int tt = 0; tt < 4; ++tt) aw[tt] = *reinterpret_cast<const bf16x8*>((AP ? sK : sW) + tix(16 * tt + t, 32 * ks + 8 * q));
           if (!warm) {
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) aq[tt] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * tt + t, 32 * ks + 8 * q));
@@ -984,6 +1019,30 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 #pragma unroll
           for (int cb = 0; cb < CBW; ++cb) uv[tt][e][cb] = no_u ? 0.f : uv[tt][e][cb];  // U tile not copied for M
         }
+      if constexpr (AP) {   // vn holds K h: Vnew = A''(V - Gamma * K h), A'' lower triangular
+        const float* sGa = sD + 2 * CH;
+        f32x4 xv[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const f32x4 ga = *reinterpret_cast<const f32x4*>(sGa + 16 * tt + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[tt][e] = uv[tt][e][0] - ga[e] * vn[tt][0][e];
+        }
+        const bf16x8 xb[2] = {pack_b(xv[0], xv[1]), pack_b(xv[2], xv[3])};
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          vn[tt][0] = zero4();
+#pragma unroll
+          for (int ks = 0; ks <= tt / 2; ++ks) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(sW + tix8(16 * tt + t, 32 * ks + 4 * q));
+            const uint2 hi = *reinterpret_cast<const uint2*>(sW + tix8(16 * tt + t, 32 * ks + 16 + 4 * q));
+            bf16x8 a;
+            __builtin_memcpy(&a, &lo, 8);
+            __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+            vn[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[ks], vn[tt][0], 0, 0, 0);
+          }
+        }
+      }
       f32x4 vd[4][CBW];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -994,7 +1053,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           const float gm = sM[r];
 #pragma unroll
           for (int cb = 0; cb < CBW; ++cb) {
-            vn[tt][cb][e] = uv[tt][e][cb] - vn[tt][cb][e];
+            if constexpr (!AP) vn[tt][cb][e] = uv[tt][e][cb] - vn[tt][cb][e];
             vd[tt][cb][e] = vn[tt][cb][e] * d;
             oa[tt][cb][e] *= gm;
           }
@@ -1263,8 +1322,15 @@ template <typename T, int KD>
 static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t st) {
   const int total = total_segs * p.Hv * (p.trans ? 2 : 1);
   const bool states = p.hbuf != nullptr && !p.trans;
+  // bf16 output and forward transition passes read A diag(beta) and V; the
+  // backward's passes read W and U
+  constexpr bool F32 = std::is_same<T, float>::value;
+  const bool apath = !F32 && !states && p.Au != nullptr;
+  if (!F32 && !states && !p.trans && !apath) return hipErrorInvalidValue;
+  if (apath ? (p.v == nullptr) : (p.W == nullptr || p.U == nullptr)) return hipErrorInvalidValue;
   timing_before(p.trans ? "cp_transition" : states ? "chunk_states" : "chunk_fused", st);
-  if (p.trans) hipLaunchKernelGGL((k_fused<T, KD, 2>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  if (p.trans && apath) hipLaunchKernelGGL((k_fused<T, KD, 2>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  else if (p.trans) hipLaunchKernelGGL((k_fused<T, KD, 3>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
   else if (states) hipLaunchKernelGGL((k_fused<T, KD, 1>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
   else hipLaunchKernelGGL((k_fused<T, KD, 0>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
   hipError_t err = hipGetLastError();

@@ -35,50 +35,6 @@
 
 namespace gdr {
 
-// Sum over the 16 lanes of a DPP row (the lanes sharing lane / 16), on the
-// VALU: quad swaps, then the mirrored half-row, then the mirrored row.
-template <int C>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), C, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f<0xB1>(x);    // quad_perm [1, 0, 3, 2]
-  x += dpp_f<0x4E>(x);    // quad_perm [2, 3, 0, 1]
-  x += dpp_f<0x141>(x);   // row_half_mirror
-  x += dpp_f<0x140>(x);   // row_mirror
-  return x;
-}
-
-// 4 x 4 transpose within each quad of lanes: on entry lane 4k + i holds
-// x[e] = M[e][i]; on exit x[c] = M[i][c].  Accumulator tiles then give each
-// lane four consecutive columns of one row (8-byte bf16 stores).
-__device__ __forceinline__ f32x4 quad_t(f32x4 x) {
-  const int i = lane_id() & 3;
-  {
-    const bool odd = (i & 1) != 0;
-    float s0 = odd ? x[0] : x[1], s1 = odd ? x[2] : x[3];
-    s0 = dpp_f<0xB1>(s0);
-    s1 = dpp_f<0xB1>(s1);
-    if (odd) { x[0] = s0; x[2] = s1; } else { x[1] = s0; x[3] = s1; }
-  }
-  {
-    const bool hi = (i & 2) != 0;
-    float s0 = hi ? x[0] : x[2], s1 = hi ? x[1] : x[3];
-    s0 = dpp_f<0x4E>(s0);
-    s1 = dpp_f<0x4E>(s1);
-    if (hi) { x[0] = s0; x[1] = s1; } else { x[2] = s0; x[3] = s1; }
-  }
-  return x;
-}
-__device__ __forceinline__ uint2 pack4_bf16(f32x4 x) {
-  bf16x4 b;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) b[c] = static_cast<bf16>(x[c]);
-  uint2 u;
-  __builtin_memcpy(&u, &b, 8);
-  return u;
-}
-
 template <int KD>
 __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, int per_wg) {
   using T = bf16;
@@ -88,7 +44,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   __shared__ __align__(16) T sQ[TE], sK[TE], sdO[TE], sVn[TE], sdVn[TE], sV[TE], sW[TE];
   __shared__ __align__(16) T sA2[2][TE8], sPD[TE8];
   __shared__ __align__(16) float sGc[2][CH], sBe[2][CH];
-  __shared__ float sGam[CH], sGm[CH], sDec[CH], sBt[CH];
+  __shared__ __align__(16) float sGam[CH], sGm[CH], sDec[CH], sBt[CH];
   __shared__ float sRowP[FNW][CH], sColP[FNW][CH], sDbP[FNW][CH], sRed[2][FNW];
   if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
     const T z = from_f<T>(0.f);

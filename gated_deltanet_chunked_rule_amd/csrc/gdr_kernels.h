@@ -50,6 +50,8 @@ struct IntraParams {
   void *W, *U;
   float* A_ws;               // nullable, [Hv][Ttot][64]
   void* A_bf;                // nullable, bf16 [Hv][Ttot][64] (the per-chunk gradient kernel's copy)
+  void* Au;                  // non-null (bf16 forward): store A diag(beta) rows [Hv][Ttot][64]
+                             //   instead of W and U (V is then not read)
   float* A_out;              // nullable, [Ttot][Hv][64]
   const float* A_in;         // nullable: use this A ([Ttot][Hv][64]) instead of inverting
 };
@@ -71,6 +73,7 @@ struct StateParams {
 struct FusedParams {         // forward state recurrence fused with the output
   SeqTables s;
   const void *q, *k, *W, *U;
+  const void *v, *Au;        // bf16 output / transition passes: V and A diag(beta) rows instead of W, U
   const float *gcum, *cert;
   const float* h0;           // nullable [N][Hv][K][V]
   float* ht;                 // nullable [N][Hv][K][V]
