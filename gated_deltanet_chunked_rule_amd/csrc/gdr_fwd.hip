@@ -157,8 +157,11 @@ __device__ __forceinline__ void kk_tile(int w, int n, int& i, int& j) {
   else { i = 3; j = 2 + n; }
 }
 
-template <typename T, int KD>
-__global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_items, int per_wg, int nwg) {
+// AM: the bf16 forward's mode, storing A diag(beta) rows instead of W and U
+// (no V tile, no W/U products: smaller LDS and register footprint, four
+// workgroups per CU).
+template <typename T, int KD, bool AM>
+__global__ __launch_bounds__(NTHR, AM ? 4 : 3) void k_intra(IntraParams p, int total_items, int per_wg, int nwg) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
   constexpr int NT = KD / 16;                 // column tiles of W and U
@@ -170,13 +173,14 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
   constexpr int SZ_AT = 2 * CH * PA * (int)sizeof(T);
   constexpr int SZ_X = F32 ? SZ_AT : 0;       // fp32: A' / A'' cannot overlay the fp32 tiles
   static_assert(F32 || SZ_AT <= SZ_F, "A' and A'' must fit over the fp32 tiles");
-  __shared__ __align__(16) char smem[2 * SZ_K + SZ_F + SZ_X];
+  constexpr int NKV = AM ? 1 : 2;             // staged row tiles: K (and V)
+  __shared__ __align__(16) char smem[NKV * SZ_K + SZ_F + SZ_X];
   __shared__ float sG[CH], sB[CH];
   __shared__ int sFlag[NWAVE];
   T* sK = reinterpret_cast<T*>(smem);
-  T* sV = reinterpret_cast<T*>(smem + SZ_K);
-  float* sF = reinterpret_cast<float*>(smem + 2 * SZ_K);
-  T* sAw = reinterpret_cast<T*>(smem + 2 * SZ_K + (F32 ? SZ_F : 0));  // A'^T  [token j][token i]
+  T* sV = reinterpret_cast<T*>(smem + (NKV - 1) * SZ_K);
+  float* sF = reinterpret_cast<float*>(smem + NKV * SZ_K);
+  T* sAw = reinterpret_cast<T*>(smem + NKV * SZ_K + (F32 ? SZ_F : 0));  // A'^T  [token j][token i]
   T* sAu = sAw + CH * PA;                                              // A''^T
 
   const SeqTables& s = p.s;
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
     const int len = it.ok ? it.len : 0;
     const int t0 = it.ok ? it.t0 : 0;
     rk.load((const T*)p.k + ((long)t0 * p.Hq + it.hk) * KD, (long)p.Hq * KD, len);
-    rv.load((const T*)p.v + ((long)t0 * p.Hv + it.h) * VD, (long)p.Hv * VD, p.Au ? 0 : len);
+    if constexpr (!AM) rv.load((const T*)p.v + ((long)t0 * p.Hv + it.h) * VD, (long)p.Hv * VD, len);
     const rsrc_t gr = make_rsrc(p.g + (long)t0 * p.Hv + it.h, (long)len * p.Hv * 4);
     const rsrc_t br = make_rsrc(p.beta + (long)t0 * p.Hv + it.h, (long)len * p.Hv * 4);
     gv = buf_load_f32(gr, (uint32_t)(l * p.Hv) * 4u);
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
       }
     }
     rk.template store_perm<PK>(sK);
-    if (!p.Au) rv.template store_perm<PK>(sV);
+    if constexpr (!AM) rv.template store_perm<PK>(sV);
     lds_barrier();
     fetch(nx, rkn, rvn, gvn, bvn);
 
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
       su[j] = sB[16 * j + t];
       sw[j] = su[j] * __expf(sG[16 * j + t]);
     }
-    if (p.Au) {   // A'' rows (bf16) for the fused pass, which forms Vnew = A''(V - Gamma K h) itself
+    if constexpr (AM) {   // A'' rows (bf16) for the fused pass, which forms Vnew = A''(V - Gamma K h) itself
       if constexpr (!F32) {
         const f32x4 av[4] = {a0, a1, a2, a3};
         const int r = 16 * rb + 4 * q + (t & 3);   // after the in-quad transpose: row r, columns 16j + 4(t/4) ..
@@ -981,24 +985,25 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       } else {
 #pragma unroll
         for (int ks = 0; ks < KD / 32; ++ks) {
-          bf16x8 aw[4], aq[4], hb[CBW];
+          bf16x8 aw[4], hb[CBW];
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) aw[tt] = *reinterpret_cast<const bf16x8*>((AP ? sK : sW) + tix(16 * tt + t, 32 * ks + 8 * q));
-          if (!warm) {
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) aq[tt] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * tt + t, 32 * ks + 8 * q));
-          }
 #pragma unroll
           for (int cb = 0; cb < CBW; ++cb) hb[cb] = pack_b(hs[2 * ks][cb], hs[2 * ks + 1][cb]);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int cb = 0; cb < CBW; ++cb) vn[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[tt], hb[cb], vn[tt][cb], 0, 0, 0);
-          if (!warm) {
+        }
+        if (!warm) {   // Q h after K h: its products fill the K h -> Vnew latency
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
+          for (int ks = 0; ks < KD / 32; ++ks) {
+            bf16x8 aq[4];
+            const bf16x8 hb = pack_b(hs[2 * ks][0], hs[2 * ks + 1][0]);
 #pragma unroll
-              for (int cb = 0; cb < CBW; ++cb) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[tt], hb[cb], oa[tt][cb], 0, 0, 0);
+            for (int tt = 0; tt < 4; ++tt) aq[tt] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * tt + t, 32 * ks + 8 * q));
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) oa[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[tt], hb, oa[tt][0], 0, 0, 0);
           }
         }
       }
@@ -1301,11 +1306,19 @@ static unsigned padded_grid(long total) { return (unsigned)(((total + 7) / 8) * 
 template <typename T, int KD>
 static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
   hipError_t err;
-  // persistent grid: three workgroups per CU, each over a contiguous item range
+  // persistent grid: three (A diag(beta) mode: four) workgroups per CU, each
+  // over a contiguous item range
+  constexpr bool BF = std::is_same<T, bf16>::value;
+  const bool am = BF && p.Au != nullptr;
+  if (p.Au ? !BF : (p.W == nullptr || p.U == nullptr)) return hipErrorInvalidValue;
   const long total = (long)p.s.NTtot * p.Hv;
-  const int nwg = (int)std::min<long>(padded_grid(total), 3 * 256);
+  const int nwg = (int)std::min<long>(padded_grid(total), (am ? 4 : 3) * 256);
   const int per_wg = (int)((total + nwg - 1) / nwg);
-  GDR_LAUNCH("intra_wy", (k_intra<T, KD>), dim3(nwg), st, p, (int)total, per_wg, nwg);
+  if (am) {
+    GDR_LAUNCH("intra_wy", (k_intra<T, KD, BF>), dim3(nwg), st, p, (int)total, per_wg, nwg);
+  } else {
+    GDR_LAUNCH("intra_wy", (k_intra<T, KD, false>), dim3(nwg), st, p, (int)total, per_wg, nwg);
+  }
   return err;
 }
 
