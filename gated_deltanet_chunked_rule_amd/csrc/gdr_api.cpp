@@ -46,9 +46,10 @@ struct Layout {
   size_t A = 0, dhbuf = 0, dvn = 0, segtr = 0, hstart = 0, Au = 0, total = 0;
 };
 
-// The bf16 forward stages A diag(beta) per chunk and V, and forms Vnew from
-// them inside the fused pass, instead of a W and U round trip through HBM.
-bool forward_apath(const Problem& P, bool bwd) { return !bwd && P.dt == gdr::DType::BF16; }
+// bf16 stages A diag(beta) per chunk and V, and forms Vnew (and, in the
+// backward's reverse pass, W^T dVnew) from them, instead of a W and U round
+// trip through HBM; fp32 keeps W and U.
+bool apath(const Problem& P) { return P.dt == gdr::DType::BF16; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -191,7 +192,7 @@ Layout layout(const Problem& P, bool bwd) {
   Lo.seg_off = take(nn * 4);
   Lo.gcum = take(hv * tt * 4);
   Lo.cert = take(hv * nt * 4);
-  if (forward_apath(P, bwd)) {
+  if (apath(P)) {
     Lo.Au = take(hv * tt * kChunk * 2);
   } else {
     Lo.W = take(hv * tt * P.K * P.esize);
@@ -254,7 +255,7 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     ip.gcum = reinterpret_cast<float*>(ws + Lo.gcum);
     ip.g_cum_out = g_cum_out;
     ip.cert = reinterpret_cast<float*>(ws + Lo.cert);
-    const bool ap = forward_apath(P, bwd);
+    const bool ap = apath(P);
     ip.W = ap ? nullptr : ws + Lo.W; ip.U = ap ? nullptr : ws + Lo.U;
     ip.Au = ap ? ws + Lo.Au : nullptr;
     ip.A_ws = A_ws; ip.A_bf = A_bf; ip.A_out = A_out; ip.A_in = A_in;
@@ -267,7 +268,7 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     // the same pass storing every chunk's entry state and Vnew instead
     gdr::FusedParams fp;
     fp.s = s; fp.q = q; fp.k = k; fp.W = ws + Lo.W; fp.U = ws + Lo.U;
-    fp.v = v; fp.Au = forward_apath(P, bwd) ? ws + Lo.Au : nullptr;
+    fp.v = v; fp.Au = apath(P) ? ws + Lo.Au : nullptr;
     fp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
     fp.cert = reinterpret_cast<const float*>(ws + Lo.cert);
     fp.h0 = h0; fp.ht = ht; fp.o = o;
@@ -416,7 +417,7 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
   hipError_t e;
   if (bwd_segmented(P)) {
     gdr::DFusedParams dp;
-    dp.s = s; dp.q = q; dp.k = k; dp.W = ws + Lo.W; dp.d_o = d_o;
+    dp.s = s; dp.q = q; dp.k = k; dp.Au = ws + Lo.Au; dp.d_o = d_o;
     dp.gcum = reinterpret_cast<const float*>(ws + Lo.gcum);
     dp.cert = reinterpret_cast<const float*>(ws + Lo.cert);
     dp.dht = dht; dp.dh0 = dh0; dp.dhbuf = ws + Lo.dhbuf; dp.dvn = ws + Lo.dvn;

@@ -190,7 +190,8 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
 //   kd  = K dh                             (dh as the MFMA B operand)
 //   dh <- Gamma_n dh + s (Gamma Q)^T dO    (Q^T by transposing LDS reads)
 //   dVn = s P^T dO + dec * kd,  dec_t = e^{gamma_n - gamma_t},  P = lower(D * Q K^T)
-//   dh <- dh - W^T dVn
+//   dh <- dh - W^T dVn = dh - K^T (Gamma * (A''^T dVn)),  W = A'' diag(Gamma) K,
+//         A'' = A diag(beta) (staged instead of W, as in the forward)
 // and dh entering the chunk (before the update) and dVn are stored for the
 // per-chunk gradients.  The dO terms do not depend on dh, so the map from a
 // segment's end gradient to its start gradient is affine with the forward
@@ -199,13 +200,13 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
 // final-state gradient when the window reaches the sequence end); other
 // heads run from exact end gradients (k_segscan, reverse mode), and with
 // trans = 1 compute the offsets d of their segments from a zero end
-// gradient (the last from the final-state gradient).  Q, K, W, dO and the
+// gradient (the last from the final-state gradient).  Q, K, A'', dO and the
 // gate cumsums are copied into LDS one chunk ahead as in k_fused; P^T is
 // stored with its token columns permuted as k_fused permutes P.
 template <typename T>
 struct DFusedBufs {   // one buffer of staged chunk inputs
-  T *W, *Q, *K, *O;
-  float *G, *D;       // gate cumsums; per-row factors {e^{gamma_n - gamma_t}, s e^{gamma_t}}
+  T *W, *Q, *K, *O;   // W: the A'' tile (64 x 64)
+  float *G, *D;       // gate cumsums; per-row factors {e^{gamma_n - gamma_t}, s e^{gamma_t}, e^{gamma_t}}
 };
 
 template <int KD, bool TRANS>
@@ -219,9 +220,9 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   constexpr int NKB = KD / 16, NCB = VD / 16;
   constexpr int NWV = NCB < FNW ? NCB : FNW;
   static_assert(NCB <= FNW && NKB % 2 == 0, "one column tile per wave, paired row tiles");
-  __shared__ __align__(16) T sW0[TE], sQ0[TE], sK0[TE], sO0[TE], sW1[TE], sQ1[TE], sK1[TE], sO1[TE];
+  __shared__ __align__(16) T sW0[CH * CH], sQ0[TE], sK0[TE], sO0[TE], sW1[CH * CH], sQ1[TE], sK1[TE], sO1[TE];
   __shared__ __align__(16) T sP[CH * PP];
-  __shared__ float sG0[CH], sG1[CH], sD0[2 * CH], sD1[2 * CH];
+  __shared__ __align__(16) float sG0[CH], sG1[CH], sD0[3 * CH], sD1[3 * CH];
   if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
     const T z = from_f<T>(0.f);
     sW0[threadIdx.x] = z; sQ0[threadIdx.x] = z; sK0[threadIdx.x] = z; sO0[threadIdx.x] = z;
@@ -284,23 +285,28 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   // Copies of chunk jc's tiles into buffer bc in four parts (0 W, 1 dO, 2 K,
   // 3 Q and the gate cumsums); rows past the chunk read as zero.
   constexpr int NCP = (NCH + FNW - 1) / FNW;
-  uint32_t off_w[NCP], off_qk[NCP], off_o[NCP];
+  uint32_t off_qk[NCP], off_o[NCP], off_a[1];
 #pragma unroll
   for (int j = 0; j < NCP; ++j) {
     const int i = w + FNW * j;
     const int pidx = 64 * i + l;
     const int r = pidx / NCH, c = (pidx % NCH) ^ stage_swz<NCH>(r);
-    off_w[j] = (uint32_t)(r * KD * (int)sizeof(T) + c * 16);
     off_qk[j] = (uint32_t)(r * p.Hq * KD * (int)sizeof(T) + c * 16);
     off_o[j] = (uint32_t)(r * p.Hv * VD * (int)sizeof(T) + c * 16);
   }
+  {  // the 64-wide A'' tile: eight 1 KB blocks, one per wave
+    const int pidx = 64 * w + l;
+    const int r = pidx >> 3, c = (pidx & 7) ^ stage_swz<8>(r);
+    off_a[0] = (uint32_t)(r * CH * 2 + c * 16);
+  }
+  auto tix8 = [](int r, int c) { return (r * 8 + ((c >> 3) ^ stage_swz<8>(r))) * 8 + (c & 7); };
   auto copy_part = [&](int jc, auto bc, int piece) __attribute__((always_inline)) {
     const DFusedBufs<T> bf = bufs(bc);
     const int t0 = seq0 + jc * CH;
     const int len = min(CH, seq1 - t0);
     const long rbytes = (long)len * KD * (long)sizeof(T);
     if (piece == 0)
-      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, rbytes), off_w, w);
+      lds_copy_tile<1, 8, FNW, 8>(bf.W, make_rsrc((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, (long)len * CH * 2), off_a, w);
     if (piece == 1)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.O, make_rsrc((const T*)p.d_o + ((long)t0 * p.Hv + h) * VD, rbytes * p.Hv), off_o, w);
     if (piece == 2)
@@ -328,6 +334,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
       const float gl = bf.G[max(ln, 1) - 1], gv = bf.G[l];
       bf.D[l] = (l < ln) ? __expf(gl - gv) : 0.f;
       bf.D[CH + l] = p.scale * __expf(gv);
+      bf.D[2 * CH + l] = __expf(gv);
       __builtin_amdgcn_s_waitcnt(0xC07F);
     }
     __builtin_amdgcn_s_barrier();
@@ -472,15 +479,39 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
             if (r < len) vb[(long)r * VD] = from_f<T>(dv[tt][e]);
           }
       }
+      // z = Gamma * (A''^T dVn), rows s in blocks st (A'' lower triangular)
+      f32x4 z[4];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {   // dh -= W^T dVn
+      for (int st = 0; st < 4; ++st) z[st] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bv = pack_b(dv[2 * ks], dv[2 * ks + 1]);
         const int ra = 32 * ks + 4 * q + (sl >> 2);
-        const bf16x8 bv = pack_b(-dv[2 * ks], -dv[2 * ks + 1]);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          if (2 * ks + 1 >= st) {
+            const int cs = 16 * st + 4 * (sl & 3);
+            const bf16x8 aa = cat4(trd(sW + tix8(ra, cs)), trd(sW + tix8(ra + 16, cs)));
+            z[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, bv, z[st], 0, 0, 0);
+          }
+        }
+      }
+      const float* sGa = sD + 2 * CH;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const f32x4 ga = *reinterpret_cast<const f32x4*>(sGa + 16 * st + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[st][e] *= -ga[e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {   // dh -= K^T z
+        const int ra = 32 * ks + 4 * q + (sl >> 2);
+        const bf16x8 bz = pack_b(z[2 * ks], z[2 * ks + 1]);
 #pragma unroll
         for (int rb = 0; rb < NKB; ++rb) {
           const int cc = 32 * (rb >> 1) + 8 * (sl & 3) + 4 * (rb & 1);
-          const bf16x8 aw = cat4(trd(sW + tix(ra, cc)), trd(sW + tix(ra + 16, cc)));
-          ds[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bv, ds[rb], 0, 0, 0);
+          const bf16x8 ak = cat4(trd(sK + tix(ra, cc)), trd(sK + tix(ra + 16, cc)));
+          ds[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bz, ds[rb], 0, 0, 0);
         }
       }
     }

@@ -688,9 +688,9 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   constexpr int NWV = NCB < FNW ? NCB : FNW;       // waves owning state columns
   constexpr int CBW = NCB / NWV;                   // column tiles per owning wave
   static_assert(CBW == 1, "one column tile per wave");
-  // bf16 output and transition passes stage A'' = A diag(beta) (64 x 64) and
-  // V instead of W and U, and form Vnew = A''(V - Gamma * K h) themselves.
-  constexpr bool AP = !F32 && (MODE == 0 || MODE == 2);
+  // bf16 passes stage A'' = A diag(beta) (64 x 64) and V instead of W and U,
+  // and form Vnew = A''(V - Gamma * K h) themselves.
+  constexpr bool AP = !F32;
   constexpr int TW = AP ? CH * CH : TE;
   __shared__ __align__(16) T sW0[TW], sQ0[TE], sK0[TE], sU0[TE], sW1[TW], sQ1[TE], sK1[TE], sU1[TE];
   __shared__ __align__(16) T sP[CH * PP];
@@ -1335,12 +1335,10 @@ template <typename T, int KD>
 static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t st) {
   const int total = total_segs * p.Hv * (p.trans ? 2 : 1);
   const bool states = p.hbuf != nullptr && !p.trans;
-  // bf16 output and forward transition passes read A diag(beta) and V; the
-  // backward's passes read W and U
+  // bf16 passes read A diag(beta) and V; fp32 passes read W and U
   constexpr bool F32 = std::is_same<T, float>::value;
-  const bool apath = !F32 && !states && p.Au != nullptr;
-  if (!F32 && !states && !p.trans && !apath) return hipErrorInvalidValue;
-  if (apath ? (p.v == nullptr) : (p.W == nullptr || p.U == nullptr)) return hipErrorInvalidValue;
+  const bool apath = !F32;
+  if (apath ? (p.Au == nullptr || p.v == nullptr) : (p.W == nullptr || p.U == nullptr)) return hipErrorInvalidValue;
   timing_before(p.trans ? "cp_transition" : states ? "chunk_states" : "chunk_fused", st);
   if (p.trans && apath) hipLaunchKernelGGL((k_fused<T, KD, 2>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
   else if (p.trans) hipLaunchKernelGGL((k_fused<T, KD, 3>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);

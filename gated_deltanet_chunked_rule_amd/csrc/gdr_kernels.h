@@ -91,7 +91,7 @@ struct FusedParams {         // forward state recurrence fused with the output
 
 struct DFusedParams {        // reverse state pass with CP segments (backward)
   SeqTables s;
-  const void *q, *k, *W, *d_o;
+  const void *q, *k, *Au, *d_o;   // Au: A diag(beta) rows [Hv][Ttot][64] (bf16)
   const float *gcum, *cert;
   const float* dht;          // nullable [N][Hv][K][V]
   float* dh0;                // nullable [N][Hv][K][V]
