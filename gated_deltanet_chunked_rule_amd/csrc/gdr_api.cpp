@@ -214,7 +214,8 @@ Layout layout(const Problem& P, bool bwd) {
   return Lo;
 }
 
-gdr::SeqTables tables(const Problem& P, const Layout& Lo, char* ws) {
+// L: the CP segment length of the passes that read the segment offsets.
+gdr::SeqTables tables(const Problem& P, const Layout& Lo, char* ws, int L) {
   gdr::SeqTables s;
   s.cu = reinterpret_cast<const int32_t*>(ws + Lo.cu);
   s.chunk_off = reinterpret_cast<const int32_t*>(ws + Lo.chunk_off);
@@ -223,6 +224,8 @@ gdr::SeqTables tables(const Problem& P, const Layout& Lo, char* ws) {
   s.Ttot = P.Ttot;
   s.NTtot = P.NTtot;
   s.T_uniform = P.packed ? 0 : P.T;
+  const int ntu = (P.T + kChunk - 1) / kChunk;
+  s.segs_uniform = std::max(1, (ntu + std::max(L, 1) - 1) / std::max(L, 1));
   return s;
 }
 
@@ -247,8 +250,9 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
   pp.cu = reinterpret_cast<int32_t*>(ws + Lo.cu);
   pp.chunk_off = reinterpret_cast<int32_t*>(ws + Lo.chunk_off);
   pp.seg_off = reinterpret_cast<int32_t*>(ws + Lo.seg_off);
-  if ((e = gdr::launch_plan(pp, st)) != hipSuccess) return hip_fail(e, "plan launch");
-  const gdr::SeqTables s = tables(P, Lo, ws);
+  const gdr::SeqTables s = tables(P, Lo, ws, L);
+  // uniform rows need no tables: every kernel derives them arithmetically
+  if (s.T_uniform <= 0 && (e = gdr::launch_plan(pp, st)) != hipSuccess) return hip_fail(e, "plan launch");
   if (P.NTtot > 0) {
     gdr::IntraParams ip;
     ip.s = s; ip.k = k; ip.v = v; ip.g = g; ip.beta = beta; ip.Hq = P.Hq; ip.Hv = P.Hv;
@@ -413,7 +417,7 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
                          nullptr, nullptr, nullptr, A_ws, A_bf, A, L, true, hs);
   if (st != GDR_OK) return st;
   if (P.NTtot == 0 && !dh0) return GDR_OK;
-  const gdr::SeqTables s = tables(P, Lo, ws);
+  const gdr::SeqTables s = tables(P, Lo, ws, L);
   hipError_t e;
   if (bwd_segmented(P)) {
     gdr::DFusedParams dp;

@@ -61,8 +61,8 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
   const int h = (u / p.nvb) % p.Hv;
   const int n = u / (p.nvb * p.Hv);
   if (n >= s.N) return;
-  const int c0 = s.chunk_off[n];
-  const int nch = s.chunk_off[n + 1] - c0;
+  const int c0 = s.chunk_at(n);
+  const int nch = s.chunk_at(n + 1) - c0;
   if (c0 < 0 || nch < 0 || c0 + nch > s.NTtot) return;
   const int hk = h / (p.Hv / p.Hq);
   const int w = wave_id(), l = lane_id();
@@ -83,8 +83,8 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
   float gam_next = 0.f, glast_next = 0.f;
   auto prefetch = [&](int jc) {  // unconditional; empty range before the first chunk
     const bool valid = jc >= 0;
-    const int t0 = s.cu[n] + max(jc, 0) * CH;
-    const int len = valid ? min(CH, s.cu[n + 1] - t0) : 0;
+    const int t0 = s.cu_at(n) + max(jc, 0) * CH;
+    const int len = valid ? min(CH, s.cu_at(n + 1) - t0) : 0;
     rq.load((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
     rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
     rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
@@ -98,8 +98,8 @@ __global__ __launch_bounds__(NTHR) void k_dstate(DStateParams p, int total_items
 
   for (int jc = nch - 1; jc >= 0; --jc) {
     const int gc = c0 + jc;
-    const int t0 = s.cu[n] + jc * CH;
-    const int len = min(CH, s.cu[n + 1] - t0);
+    const int t0 = s.cu_at(n) + jc * CH;
+    const int len = min(CH, s.cu_at(n + 1) - t0);
     if (len <= 0 || t0 < 0 || (long)t0 + len > s.Ttot) break;
     const float glast = glast_next, gam = gam_next;
     rq.template store<PK>(sQ);
@@ -240,13 +240,13 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   if (u >= total_items) return;
   const int h = u % p.Hv;
   const int item = u / p.Hv;
-  const int n = find_seq(s.seg_off, s.N, item);
-  const int pseg = item - s.seg_off[n];
-  const int nseg = s.seg_off[n + 1] - s.seg_off[n];
-  const int c0 = s.chunk_off[n];
-  const int nch = s.chunk_off[n + 1] - c0;
+  const int n = s.seq_of_seg(item);
+  const int pseg = item - s.seg_at(n);
+  const int nseg = s.seg_at(n + 1) - s.seg_at(n);
+  const int c0 = s.chunk_at(n);
+  const int nch = s.chunk_at(n + 1) - c0;
   if (pseg < 0 || pseg >= nseg || c0 < 0 || c0 + nch > s.NTtot) return;
-  const int seq0 = s.cu[n], seq1 = s.cu[n + 1];
+  const int seq0 = s.cu_at(n), seq1 = s.cu_at(n + 1);
   const int L = p.seg_chunks;
   const int hk = h / (p.Hv / p.Hq);
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15, sl = l & 15;
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   const int col = 16 * w + t;
   const bool certified =
       head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, true);
-  const int gseg = s.seg_off[n] + pseg;
+  const int gseg = s.seg_at(n) + pseg;
   const long hbase = ((long)n * p.Hv + h) * KD * VD;
   // chunks crs down to cbeg; those below cend are the segment's own
   int cbeg = pseg * L, cend = min(cbeg + L, nch), crs;

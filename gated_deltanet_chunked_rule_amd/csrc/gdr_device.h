@@ -444,17 +444,6 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return (id & 7) * per + (id >> 3);
 }
 
-// Finds the sequence n with off[n] <= c < off[n + 1] (off non-decreasing,
-// length N + 1); returns the last such n among empty sequences.
-__device__ __forceinline__ int find_seq(const int32_t* off, int N, int c) {
-  int lo = 0, hi = N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= c) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // ---- staged chunk tiles (the fused state kernels) ----
 // Staged tiles are unpadded: row r holds NCH 16-byte pieces, piece c stored
 // at position c ^ stage_swz(r), which keeps 8-byte fragment reads and the
@@ -582,9 +571,9 @@ __device__ __forceinline__ bool head_certified(const float* cert, int nseg, int 
 // Chunk c of the packed batch: its sequence n, first token t0 and length.
 __device__ __forceinline__ bool locate_chunk_b(const SeqTables& s, int c, int& n, int& t0, int& len) {
   if (c >= s.NTtot) return false;
-  n = find_seq(s.chunk_off, s.N, c);
-  t0 = s.cu[n] + (c - s.chunk_off[n]) * CH;
-  len = min(CH, s.cu[n + 1] - t0);
+  n = s.seq_of_chunk(c);
+  t0 = s.cu_at(n) + (c - s.chunk_at(n)) * CH;
+  len = min(CH, s.cu_at(n + 1) - t0);
   return len > 0 && t0 >= 0 && (long)t0 + len <= s.Ttot;
 }
 

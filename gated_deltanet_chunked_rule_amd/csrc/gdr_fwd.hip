@@ -81,9 +81,9 @@ __global__ __launch_bounds__(1024) void k_plan(PlanParams p) {
 // device tables disagree with the grid (then the workgroup writes nothing).
 __device__ __forceinline__ bool locate_chunk(const SeqTables& s, int c, int& n, int& t0, int& len) {
   if (c >= s.NTtot) return false;
-  n = find_seq(s.chunk_off, s.N, c);
-  t0 = s.cu[n] + (c - s.chunk_off[n]) * CH;
-  len = min(CH, s.cu[n + 1] - t0);
+  n = s.seq_of_chunk(c);
+  t0 = s.cu_at(n) + (c - s.chunk_at(n)) * CH;
+  len = min(CH, s.cu_at(n + 1) - t0);
   return len > 0 && t0 >= 0 && (long)t0 + len <= s.Ttot;
 }
 
@@ -499,11 +499,11 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
   const int vb = u % p.nvb;
   const int h = (u / p.nvb) % p.Hv;
   const int item = u / (p.nvb * p.Hv);
-  const int n = find_seq(s.seg_off, s.N, item);
-  const int pseg = item - s.seg_off[n];
-  const int nseg = s.seg_off[n + 1] - s.seg_off[n];
-  const int c0 = s.chunk_off[n];
-  const int nch = s.chunk_off[n + 1] - c0;
+  const int n = s.seq_of_seg(item);
+  const int pseg = item - s.seg_at(n);
+  const int nseg = s.seg_at(n + 1) - s.seg_at(n);
+  const int c0 = s.chunk_at(n);
+  const int nch = s.chunk_at(n + 1) - c0;
   if (pseg < 0 || pseg >= nseg || c0 < 0 || c0 + nch > s.NTtot) return;
   const int L = p.seg_chunks;
   const int hk = h / (p.Hv / p.Hq);
@@ -542,8 +542,8 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
   float glast_next = 0.f;
   auto prefetch = [&](int jc) {  // unconditional; empty range past the segment
     const bool valid = jc < cend;
-    const int t0 = s.cu[n] + min(jc, cend - 1) * CH;
-    const int len = valid ? min(CH, s.cu[n + 1] - t0) : 0;
+    const int t0 = s.cu_at(n) + min(jc, cend - 1) * CH;
+    const int len = valid ? min(CH, s.cu_at(n + 1) - t0) : 0;
     rw.load((const T*)p.W + ((long)h * s.Ttot + t0) * KD, KD, len);
     rk.load((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)p.Hq * KD, len);
     ru.load((const T*)p.U + ((long)h * s.Ttot + t0) * VD + vb * BV, VD, len);
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(NTHR) void k_state(StateParams p, int total_items) 
 
   for (int jc = cstart; jc < cend; ++jc) {
     const int gc = c0 + jc;
-    const int t0 = s.cu[n] + jc * CH;
-    const int len = min(CH, s.cu[n + 1] - t0);
+    const int t0 = s.cu_at(n) + jc * CH;
+    const int len = min(CH, s.cu_at(n + 1) - t0);
     const bool warm = jc < cbeg;
     const float glast = glast_next;
     rw.template store<PK>(sW);
@@ -716,13 +716,13 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   const int item2 = u / p.Hv;
   const int part = TRANS ? (item2 & 1) : 1;   // transition pass: 0 M, 1 b
   const int item = TRANS ? (item2 >> 1) : item2;
-  const int n = find_seq(s.seg_off, s.N, item);
-  const int pseg = item - s.seg_off[n];
-  const int nseg = s.seg_off[n + 1] - s.seg_off[n];
-  const int c0 = s.chunk_off[n];
-  const int nch = s.chunk_off[n + 1] - c0;
+  const int n = s.seq_of_seg(item);
+  const int pseg = item - s.seg_at(n);
+  const int nseg = s.seg_at(n + 1) - s.seg_at(n);
+  const int c0 = s.chunk_at(n);
+  const int nch = s.chunk_at(n + 1) - c0;
   if (pseg < 0 || pseg >= nseg || c0 < 0 || c0 + nch > s.NTtot) return;
-  const int seq0 = s.cu[n], seq1 = s.cu[n + 1];   // token range of the sequence
+  const int seq0 = s.cu_at(n), seq1 = s.cu_at(n + 1);   // token range of the sequence
   const int L = p.seg_chunks;
   const int hk = h / (p.Hv / p.Hq);
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
@@ -731,7 +731,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 
   const bool certified =
       head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0);
-  const int gseg = s.seg_off[n] + pseg;          // global segment index
+  const int gseg = s.seg_at(n) + pseg;          // global segment index
   const bool exact = !certified && p.hstart != nullptr;
   int cstart, cbeg, cend;
   bool write_final;
@@ -1222,16 +1222,16 @@ __global__ __launch_bounds__(KD * 4) void k_segscan(ScanParams p, int total_item
   if (u >= total_items) return;
   const int cb = u % NCB, h = (u / NCB) % p.Hv, n = u / (NCB * p.Hv);
   if (n >= s.N) return;
-  const int nseg = s.seg_off[n + 1] - s.seg_off[n];
-  const int c0 = s.chunk_off[n];
+  const int nseg = s.seg_at(n + 1) - s.seg_at(n);
+  const int c0 = s.chunk_at(n);
   const int L = p.seg_chunks;
   if (nseg <= 1 || c0 < 0) return;
-  const int nch = s.chunk_off[n + 1] - c0;
+  const int nch = s.chunk_at(n + 1) - c0;
   if (head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0))
     return;   // certified: the warmup path needs no start states
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
   const int col = 16 * cb + t, row0 = 16 * w + 4 * q;
-  const long head = (long)h * p.total_segs + s.seg_off[n];
+  const long head = (long)h * p.total_segs + s.seg_at(n);
   auto tr = [&](int sg, int part) { return p.segtr + ((head + sg) * 2 + part) * KD * VD; };
   auto load_m = [&](int sg, f32x4 (&a)[NKB]) {
     if (p.rev) {   // M^T: lane reads column 16w + t of M, rows 16rb + 4q .. +3

@@ -30,7 +30,29 @@ struct SeqTables {
   int N;
   long Ttot;                 // tokens in the packed batch
   int NTtot;                 // chunks (host count; device tables must agree)
-  int T_uniform;             // > 0: N rows of T_uniform tokens (no cu_seqlens)
+  int T_uniform;             // > 0: N rows of T_uniform tokens (no cu_seqlens); the
+  int segs_uniform;          //   tables are then arithmetic (segments per row) and never read
+
+  __device__ __forceinline__ int nt_uniform() const { return (T_uniform + 63) / 64; }
+  __device__ __forceinline__ int cu_at(int n) const { return T_uniform > 0 ? n * T_uniform : cu[n]; }
+  __device__ __forceinline__ int chunk_at(int n) const { return T_uniform > 0 ? n * nt_uniform() : chunk_off[n]; }
+  __device__ __forceinline__ int seg_at(int n) const { return T_uniform > 0 ? n * segs_uniform : seg_off[n]; }
+  // The sequence n with off[n] <= x < off[n + 1] (the last such n among empty
+  // sequences) for the chunk and segment offsets.
+  __device__ __forceinline__ static int search(const int32_t* off, int N, int x) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+  __device__ __forceinline__ int seq_of_chunk(int c) const {
+    return T_uniform > 0 ? min(c / nt_uniform(), N - 1) : search(chunk_off, N, c);
+  }
+  __device__ __forceinline__ int seq_of_seg(int i) const {
+    return T_uniform > 0 ? min(i / segs_uniform, N - 1) : search(seg_off, N, i);
+  }
 };
 
 struct PlanParams {
