@@ -369,11 +369,11 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
     const float* sM = cur.D + CH;
     const float glast = sG[len - 1];
     if (keep && owner) {   // gradient of the state leaving the chunk, [K][V] rows
-      T* db = (T*)p.dhbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD + col;
+      // 4x4 transposes within lane quads: one 8-byte row piece per lane and tile.
+      T* db = (T*)p.dhbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD + 16 * w + 4 * (t >> 2);
 #pragma unroll
       for (int rb = 0; rb < NKB; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) db[(long)krow(rb, e) * VD] = from_f<T>(ds[rb][e]);
+        *reinterpret_cast<uint2*>(db + (long)krow(rb, t & 3) * VD) = pack4_bf16(quad_t(ds[rb]));
     }
     {  // P tiles (the ten lower ones and the masked (0,1), (2,3)), stored transposed
       constexpr int TI[12] = {3, 3, 2, 2, 3, 3, 2, 1, 1, 0, 0, 2};
@@ -469,15 +469,14 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) dv[tt][e] += sD[16 * tt + acc_row(e)] * kd[tt][e];
-      if (keep) {   // dVn token rows
-        T* vb = (T*)p.dvn + ((long)h * s.Ttot + t0) * VD + col;
+      if (keep) {   // dVn token rows, 8-byte row pieces after quad transposes
+        T* vb = (T*)p.dvn + ((long)h * s.Ttot + t0) * VD + 16 * w + 4 * (t >> 2);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * tt + acc_row(e);
-            if (r < len) vb[(long)r * VD] = from_f<T>(dv[tt][e]);
-          }
+        for (int tt = 0; tt < 4; ++tt) {
+          const uint2 u = pack4_bf16(quad_t(dv[tt]));
+          const int r = 16 * tt + 4 * q + (t & 3);
+          if (r < len) *reinterpret_cast<uint2*>(vb + (long)r * VD) = u;
+        }
       }
       // z = Gamma * (A''^T dVn), rows s in blocks st (A'' lower triangular)
       f32x4 z[4];

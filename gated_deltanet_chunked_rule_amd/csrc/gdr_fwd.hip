@@ -872,6 +872,21 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   if (cstart < cend) copy_chunk(cstart, ic<0>());
   wait_copies(cstart, ic<0>());
 
+  // P tiles of this wave (rows of tile ti, columns of tile tj): the ten
+  // lower tiles and the upper tiles (0,1), (2,3) that the 32-token
+  // contraction steps read (masked to zero); waves 0-3 take two, waves 4-7 one.
+  const int pcnt = w < 4 ? 2 : 1;
+  int pti[2], ptj[2];
+  {
+    constexpr int TI[12] = {3, 3, 2, 2, 3, 3, 2, 1, 1, 0, 0, 2};
+    constexpr int TJ[12] = {0, 1, 0, 1, 2, 3, 2, 0, 1, 0, 1, 3};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int idx = w < 4 ? 2 * w + m : 8 + (w - 4);
+      pti[m] = TI[idx];
+      ptj[m] = TJ[idx];
+    }
+  }
   int prev_t0 = 0, prev_len = 0;
   bool prev_out = false;
   // One chunk from buffer bc, copying chunk jc + 1 into the other buffer;
@@ -898,34 +913,30 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const float* sM = cur.D + CH;
     const float glast = sG[len - 1];
     if (keep && owner) {   // entry state of the chunk, [K][V] rows
-      T* hb = (T*)p.hbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD + vcol(0);
+      T* hb = (T*)p.hbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD;
+      if constexpr (F32) {
 #pragma unroll
-      for (int rb = 0; rb < NKB; ++rb)
+        for (int rb = 0; rb < NKB; ++rb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hb[(long)(F32 ? 16 * rb + acc_row(e) : krow(rb, e)) * VD] = from_f<T>(hs[rb][0][e]);
+          for (int e = 0; e < 4; ++e) hb[(long)(16 * rb + acc_row(e)) * VD + vcol(0)] = hs[rb][0][e];
+      } else {
+        // A 4x4 transpose within each lane quad gives a lane one K row over
+        // the quad's four columns: one 8-byte store per tile.
+#pragma unroll
+        for (int rb = 0; rb < NKB; ++rb)
+          *reinterpret_cast<uint2*>(hb + (long)krow(rb, t & 3) * VD + 16 * w + 4 * (t >> 2)) =
+              pack4_bf16(quad_t(hs[rb][0]));
+      }
     }
 
-    if (!warm) {  // P tiles: rows of tile ti, columns of tile tj
-      // The ten lower tiles and the upper tiles (0,1), (2,3) that the
-      // 32-token contraction steps read (masked to zero): waves 0-3 take two,
-      // waves 4-7 one.
-      constexpr int TI[12] = {3, 3, 2, 2, 3, 3, 2, 1, 1, 0, 0, 2};
-      constexpr int TJ[12] = {0, 1, 0, 1, 2, 3, 2, 0, 1, 0, 1, 3};
-      const int cnt = w < 4 ? 2 : 1;
-      int ti[2], tj[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int idx = w < 4 ? 2 * w + m : 8 + (w - 4);
-        ti[m] = TI[idx];
-        tj[m] = TJ[idx];
-      }
+    if (!warm) {  // P tiles of this wave
       f32x4 pa[2] = {zero4(), zero4()};
       if constexpr (F32) {
 #pragma unroll
         for (int k0 = 0; k0 < KD; k0 += 4)
 #pragma unroll
           for (int m = 0; m < 2; ++m)
-            pa[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[tix(16 * ti[m] + t, k0 + q)], sK[tix(16 * tj[m] + t, k0 + q)],
+            pa[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[tix(16 * pti[m] + t, k0 + q)], sK[tix(16 * ptj[m] + t, k0 + q)],
                                                          pa[m], 0, 0, 0);
       } else {
 #pragma unroll
@@ -933,8 +944,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           bf16x8 fa[2], fb[2];
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            fa[m] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * ti[m] + t, k0 + 8 * q));
-            fb[m] = *reinterpret_cast<const bf16x8*>(sK + tix(16 * tj[m] + t, k0 + 8 * q));
+            fa[m] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * pti[m] + t, k0 + 8 * q));
+            fb[m] = *reinterpret_cast<const bf16x8*>(sK + tix(16 * ptj[m] + t, k0 + 8 * q));
           }
 #pragma unroll
           for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[m], pa[m], 0, 0, 0);
@@ -942,13 +953,28 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        if (m < cnt) {
+        if (m < pcnt) {
+          // Masked scaled decays (selects, no branches); the gate cumsums of
+          // the lane's four rows are one 16-byte read.
+          const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
+          const f32x4 gr = *reinterpret_cast<const f32x4*>(sG + r0);
+          const float gc = sG[c];
+          f32x4 pv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 16 * ti[m] + acc_row(e), c = 16 * tj[m] + acc_col();
-            const float v = (r >= c && r < len) ? p.scale * __expf(sG[r] - sG[c]) * pa[m][e] : 0.f;
-            const int pc = F32 ? c : (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
-            sP[r * PP + pc] = from_f<T>(v);
+            const float x = p.scale * __expf(gr[e] - gc) * pa[m][e];
+            pv[e] = (r0 + e >= c && r0 + e < len) ? x : 0.f;
+          }
+          if constexpr (F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sP[(r0 + e) * PP + c] = pv[e];
+          } else {
+            // Quad transpose: a lane gets one row over four consecutive
+            // columns, which the column permutation keeps adjacent (one
+            // 8-byte store).
+            const int rr = r0 + (t & 3), cc = 16 * ptj[m] + 4 * (t >> 2);
+            const int pc = (cc & ~31) + 8 * ((cc >> 2) & 3) + 4 * ((cc >> 4) & 1);
+            *reinterpret_cast<uint2*>(sP + rr * PP + pc) = pack4_bf16(quad_t(pv));
           }
         }
       }
@@ -1064,14 +1090,23 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           }
         }
       if (keep) {   // Vnew token rows
-        T* vb = (T*)p.vnew + ((long)h * s.Ttot + t0) * VD + vcol(0);
+        T* vb = (T*)p.vnew + ((long)h * s.Ttot + t0) * VD;
+        if constexpr (F32) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+          for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * tt + acc_row(e);
-            if (r < len) vb[(long)r * VD] = from_f<T>(vn[tt][0][e]);
+            for (int e = 0; e < 4; ++e) {
+              const int r = 16 * tt + acc_row(e);
+              if (r < len) vb[(long)r * VD + vcol(0)] = vn[tt][0][e];
+            }
+        } else {   // quad transposes as for the entry state: 8-byte row pieces
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const uint2 u = pack4_bf16(quad_t(vn[tt][0]));
+            const int r = 16 * tt + 4 * q + (t & 3);
+            if (r < len) *reinterpret_cast<uint2*>(vb + (long)r * VD + 16 * w + 4 * (t >> 2)) = u;
           }
+        }
       }
       // h' = Gamma_n h + K^T (d * Vnew).
       const float gn = __expf(glast);
