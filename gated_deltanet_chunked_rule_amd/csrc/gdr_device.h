@@ -463,11 +463,17 @@ __device__ __forceinline__ int stage_swz(int r) {
 // kernels that use these wait for the copies themselves (vmcnt(0)) before
 // the barrier that publishes the data; nothing else in them uses M0.
 typedef int i32x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4v rsrc_words(rsrc_t r) {   // wave-uniform, in SGPRs
+// Words of the buffer descriptor that make_rsrc(base, bytes) describes (base
+// address, stride 0, byte range, flags), built in wave-uniform registers for
+// the inline-assembly copies.  (Taking them from an rsrc_t value goes through
+// private memory, which the compiler then places in LDS, one slot per thread.)
+__device__ __forceinline__ i32x4v rsrc_words(const void* base, long bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
   i32x4v v;
-  __builtin_memcpy(&v, &r, 16);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  v[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  v[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  v[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  v[3] = kBufWord3;
   return v;
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -484,8 +490,7 @@ __device__ __forceinline__ void lds_copy4(i32x4v rsrc, uint32_t voff, uint32_t l
 // instruction j fills the 1 KB block w + 8j of the tile; off[j] is this
 // lane's byte offset in the source (rows past the descriptor range read 0).
 template <int NCP, int NCH, int FNWV, int VEC, typename T>
-__device__ __forceinline__ void lds_copy_tile(T* dst, rsrc_t rr, const uint32_t* off, int w) {
-  const i32x4v rv = rsrc_words(rr);
+__device__ __forceinline__ void lds_copy_tile(T* dst, i32x4v rv, const uint32_t* off, int w) {
 #pragma unroll
   for (int j = 0; j < NCP; ++j) {
     const int i = w + FNWV * j;

@@ -726,7 +726,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   const int L = p.seg_chunks;
   const int hk = h / (p.Hv / p.Hq);
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
-  const bool owner = w < NWV;
+  const bool owner = NWV == FNW || w < NWV;   // a constant when every wave owns columns
   auto vcol = [&](int cb) { return CBW == 2 ? 32 * w + 2 * t + cb : 16 * w + t; };
 
   const bool certified =
@@ -813,23 +813,23 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const long wbytes = (long)len * KD * (long)sizeof(T), qbytes = wbytes * p.Hq;
     if constexpr (AP) {
       if (piece == 0)
-        lds_copy_tile<1, 8, FNW, 8>(bf.W, make_rsrc((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, (long)len * CH * 2), off_a, w);
+        lds_copy_tile<1, 8, FNW, 8>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, (long)len * CH * 2), off_a, w);
       if (piece == 1 && !no_u)
-        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, make_rsrc((const T*)p.v + ((long)t0 * p.Hv + h) * VD, wbytes * p.Hv), off_v, w);
+        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, rsrc_words((const T*)p.v + ((long)t0 * p.Hv + h) * VD, wbytes * p.Hv), off_v, w);
     } else {
       if (piece == 0)
-        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, make_rsrc((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
+        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, rsrc_words((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
       if (piece == 1 && !no_u)
-        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, make_rsrc((const T*)p.U + ((long)h * s.Ttot + t0) * VD, wbytes), off_wu, w);
+        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, rsrc_words((const T*)p.U + ((long)h * s.Ttot + t0) * VD, wbytes), off_wu, w);
     }
     if (piece == 2)
-      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, make_rsrc((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
+      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, rsrc_words((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
     if (piece == 3) {
       if (jc >= cbeg && !TRANS && !st_mode)
-        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.Q, make_rsrc((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
+        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.Q, rsrc_words((const T*)p.q + ((long)t0 * p.Hq + hk) * KD, qbytes), off_qk, w);
       if (w == 0) {
-        const rsrc_t gr = make_rsrc(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
-        lds_copy4(rsrc_words(gr), (uint32_t)l * 4u, lds_addr(bf.G));
+        const i32x4v gr = rsrc_words(p.gcum + (long)h * s.Ttot + t0, (long)len * 4);
+        lds_copy4(gr, (uint32_t)l * 4u, lds_addr(bf.G));
       }
     }
   };
@@ -930,6 +930,17 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     }
 
     if (!warm) {  // P tiles of this wave
+      // Masked scaled decays first (they do not depend on the products); the
+      // gate cumsums of the lane's four rows are one 16-byte read.
+      f32x4 dec[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(sG + r0);
+        const float gc = sG[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dec[m][e] = (r0 + e >= c && r0 + e < len) ? p.scale * __expf(gr[e] - gc) : 0.f;
+      }
       f32x4 pa[2] = {zero4(), zero4()};
       if constexpr (F32) {
 #pragma unroll
@@ -954,17 +965,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (m < pcnt) {
-          // Masked scaled decays (selects, no branches); the gate cumsums of
-          // the lane's four rows are one 16-byte read.
           const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
-          const f32x4 gr = *reinterpret_cast<const f32x4*>(sG + r0);
-          const float gc = sG[c];
-          f32x4 pv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = p.scale * __expf(gr[e] - gc) * pa[m][e];
-            pv[e] = (r0 + e >= c && r0 + e < len) ? x : 0.f;
-          }
+          const f32x4 pv = dec[m] * pa[m];
           if constexpr (F32) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) sP[(r0 + e) * PP + c] = pv[e];
@@ -1034,22 +1036,27 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
         }
       }
       float uv[4][4][CBW];
+      if constexpr (!F32 && CBW == 1) {
+        // The wave's 16 value columns over a tile's rows 4g..4g+3: one
+        // transposing read per tile gives each lane its column's four rows.
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const int sl = l & 15;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt) {
+          const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(sU + tix(16 * tt + 4 * q + (sl >> 2), 16 * w + 4 * (sl & 3))));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tt + acc_row(e);
-          if constexpr (CBW == 2 && !F32) {
-            const uint32_t pr = *reinterpret_cast<const uint32_t*>(sU + tix(r, 32 * w + 2 * t));
-            uv[tt][e][0] = __uint_as_float(pr << 16);
-            uv[tt][e][1] = __uint_as_float(pr & 0xffff0000u);
-          } else {
-#pragma unroll
-            for (int cb = 0; cb < CBW; ++cb) uv[tt][e][cb] = to_f(sU[tix(r, vcol(cb))]);
-          }
-#pragma unroll
-          for (int cb = 0; cb < CBW; ++cb) uv[tt][e][cb] = no_u ? 0.f : uv[tt][e][cb];  // U tile not copied for M
+          for (int e = 0; e < 4; ++e) uv[tt][e][0] = no_u ? 0.f : __uint_as_float((uint32_t)(uint16_t)x[e] << 16);
         }
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int cb = 0; cb < CBW; ++cb)   // (the U tile is not copied for M)
+              uv[tt][e][cb] = no_u ? 0.f : to_f(sU[tix(16 * tt + acc_row(e), vcol(cb))]);
+      }
       if constexpr (AP) {   // vn holds K h: Vnew = A''(V - Gamma * K h), A'' lower triangular
         const float* sGa = sD + 2 * CH;
         f32x4 xv[4];

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   };
   auto tile = [&](T* dst, const void* base, long elem0, long row_elems, int len, const uint32_t* off)
       __attribute__((always_inline)) {
-    lds_copy_tile<2, 16, FNW, 8>(dst, make_rsrc((const T*)base + elem0, (long)len * row_elems * 2), off, w);
+    lds_copy_tile<2, 16, FNW, 8>(dst, rsrc_words((const T*)base + elem0, (long)len * row_elems * 2), off, w);
   };
   auto copy_dO_Vn = [&](const Unit& u) __attribute__((always_inline)) {
     tile(sdO, p.d_o, ((long)u.t0 * p.Hv + u.h) * VD, (long)p.Hv * VD, u.len, off_hv);
@@ -181,13 +181,13 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   auto copy_A_gates = [&](const Unit& u, auto abc) __attribute__((always_inline)) {   // into buffer ab
     constexpr int ab = decltype(abc)::value;
     lds_copy_tile<1, 8, FNW, 8>(&sA2[ab][0],
-                                make_rsrc((const T*)p.A_bf + ((long)u.h * s.Ttot + u.t0) * CH, (long)u.len * CH * 2),
+                                rsrc_words((const T*)p.A_bf + ((long)u.h * s.Ttot + u.t0) * CH, (long)u.len * CH * 2),
                                 off_a, w);
     if (w == 0) {
-      const rsrc_t gr = make_rsrc(p.gcum + (long)u.h * s.Ttot + u.t0, (long)u.len * 4);
-      lds_copy4(rsrc_words(gr), (uint32_t)l * 4u, lds_addr(&sGc[ab][0]));
-      const rsrc_t br = make_rsrc(p.beta + (long)u.t0 * p.Hv + u.h, ((long)(u.len - 1) * p.Hv + 1) * 4);
-      lds_copy4(rsrc_words(br), (uint32_t)(l * p.Hv * 4), lds_addr(&sBe[ab][0]));
+      const i32x4v gr = rsrc_words(p.gcum + (long)u.h * s.Ttot + u.t0, (long)u.len * 4);
+      lds_copy4(gr, (uint32_t)l * 4u, lds_addr(&sGc[ab][0]));
+      const i32x4v br = rsrc_words(p.beta + (long)u.t0 * p.Hv + u.h, ((long)(u.len - 1) * p.Hv + 1) * 4);
+      lds_copy4(br, (uint32_t)(l * p.Hv * 4), lds_addr(&sBe[ab][0]));
     }
   };
   // rows 16w..16w+15 of h and dh as B fragments (contraction over V)
