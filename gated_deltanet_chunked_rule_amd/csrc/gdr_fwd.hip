@@ -467,6 +467,235 @@ __global__ __launch_bounds__(NTHR, AM ? 4 : 3) void k_intra(IntraParams p, int t
   }
 }
 
+// ------------------------------------------------------------- k_intra_w --
+// The bf16 intra-chunk pass in A diag(beta) mode, one (chunk, value head)
+// item per wave.  The items are independent and the whole 64 x 64 inverse of
+// one item fits one wave's registers, so no workgroup barrier is needed: the
+// sixteen waves a CU holds overlap each other's latencies (global loads, LDS
+// round trips, the dependent fp32 MFMA chains of the inverse) instead of
+// meeting at a barrier after every step.  Per item:
+//   1. g, beta (lane = token) and the gate scan; K as bf16 MFMA fragments
+//      straight from memory (lane (q, t) holds K[16i + t][32ks + 8q ..+8]),
+//      which serve as both the A and the B operand of K K^T.
+//   2. The ten lower 16 x 16 tiles of K K^T (fp32 accumulators), then L =
+//      strict_lower(diag(b)(D * K K^T)) in place and the certificate check
+//      0 <= b |k|^2 <= 2 on the diagonal.
+//   3. The blocked inverse, same algebra as k_intra's: diagonal blocks by the
+//      product (I + N^8)(I + N^4)(I + N^2)(I - N), M_ij = A_ii L_ij, and the
+//      off-diagonal blocks from M and the A_ii.  A product's left factor must
+//      be in MFMA A layout (lane t holds row t): accumulator tiles get there
+//      through a per-wave LDS tile (written by columns, read by rows).
+//   4. A'' = A diag(b) rows in bf16 (and, XA, A itself).
+template <int KD, bool XA>
+__global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_items, int nwg) {
+  constexpr int NKS = KD / 32;   // contraction steps of K K^T
+  constexpr int TP = 20;         // row pitch of the per-wave fp32 tiles (16-byte rows)
+  constexpr int NTT = 6;         // per-wave fp32 tiles
+  __shared__ __align__(16) float sT[NWAVE][NTT][16 * TP];
+  __shared__ __align__(16) float sGw[NWAVE][CH];
+  __shared__ __align__(16) float sBw[NWAVE][CH];
+  const SeqTables& s = p.s;
+  const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
+  const int x = xcd_remap(blockIdx.x, nwg);
+  if (x >= nwg) return;
+  const int u = x * NWAVE + w;
+  if (u >= total_items) return;
+  const int c = u / p.Hv;
+  const int h = u - c * p.Hv;
+  const int hk = h / (p.Hv / p.Hq);
+  int n, t0, len;
+  if (s.T_uniform > 0) {
+    const int nc = (s.T_uniform + CH - 1) / CH;
+    n = c / nc;
+    const int cj = c - n * nc;
+    t0 = n * s.T_uniform + cj * CH;
+    len = min(CH, s.T_uniform - cj * CH);
+    if (c >= s.NTtot || len <= 0) return;
+  } else if (!locate_chunk(s, c, n, t0, len)) {
+    return;
+  }
+  float* sG = sGw[w];
+  float* sB = sBw[w];
+  auto tl = [&](int i) { return &sT[w][i][0]; };
+  // accumulator tile -> rows of an LDS tile, and a row-layout (A operand) read
+  auto st_t = [&](float* X, const f32x4& a) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) X[(4 * q + e) * TP + t] = a[e];
+  };
+  auto ld_t = [&](const float* X) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(X + t * TP + 4 * q);
+  };
+
+  // 1. loads (rows past the chunk read as zero)
+  const rsrc_t gr = make_rsrc(p.g + (long)t0 * p.Hv + h, (long)len * p.Hv * 4);
+  const rsrc_t br = make_rsrc(p.beta + (long)t0 * p.Hv + h, (long)len * p.Hv * 4);
+  const float gv = buf_load_f32(gr, (uint32_t)(l * p.Hv) * 4u);
+  const float bv = buf_load_f32(br, (uint32_t)(l * p.Hv) * 4u);
+  const uint32_t krs = (uint32_t)(p.Hq * KD * 2);   // bytes between token rows of k
+  const rsrc_t kr = make_rsrc((const bf16*)p.k + ((long)t0 * p.Hq + hk) * KD, (long)len * krs);
+  bf16x8 kf[4][NKS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint4 r = buf_load16(kr, (uint32_t)(16 * i + t) * krs + (uint32_t)(32 * ks + 8 * q) * 2u);
+      __builtin_memcpy(&kf[i][ks], &r, 16);
+    }
+  const float gc = wave_inclusive_scan((l < len) ? gv : 0.f);
+  sG[l] = gc;
+  sB[l] = (l < len) ? bv : 0.f;
+  if (l < len) {
+    p.gcum[(long)h * s.Ttot + t0 + l] = gc;
+    if (p.g_cum_out) p.g_cum_out[(long)(t0 + l) * p.Hv + h] = gc;
+  }
+
+  // 2. lower tiles of K K^T; tile (i, j) at index i(i+1)/2 + j
+  f32x4 L[10];
+#pragma unroll
+  for (int m = 0; m < 10; ++m) L[m] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j <= i; ++j)
+        L[i * (i + 1) / 2 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[i][ks], kf[j][ks], L[i * (i + 1) / 2 + j], 0, 0, 0);
+  wave_sync();   // sG, sB visible to the whole wave
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 grow = *reinterpret_cast<const f32x4*>(sG + 16 * i + 4 * q);
+    const f32x4 brow = *reinterpret_cast<const f32x4*>(sB + 16 * i + 4 * q);
+#pragma unroll
+    for (int j = 0; j <= i; ++j) {
+      const float gcol = sG[16 * j + t];
+      f32x4& a = L[i * (i + 1) / 2 + j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * i + 4 * q + e, cc = 16 * j + t;
+        if (i == j && r == cc && r < len) {
+          const float bn = brow[e] * a[e];
+          if (!(bn >= 0.f && bn <= 2.f)) bad = 1;
+        }
+        a[e] = (r > cc) ? brow[e] * __expf(grow[e] - gcol) * a[e] : 0.f;
+      }
+    }
+  }
+  const bool any_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  if (l == 0) p.cert[(long)h * s.NTtot + c] = any_bad ? INFINITY : sG[len - 1];
+
+  // 4. (emitted per 16 x 16 block of A as soon as it is final) A'' rows:
+  // column scales b, an in-quad transpose gives each lane four adjacent
+  // columns of one row (one 8-byte store per block); A itself when asked for.
+  float su[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) su[j] = sB[16 * j + t];
+  const rsrc_t ar = make_rsrc((bf16*)p.Au + ((long)h * s.Ttot + t0) * CH, (long)len * CH * 2);
+  // A itself (XA): fp32 or bf16 head-major rows, or fp32 token-major rows
+  // (a null pointer gets an empty range: its stores are dropped)
+  const long hrow = ((long)h * s.Ttot + t0) * CH;
+  const rsrc_t xw = make_rsrc(p.A_ws ? p.A_ws + hrow : nullptr, p.A_ws ? (long)len * CH * 4 : 0);
+  const rsrc_t xb = make_rsrc(p.A_bf ? (bf16*)p.A_bf + hrow : nullptr, p.A_bf ? (long)len * CH * 2 : 0);
+  const rsrc_t xo = make_rsrc(p.A_out ? p.A_out + ((long)t0 * p.Hv + h) * CH : nullptr,
+                              p.A_out ? (long)len * p.Hv * CH * 4 : 0);
+  auto emit = [&](int i, int j, f32x4 v) __attribute__((always_inline)) {
+    if constexpr (XA) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t r = (uint32_t)(16 * i + 4 * q + e), cc = (uint32_t)(16 * j + t);
+        buf_store4(xw, (r * CH + cc) * 4u, __float_as_uint(v[e]));
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f<bf16>(v[e])), xb,
+                                              (r * CH + cc) * 2u, 0, 0);
+        buf_store4(xo, (r * (uint32_t)(p.Hv * CH) + cc) * 4u, __float_as_uint(v[e]));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= su[j];
+    const int r = 16 * i + 4 * q + (t & 3);
+    buf_store8(ar, (uint32_t)(r * CH + 16 * j + 4 * (t >> 2)) * 2u, pack4_bf16(quad_t(v)));
+  };
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int j = i + 1; j < 4; ++j) emit(i, j, zero4());
+
+  // 3. A = (I + L)^-1 by 16 x 16 blocks.
+  if (p.A_in) {
+    const float* src = p.A_in + ((long)t0 * p.Hv + h) * CH;
+    const long rs = (long)p.Hv * CH;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j <= i; ++j) {
+        f32x4 v = zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * i + 4 * q + e;
+          if (r < len && 16 * j + t < len) v[e] = src[(long)r * rs + 16 * j + t];
+        }
+        emit(i, j, v);
+      }
+    return;
+  }
+  // diagonal blocks: dg = (I - N), then (I + N^2), (I + N^4), (I + N^8) from the left
+  f32x4 dg[4], pw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st_t(tl(i), L[i * (i + 1) / 2 + i]);
+  wave_sync();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 cN = L[i * (i + 1) / 2 + i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dg[i][e] = (4 * q + e == t ? 1.f : 0.f) - cN[e];
+    pw[i] = mm(zero4(), ld_t(tl(i)), cN);   // N^2
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st_t(tl(i), pw[i]);
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 ap = ld_t(tl(i));
+      dg[i] = mm(dg[i], ap, dg[i]);
+      if (k < 2) pw[i] = mm(zero4(), ap, pw[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) emit(i, i, dg[i]);
+  // M_ij = A_ii L_ij (j < i), then into A layout
+  wave_sync();
+#pragma unroll
+  for (int i = 1; i < 4; ++i) st_t(tl(i - 1), dg[i]);
+  wave_sync();
+  {
+    f32x4 mc[6];   // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    const f32x4 a1 = ld_t(tl(0)), a2 = ld_t(tl(1)), a3 = ld_t(tl(2));
+    mc[0] = mm(zero4(), a1, L[1]);
+    mc[1] = mm(zero4(), a2, L[3]);
+    mc[2] = mm(zero4(), a2, L[4]);
+    mc[3] = mm(zero4(), a3, L[6]);
+    mc[4] = mm(zero4(), a3, L[7]);
+    mc[5] = mm(zero4(), a3, L[8]);
+    wave_sync();
+#pragma unroll
+    for (int m = 0; m < 6; ++m) st_t(tl(m), mc[m]);
+    wave_sync();
+  }
+  const f32x4 m10 = ld_t(tl(0)), m20 = ld_t(tl(1)), m21 = ld_t(tl(2));
+  const f32x4 m30 = ld_t(tl(3)), m31 = ld_t(tl(4)), m32 = ld_t(tl(5));
+  const f32x4 t10 = mm(zero4(), m10, dg[0]);
+  emit(1, 0, -t10);
+  const f32x4 t21 = mm(zero4(), m21, dg[1]);
+  emit(2, 1, -t21);
+  emit(3, 2, -mm(zero4(), m32, dg[2]));
+  const f32x4 a20 = mm(-mm(zero4(), m20, dg[0]), m21, t10);
+  emit(2, 0, a20);
+  emit(3, 1, mm(-mm(zero4(), m31, dg[1]), m32, t21));
+  emit(3, 0, mm(mm(-mm(zero4(), m30, dg[0]), m31, t10), m32, -a20));
+}
+
 // --------------------------------------------------------------- k_state --
 // One workgroup per (sequence, value head, V block, CP segment), serial over
 // the segment's chunks.  h (K x BV) stays in fp32 MFMA accumulators; the next
@@ -1357,7 +1586,13 @@ static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
   const int nwg = (int)std::min<long>(padded_grid(total), (am ? 4 : 3) * 256);
   const int per_wg = (int)((total + nwg - 1) / nwg);
   if (am) {
-    GDR_LAUNCH("intra_wy", (k_intra<T, KD, BF>), dim3(nwg), st, p, (int)total, per_wg, nwg);
+    // one item per wave
+    const int nw = (int)((total + NWAVE - 1) / NWAVE);
+    if (p.A_ws || p.A_bf || p.A_out) {
+      GDR_LAUNCH("intra_wy", (k_intra_w<KD, true>), dim3(padded_grid(nw)), st, p, (int)total, nw);
+    } else {
+      GDR_LAUNCH("intra_wy", (k_intra_w<KD, false>), dim3(padded_grid(nw)), st, p, (int)total, nw);
+    }
   } else {
     GDR_LAUNCH("intra_wy", (k_intra<T, KD, false>), dim3(nwg), st, p, (int)total, per_wg, nwg);
   }
