@@ -13,8 +13,10 @@
 //
 // Kernels, in launch order:
 //   k_plan    token/chunk/segment offset tables (one workgroup)
-//   k_intra   per (chunk, value head): gate cumsum, K K^T, blocked fp32
-//             triangular inverse, W and U on MFMA            [fully parallel]
+//   k_intra_w per (chunk, value head), one item per wave (bf16): gate
+//             cumsum, K K^T, blocked fp32 triangular inverse, A diag(beta)
+//             rows                                           [fully parallel]
+//   k_intra   the same per workgroup for fp32, storing W and U instead
 //   k_fused   per (sequence, value head, CP segment): the serial chunk
 //             recurrence with h in fp32 registers, fused with O  [serial part]
 //   (k_state  the same recurrence storing every chunk's entry state, for the
@@ -157,11 +159,9 @@ __device__ __forceinline__ void kk_tile(int w, int n, int& i, int& j) {
   else { i = 3; j = 2 + n; }
 }
 
-// AM: the bf16 forward's mode, storing A diag(beta) rows instead of W and U
-// (no V tile, no W/U products: smaller LDS and register footprint, four
-// workgroups per CU).
-template <typename T, int KD, bool AM>
-__global__ __launch_bounds__(NTHR, AM ? 4 : 3) void k_intra(IntraParams p, int total_items, int per_wg, int nwg) {
+// (fp32 path; the bf16 path stores A diag(beta) rows instead: k_intra_w)
+template <typename T, int KD>
+__global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_items, int per_wg, int nwg) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
   constexpr int NT = KD / 16;                 // column tiles of W and U
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(NTHR, AM ? 4 : 3) void k_intra(IntraParams p, int t
   constexpr int SZ_AT = 2 * CH * PA * (int)sizeof(T);
   constexpr int SZ_X = F32 ? SZ_AT : 0;       // fp32: A' / A'' cannot overlay the fp32 tiles
   static_assert(F32 || SZ_AT <= SZ_F, "A' and A'' must fit over the fp32 tiles");
-  constexpr int NKV = AM ? 1 : 2;             // staged row tiles: K (and V)
+  constexpr int NKV = 2;                      // staged row tiles: K and V
   __shared__ __align__(16) char smem[NKV * SZ_K + SZ_F + SZ_X];
   __shared__ float sG[CH], sB[CH];
   __shared__ int sFlag[NWAVE];
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NTHR, AM ? 4 : 3) void k_intra(IntraParams p, int t
     const int len = it.ok ? it.len : 0;
     const int t0 = it.ok ? it.t0 : 0;
     rk.load((const T*)p.k + ((long)t0 * p.Hq + it.hk) * KD, (long)p.Hq * KD, len);
-    if constexpr (!AM) rv.load((const T*)p.v + ((long)t0 * p.Hv + it.h) * VD, (long)p.Hv * VD, len);
+    rv.load((const T*)p.v + ((long)t0 * p.Hv + it.h) * VD, (long)p.Hv * VD, len);
     const rsrc_t gr = make_rsrc(p.g + (long)t0 * p.Hv + it.h, (long)len * p.Hv * 4);
     const rsrc_t br = make_rsrc(p.beta + (long)t0 * p.Hv + it.h, (long)len * p.Hv * 4);
     gv = buf_load_f32(gr, (uint32_t)(l * p.Hv) * 4u);
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(NTHR, AM ? 4 : 3) void k_intra(IntraParams p, int t
       }
     }
     rk.template store_perm<PK>(sK);
-    if constexpr (!AM) rv.template store_perm<PK>(sV);
+    rv.template store_perm<PK>(sV);
     lds_barrier();
     fetch(nx, rkn, rvn, gvn, bvn);
 
@@ -393,21 +393,6 @@ __global__ __launch_bounds__(NTHR, AM ? 4 : 3) void k_intra(IntraParams p, int t
       su[j] = sB[16 * j + t];
       sw[j] = su[j] * __expf(sG[16 * j + t]);
     }
-    if constexpr (AM) {   // A'' rows (bf16) for the fused pass, which forms Vnew = A''(V - Gamma K h) itself
-      if constexpr (!F32) {
-        const f32x4 av[4] = {a0, a1, a2, a3};
-        const int r = 16 * rb + 4 * q + (t & 3);   // after the in-quad transpose: row r, columns 16j + 4(t/4) ..
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4 v = av[j];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] *= su[j];
-          const uint2 u = pack4_bf16(quad_t(v));
-          if (r < len) *reinterpret_cast<uint2*>((bf16*)p.Au + ((long)h * s.Ttot + t0 + r) * CH + 16 * j + 4 * (t >> 2)) = u;
-        }
-      }
-      return;
-    }
     lds_barrier();
     const int nks = F32 ? 4 * (rb + 1) : (rb + 2) / 2;  // contraction steps (A' is zero beyond 16(rb+1))
     const int ntile = F32 ? rb + 1 : 2 * nks;          // A' tiles the steps read
@@ -480,9 +465,9 @@ __global__ __launch_bounds__(NTHR, AM ? 4 : 3) void k_intra(IntraParams p, int t
 //   2. The ten lower 16 x 16 tiles of K K^T (fp32 accumulators), then L =
 //      strict_lower(diag(b)(D * K K^T)) in place and the certificate check
 //      0 <= b |k|^2 <= 2 on the diagonal.
-//   3. The blocked inverse, same algebra as k_intra's: diagonal blocks by the
-//      product (I + N^8)(I + N^4)(I + N^2)(I - N), M_ij = A_ii L_ij, and the
-//      off-diagonal blocks from M and the A_ii.  A product's left factor must
+//   3. The blocked inverse: diagonal blocks A_ii by forward substitution
+//      (VALU, a lane per column), M_ij = A_ii L_ij, and the off-diagonal
+//      blocks from M and the A_ii as in k_intra.  A product's left factor must
 //      be in MFMA A layout (lane t holds row t): accumulator tiles get there
 //      through a per-wave LDS tile (written by columns, read by rows).
 //   4. A'' = A diag(b) rows in bf16 (and, XA, A itself).
@@ -491,7 +476,9 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   constexpr int NKS = KD / 32;   // contraction steps of K K^T
   constexpr int TP = 20;         // row pitch of the per-wave fp32 tiles (16-byte rows)
   constexpr int NTT = 6;         // per-wave fp32 tiles
-  __shared__ __align__(16) float sT[NWAVE][NTT][16 * TP];
+  constexpr int SP = CH + 8;      // row pitch (bf16) of the per-wave A'' staging rows
+  constexpr int SCR = (CH * SP * 2 > NTT * 16 * TP * 4 ? CH * SP * 2 : NTT * 16 * TP * 4) / 4;
+  __shared__ __align__(16) float sT[NWAVE][SCR];   // transposition tiles, later the A'' rows
   __shared__ __align__(16) float sGw[NWAVE][CH];
   __shared__ __align__(16) float sBw[NWAVE][CH];
   const SeqTables& s = p.s;
@@ -516,7 +503,8 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   }
   float* sG = sGw[w];
   float* sB = sBw[w];
-  auto tl = [&](int i) { return &sT[w][i][0]; };
+  auto tl = [&](int i) { return &sT[w][i * 16 * TP]; };
+  bf16* sa = reinterpret_cast<bf16*>(&sT[w][0]);
   // accumulator tile -> rows of an LDS tile, and a row-layout (A operand) read
   auto st_t = [&](float* X, const f32x4& a) __attribute__((always_inline)) {
 #pragma unroll
@@ -577,16 +565,18 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
           const float bn = brow[e] * a[e];
           if (!(bn >= 0.f && bn <= 2.f)) bad = 1;
         }
-        a[e] = (r > cc) ? brow[e] * __expf(grow[e] - gcol) * a[e] : 0.f;
+        const float lv = brow[e] * __expf(grow[e] - gcol) * a[e];
+        a[e] = (i > j || r > cc) ? lv : 0.f;
       }
     }
   }
   const bool any_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
   if (l == 0) p.cert[(long)h * s.NTtot + c] = any_bad ? INFINITY : sG[len - 1];
 
-  // 4. (emitted per 16 x 16 block of A as soon as it is final) A'' rows:
-  // column scales b, an in-quad transpose gives each lane four adjacent
-  // columns of one row (one 8-byte store per block); A itself when asked for.
+  // 4. (16 x 16 blocks of A emitted once the transposition tiles are no
+  // longer needed) A'' = A diag(b) staged as bf16 rows in LDS, then written
+  // as 16-byte row pieces (zero above the diagonal blocks); A itself when
+  // asked for.
   float su[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) su[j] = sB[16 * j + t];
@@ -598,7 +588,7 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   const rsrc_t xb = make_rsrc(p.A_bf ? (bf16*)p.A_bf + hrow : nullptr, p.A_bf ? (long)len * CH * 2 : 0);
   const rsrc_t xo = make_rsrc(p.A_out ? p.A_out + ((long)t0 * p.Hv + h) * CH : nullptr,
                               p.A_out ? (long)len * p.Hv * CH * 4 : 0);
-  auto emit = [&](int i, int j, f32x4 v) __attribute__((always_inline)) {
+  auto store_a = [&](int i, int j, const f32x4& v) __attribute__((always_inline)) {
     if constexpr (XA) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -609,15 +599,28 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
         buf_store4(xo, (r * (uint32_t)(p.Hv * CH) + cc) * 4u, __float_as_uint(v[e]));
       }
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] *= su[j];
-    const int r = 16 * i + 4 * q + (t & 3);
-    buf_store8(ar, (uint32_t)(r * CH + 16 * j + 4 * (t >> 2)) * 2u, pack4_bf16(quad_t(v)));
   };
+  // the blocks above the diagonal of A are zero
 #pragma unroll
   for (int i = 0; i < 3; ++i)
 #pragma unroll
-    for (int j = i + 1; j < 4; ++j) emit(i, j, zero4());
+    for (int j = i + 1; j < 4; ++j) store_a(i, j, zero4());
+  auto emit = [&](int i, int j, f32x4 v) __attribute__((always_inline)) {
+    store_a(i, j, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sa[(16 * i + 4 * q + e) * SP + 16 * j + t] = from_f<bf16>(v[e] * su[j]);
+  };
+  auto flush = [&]() __attribute__((always_inline)) {
+    wave_sync();
+    const int pc = l & 7;   // 16-byte piece of a row: columns 8pc .. 8pc + 7
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = (l >> 3) + 8 * k;
+      uint4 v = *reinterpret_cast<const uint4*>(sa + r * SP + 8 * pc);
+      if (pc >= 2 * ((r >> 4) + 1)) v = make_uint4(0u, 0u, 0u, 0u);
+      buf_store16(ar, (uint32_t)(r * CH + 8 * pc) * 2u, v);
+    }
+  };
 
   // 3. A = (I + L)^-1 by 16 x 16 blocks.
   if (p.A_in) {
@@ -635,49 +638,56 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
         }
         emit(i, j, v);
       }
+    flush();
     return;
   }
-  // diagonal blocks: dg = (I - N), then (I + N^2), (I + N^4), (I + N^8) from the left
-  f32x4 dg[4], pw[4];
+  // Diagonal blocks by forward substitution on the VALU: lane group b
+  // solves column t of (I + N_b)^-1, N_b = L_bb, reading the rows of N_b as
+  // LDS broadcasts; the solved column is written back as row t of A_bb^T,
+  // from which both layouts of A_bb are single reads.
 #pragma unroll
   for (int i = 0; i < 4; ++i) st_t(tl(i), L[i * (i + 1) / 2 + i]);
   wave_sync();
+  float xs[16];
+  {
+    const float* nb = tl(q);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f32x4 cN = L[i * (i + 1) / 2 + i];
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == t) ? 1.f : 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dg[i][e] = (4 * q + e == t ? 1.f : 0.f) - cN[e];
-    pw[i] = mm(zero4(), ld_t(tl(i)), cN);   // N^2
-  }
+      for (int j4 = 0; j4 < r; j4 += 4) {
+        const f32x4 nr = *reinterpret_cast<const f32x4*>(nb + r * TP + j4);
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    wave_sync();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st_t(tl(i), pw[i]);
-    wave_sync();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 ap = ld_t(tl(i));
-      dg[i] = mm(dg[i], ap, dg[i]);
-      if (k < 2) pw[i] = mm(zero4(), ap, pw[i]);
+        for (int jj = 0; jj < 4; ++jj)
+          if (j4 + jj < r) acc -= nr[jj] * xs[j4 + jj];
+      }
+      xs[r] = acc;
     }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) emit(i, i, dg[i]);
-  // M_ij = A_ii L_ij (j < i), then into A layout
-  wave_sync();
-#pragma unroll
-  for (int i = 1; i < 4; ++i) st_t(tl(i - 1), dg[i]);
   wave_sync();
   {
+    float* yb = tl(q);
+#pragma unroll
+    for (int r4 = 0; r4 < 16; r4 += 4)
+      *reinterpret_cast<f32x4*>(yb + t * TP + r4) = f32x4{xs[r4], xs[r4 + 1], xs[r4 + 2], xs[r4 + 3]};
+  }
+  wave_sync();
+  f32x4 dg[4], da[4];   // A_ii in accumulator layout and (i >= 1) in A layout
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dg[i] = ld_t(tl(i));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) da[i][e] = (i > 0) ? tl(i)[(4 * q + e) * TP + t] : 0.f;
+  }
+  // M_ij = A_ii L_ij (j < i), then into A layout
+  {
     f32x4 mc[6];   // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-    const f32x4 a1 = ld_t(tl(0)), a2 = ld_t(tl(1)), a3 = ld_t(tl(2));
-    mc[0] = mm(zero4(), a1, L[1]);
-    mc[1] = mm(zero4(), a2, L[3]);
-    mc[2] = mm(zero4(), a2, L[4]);
-    mc[3] = mm(zero4(), a3, L[6]);
-    mc[4] = mm(zero4(), a3, L[7]);
-    mc[5] = mm(zero4(), a3, L[8]);
+    mc[0] = mm(zero4(), da[1], L[1]);
+    mc[1] = mm(zero4(), da[2], L[3]);
+    mc[2] = mm(zero4(), da[2], L[4]);
+    mc[3] = mm(zero4(), da[3], L[6]);
+    mc[4] = mm(zero4(), da[3], L[7]);
+    mc[5] = mm(zero4(), da[3], L[8]);
     wave_sync();
 #pragma unroll
     for (int m = 0; m < 6; ++m) st_t(tl(m), mc[m]);
@@ -685,6 +695,9 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   }
   const f32x4 m10 = ld_t(tl(0)), m20 = ld_t(tl(1)), m21 = ld_t(tl(2));
   const f32x4 m30 = ld_t(tl(3)), m31 = ld_t(tl(4)), m32 = ld_t(tl(5));
+  wave_sync();   // the tiles are free: the A'' rows are staged over them
+#pragma unroll
+  for (int i = 0; i < 4; ++i) emit(i, i, dg[i]);
   const f32x4 t10 = mm(zero4(), m10, dg[0]);
   emit(1, 0, -t10);
   const f32x4 t21 = mm(zero4(), m21, dg[1]);
@@ -694,6 +707,7 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   emit(2, 0, a20);
   emit(3, 1, mm(-mm(zero4(), m31, dg[1]), m32, t21));
   emit(3, 0, mm(mm(-mm(zero4(), m30, dg[0]), m31, t10), m32, -a20));
+  flush();
 }
 
 // --------------------------------------------------------------- k_state --
@@ -1577,16 +1591,12 @@ static unsigned padded_grid(long total) { return (unsigned)(((total + 7) / 8) * 
 template <typename T, int KD>
 static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
   hipError_t err;
-  // persistent grid: three (A diag(beta) mode: four) workgroups per CU, each
-  // over a contiguous item range
+  // bf16: A diag(beta) rows, one item per wave; fp32: W and U, a persistent
+  // grid of three workgroups per CU, each over a contiguous item range
   constexpr bool BF = std::is_same<T, bf16>::value;
-  const bool am = BF && p.Au != nullptr;
-  if (p.Au ? !BF : (p.W == nullptr || p.U == nullptr)) return hipErrorInvalidValue;
+  if (BF ? p.Au == nullptr : (p.W == nullptr || p.U == nullptr)) return hipErrorInvalidValue;
   const long total = (long)p.s.NTtot * p.Hv;
-  const int nwg = (int)std::min<long>(padded_grid(total), (am ? 4 : 3) * 256);
-  const int per_wg = (int)((total + nwg - 1) / nwg);
-  if (am) {
-    // one item per wave
+  if constexpr (BF) {
     const int nw = (int)((total + NWAVE - 1) / NWAVE);
     if (p.A_ws || p.A_bf || p.A_out) {
       GDR_LAUNCH("intra_wy", (k_intra_w<KD, true>), dim3(padded_grid(nw)), st, p, (int)total, nw);
@@ -1594,7 +1604,9 @@ static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
       GDR_LAUNCH("intra_wy", (k_intra_w<KD, false>), dim3(padded_grid(nw)), st, p, (int)total, nw);
     }
   } else {
-    GDR_LAUNCH("intra_wy", (k_intra<T, KD, false>), dim3(nwg), st, p, (int)total, per_wg, nwg);
+    const int nwg = (int)std::min<long>(padded_grid(total), 3 * 256);
+    const int per_wg = (int)((total + nwg - 1) / nwg);
+    GDR_LAUNCH("intra_wy", (k_intra<T, KD>), dim3(nwg), st, p, (int)total, per_wg, nwg);
   }
   return err;
 }

@@ -163,3 +163,23 @@ def test_many_chunks_per_workgroup():
     w = gi.custom(B=1, T=64 * 600 + 17, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=94, initial_state=True,
                   backward=True, gate=(0.9, 0.999))
     check_bwd(gi.make_inputs(w), qk_heads=(1, 2), label="many chunks per workgroup")
+
+
+@pytest.mark.parametrize("K", [64, 128])
+def test_workspace_filled_with_nan(K):
+    # Every workspace element the backward reads (A with its zero blocks above
+    # the diagonal, the chunk states, Vnew, ...) is written before it is read:
+    # a workspace filled with NaN bit patterns gives the same gradients.
+    w = gi.custom(B=1, T=64 * 2 + 8, Hq=2, Hv=2, K=K, V=K, dtype="bf16", seed=76, backward=True)
+    inp = gi.make_inputs(w)
+    nbytes = gdr.bwd_workspace_bytes(dev(inp["q"]), dev(inp["v"]))
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    print(f"[bwd] NaN-filled workspace K={K} T={w.T}", flush=True)
+    grads = gdr.gdr_chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
+                              None, dev(inp["do"]), dev(inp["dht"]), inp["scale"], None, None, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(inp)
+    for name, x, r in zip(NAMES, grads, ref):
+        e = rel_err(x, r)
+        bound = TOL["bf16"]["dh0"] if name == "dh0" else TOL["bf16"]["grad"]
+        assert np.isfinite(e) and e <= bound, (name, e)

@@ -206,3 +206,23 @@ def test_exact_segments_varlen():
                   gate=(0.9, 0.999), zero_gate_frac=0.5)
     inp = gi.packed_from_lengths(w, [64 * 9 + 7, 1, 64 * 3, 0, 64 * 6 + 40])
     check_fwd(inp, gdr.Options(gdr.CP_FORCE, 2, 1), label="varlen exact segments")
+
+
+def test_workspace_filled_with_nan():
+    # the forward writes every workspace element it reads (the A diag(beta)
+    # rows with their zero blocks, the gate cumsums, the certificates): a
+    # workspace of NaN bit patterns changes nothing; the returned A is zero
+    # above each chunk's diagonal
+    w = gi.custom(B=1, T=64 * 3 + 8, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=77, initial_state=True)
+    inp = gi.make_inputs(w)
+    nbytes = gdr.fwd_workspace_bytes(dev(inp["q"]), dev(inp["v"]))
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    print(f"[fwd] NaN-filled workspace T={w.T}", flush=True)
+    o, ht, _, A = gpu_fwd(inp, output_A=True, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rht = oracle_fwd(inp)
+    assert rel_err(o, ro) <= TOL["bf16"]["o"] and rel_err(ht, rht) <= TOL["bf16"]["final_state"]
+    a = f64(A)   # [B, T, Hv, 64]: row t of its chunk's A
+    pos = np.arange(w.T) % 64
+    upper = np.arange(64)[None, :] > pos[:, None]
+    assert np.isfinite(a).all() and np.all(a[0][upper[:, None, :].repeat(w.Hv, 1)] == 0.0)
