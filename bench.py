@@ -7,7 +7,9 @@ context-parallel split.  One step = one full forward pass (plan, intra-chunk
 WY, serial state, output) through the C ABI on resident device buffers.
 
 Prints ONE JSON line: tokens/s and ms per step (K steps between device
-syncs, nothing else in the timed region), the roofline of the dominant
+syncs, nothing else in the timed region; the step is captured once in a HIP
+graph and replayed, its output checked bitwise against an eager step, and
+the eager launch rate is reported beside it), the roofline of the dominant
 kernel (its mean HIP-event duration on the launch stream over K more steps,
 against the algorithmic bytes or flops per launch) and the fp64 CPU
 oracle's throughput on the host.
@@ -232,6 +234,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration report")
     ap.add_argument("--no-sweep", action="store_true", help="skip the training-step sweep")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (default: HIP-graph replay of the step, eager reported beside it)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -256,17 +260,42 @@ def main():
     ws = torch.empty(gdr.fwd_workspace_bytes(q, v), device=dev, dtype=torch.uint8)
 
     def step():
-        gdr.gdr_chunk_fwd(q, k, v, g, beta, scale, workspace=ws)
+        return gdr.gdr_chunk_fwd(q, k, v, g, beta, scale, workspace=ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: the steps alone
+    # eager launches: each step enqueues its kernels from the host
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    eager_ms = (t1 - t0) * 1e3 / args.steps
+    o_ref, ht_ref, _, _ = step()
+    if not args.eager:
+        # the same step captured once in a HIP graph and replayed (fixed shapes
+        # and buffers, as in a serving loop): no host launch gaps between the
+        # kernels.  Every replay recomputes the whole forward; its output is
+        # checked bitwise against the eager step.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            o_g, ht_g, _, _ = step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(o_g, o_ref) and torch.equal(ht_g, ht_ref)):
+            raise RuntimeError("graph replay differs from the eager forward")
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     # per-kernel durations: the same number of steps again, with the
     # library's HIP events recorded around every launch on its stream (the
     # events add a few us per launch, so they stay out of the timed region)
@@ -344,7 +373,9 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "long_context", "B": w.B, "T": w.T, "Hq": w.Hq, "Hv": w.Hv, "K": w.K,
                    "V": w.V, "chunk": 64, "cp_segment_chunks": plan["segment_chunks"],
-                   "cp_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"]},
+                   "cp_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"],
+                   "launch": "eager" if args.eager else "hip_graph"},
+        "eager_ms_per_step": eager_ms, "eager_tokens_per_s": tokens / (eager_ms * 1e-3),
         "kernels_us": {n: 1e3 * t / c for n, (t, c) in kern.items()},
         "roofline": roof,
         "method_roofline": method_roof,

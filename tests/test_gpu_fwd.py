@@ -226,3 +226,32 @@ def test_workspace_filled_with_nan():
     pos = np.arange(w.T) % 64
     upper = np.arange(64)[None, :] > pos[:, None]
     assert np.isfinite(a).all() and np.all(a[0][upper[:, None, :].repeat(w.Hv, 1)] == 0.0)
+
+
+def test_graph_replay_matches_eager():
+    # The forward enqueues kernels only (no allocation, memset or sync inside
+    # the library), so one call can be captured in a HIP graph and replayed;
+    # every replay, with eager work in between, equals the eager call bitwise.
+    w = gi.custom(B=1, T=64 * 40 + 5, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=78, initial_state=True)
+    inp = gi.make_inputs(w)
+    q, k, v, g, b, h0 = (dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "initial_state"))
+    opts = gdr.Options(gdr.CP_FORCE, 8, 2)   # CP segments: transition, scan and output launches
+    print(f"[fwd] graph replay T={w.T}", flush=True)
+    call = lambda: gdr.gdr_chunk_fwd(q, k, v, g, b, inp["scale"], h0, options=opts)
+    o_ref, ht_ref, _, _ = call()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        o_g, ht_g, _, _ = call()
+    for i in range(3):
+        o_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_ref) and torch.equal(ht_g, ht_ref), i
+        o_e, _, _, _ = call()   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o_e, o_ref)
