@@ -470,8 +470,10 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
 //      blocks from M and the A_ii as in k_intra.  A product's left factor must
 //      be in MFMA A layout (lane t holds row t): accumulator tiles get there
 //      through a per-wave LDS tile (written by columns, read by rows).
-//   4. A'' = A diag(b) rows in bf16 (and, XA, A itself).
-template <int KD, bool XA>
+//   4. A'' = A diag(b) rows in bf16 (and, with XA, A itself).
+// XA: 0 A'' only; 1 also A in fp32 (A_ws and/or A_out, element stores); 2 also
+// A in bf16 (A_bf, staged through LDS like A'').
+template <int KD, int XA>
 __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_items, int nwg) {
   constexpr int NKS = KD / 32;   // contraction steps of K K^T
   constexpr int TP = 20;         // row pitch of the per-wave fp32 tiles (16-byte rows)
@@ -589,13 +591,11 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   const rsrc_t xo = make_rsrc(p.A_out ? p.A_out + ((long)t0 * p.Hv + h) * CH : nullptr,
                               p.A_out ? (long)len * p.Hv * CH * 4 : 0);
   auto store_a = [&](int i, int j, const f32x4& v) __attribute__((always_inline)) {
-    if constexpr (XA) {
+    if constexpr (XA == 1) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t r = (uint32_t)(16 * i + 4 * q + e), cc = (uint32_t)(16 * j + t);
         buf_store4(xw, (r * CH + cc) * 4u, __float_as_uint(v[e]));
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f<bf16>(v[e])), xb,
-                                              (r * CH + cc) * 2u, 0, 0);
         buf_store4(xo, (r * (uint32_t)(p.Hv * CH) + cc) * 4u, __float_as_uint(v[e]));
       }
     }
@@ -605,20 +605,46 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   for (int i = 0; i < 3; ++i)
 #pragma unroll
     for (int j = i + 1; j < 4; ++j) store_a(i, j, zero4());
+  // Staging: without a bf16 A the A'' rows of all 64 tokens; with it, A'' and
+  // A rows of one 32-token half at a time (sa: A'', sa + 32 SP: A).
+  constexpr bool two = XA == 2;
   auto emit = [&](int i, int j, f32x4 v) __attribute__((always_inline)) {
     store_a(i, j, v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sa[(16 * i + 4 * q + e) * SP + 16 * j + t] = from_f<bf16>(v[e] * su[j]);
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * i + 4 * q + e;
+      if (two) {
+        sa[(r & 31) * SP + 16 * j + t] = from_f<bf16>(v[e] * su[j]);
+        sa[(32 + (r & 31)) * SP + 16 * j + t] = from_f<bf16>(v[e]);
+      } else {
+        sa[r * SP + 16 * j + t] = from_f<bf16>(v[e] * su[j]);
+      }
+    }
   };
-  auto flush = [&]() __attribute__((always_inline)) {
+  // 16-byte row pieces from the staging rows to memory (zero above the
+  // diagonal blocks); half < 0: all 64 A'' rows, else one half of A'' and A.
+  auto flush = [&](int half) __attribute__((always_inline)) {
     wave_sync();
     const int pc = l & 7;   // 16-byte piece of a row: columns 8pc .. 8pc + 7
+    if (half < 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = (l >> 3) + 8 * k;
-      uint4 v = *reinterpret_cast<const uint4*>(sa + r * SP + 8 * pc);
-      if (pc >= 2 * ((r >> 4) + 1)) v = make_uint4(0u, 0u, 0u, 0u);
-      buf_store16(ar, (uint32_t)(r * CH + 8 * pc) * 2u, v);
+      for (int k = 0; k < 8; ++k) {
+        const int r = (l >> 3) + 8 * k;
+        uint4 v = *reinterpret_cast<const uint4*>(sa + r * SP + 8 * pc);
+        if (pc >= 2 * ((r >> 4) + 1)) v = make_uint4(0u, 0u, 0u, 0u);
+        buf_store16(ar, (uint32_t)(r * CH + 8 * pc) * 2u, v);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rl = (l >> 3) + 8 * k, r = 32 * half + rl;
+        uint4 v = *reinterpret_cast<const uint4*>(sa + rl * SP + 8 * pc);
+        uint4 u = *reinterpret_cast<const uint4*>(sa + (32 + rl) * SP + 8 * pc);
+        if (pc >= 2 * ((r >> 4) + 1)) v = u = make_uint4(0u, 0u, 0u, 0u);
+        buf_store16(ar, (uint32_t)(r * CH + 8 * pc) * 2u, v);
+        buf_store16(xb, (uint32_t)(r * CH + 8 * pc) * 2u, u);
+      }
+      wave_sync();   // the half's rows are read before the next half is staged
     }
   };
 
@@ -627,7 +653,7 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
     const float* src = p.A_in + ((long)t0 * p.Hv + h) * CH;
     const long rs = (long)p.Hv * CH;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j <= i; ++j) {
         f32x4 v = zero4();
@@ -638,7 +664,9 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
         }
         emit(i, j, v);
       }
-    flush();
+      if (i == 1 && two) flush(0);
+    }
+    flush(two ? 1 : -1);
     return;
   }
   // Diagonal blocks by forward substitution on the VALU: lane group b
@@ -696,10 +724,13 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   const f32x4 m10 = ld_t(tl(0)), m20 = ld_t(tl(1)), m21 = ld_t(tl(2));
   const f32x4 m30 = ld_t(tl(3)), m31 = ld_t(tl(4)), m32 = ld_t(tl(5));
   wave_sync();   // the tiles are free: the A'' rows are staged over them
-#pragma unroll
-  for (int i = 0; i < 4; ++i) emit(i, i, dg[i]);
+  emit(0, 0, dg[0]);
+  emit(1, 1, dg[1]);
   const f32x4 t10 = mm(zero4(), m10, dg[0]);
   emit(1, 0, -t10);
+  if (two) flush(0);
+  emit(2, 2, dg[2]);
+  emit(3, 3, dg[3]);
   const f32x4 t21 = mm(zero4(), m21, dg[1]);
   emit(2, 1, -t21);
   emit(3, 2, -mm(zero4(), m32, dg[2]));
@@ -707,7 +738,7 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   emit(2, 0, a20);
   emit(3, 1, mm(-mm(zero4(), m31, dg[1]), m32, t21));
   emit(3, 0, mm(mm(-mm(zero4(), m30, dg[0]), m31, t10), m32, -a20));
-  flush();
+  flush(two ? 1 : -1);
 }
 
 // --------------------------------------------------------------- k_state --
@@ -1598,10 +1629,13 @@ static hipError_t intra_impl(const IntraParams& p, hipStream_t st) {
   const long total = (long)p.s.NTtot * p.Hv;
   if constexpr (BF) {
     const int nw = (int)((total + NWAVE - 1) / NWAVE);
-    if (p.A_ws || p.A_bf || p.A_out) {
-      GDR_LAUNCH("intra_wy", (k_intra_w<KD, true>), dim3(padded_grid(nw)), st, p, (int)total, nw);
+    if (p.A_bf && (p.A_ws || p.A_out)) return hipErrorInvalidValue;   // one form of A per call
+    if (p.A_bf) {
+      GDR_LAUNCH("intra_wy", (k_intra_w<KD, 2>), dim3(padded_grid(nw)), st, p, (int)total, nw);
+    } else if (p.A_ws || p.A_out) {
+      GDR_LAUNCH("intra_wy", (k_intra_w<KD, 1>), dim3(padded_grid(nw)), st, p, (int)total, nw);
     } else {
-      GDR_LAUNCH("intra_wy", (k_intra_w<KD, false>), dim3(padded_grid(nw)), st, p, (int)total, nw);
+      GDR_LAUNCH("intra_wy", (k_intra_w<KD, 0>), dim3(padded_grid(nw)), st, p, (int)total, nw);
     }
   } else {
     const int nwg = (int)std::min<long>(padded_grid(total), 3 * 256);
