@@ -1661,7 +1661,9 @@ static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t s
   // bf16 passes read A diag(beta) and V; fp32 passes read W and U
   constexpr bool F32 = std::is_same<T, float>::value;
   const bool apath = !F32;
-  if (apath ? (p.Au == nullptr || p.v == nullptr) : (p.W == nullptr || p.U == nullptr)) return hipErrorInvalidValue;
+  // (with no token at all the pass only writes the final states: nothing is read)
+  if (p.s.Ttot > 0 && (apath ? (p.Au == nullptr || p.v == nullptr) : (p.W == nullptr || p.U == nullptr)))
+    return hipErrorInvalidValue;
   timing_before(p.trans ? "cp_transition" : states ? "chunk_states" : "chunk_fused", st);
   if (p.trans && apath) hipLaunchKernelGGL((k_fused<T, KD, 2>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
   else if (p.trans) hipLaunchKernelGGL((k_fused<T, KD, 3>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);

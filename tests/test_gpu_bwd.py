@@ -183,3 +183,14 @@ def test_workspace_filled_with_nan(K):
         e = rel_err(x, r)
         bound = TOL["bf16"]["dh0"] if name == "dh0" else TOL["bf16"]["grad"]
         assert np.isfinite(e) and e <= bound, (name, e)
+
+
+def test_empty_sequence_gradient_passes_through():
+    # with no token the final-state gradient reaches the initial state unchanged
+    w = gi.custom(B=2, T=0, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=81, initial_state=True, backward=True)
+    inp = gi.make_inputs(w)
+    print("[bwd] T=0", flush=True)
+    grads = gpu_bwd(inp)
+    torch.cuda.synchronize()
+    assert all(x.numel() == 0 for x in grads[:5])
+    assert torch.equal(grads[5].cpu(), inp["dht"])

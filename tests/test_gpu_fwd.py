@@ -255,3 +255,40 @@ def test_graph_replay_matches_eager():
         o_e, _, _, _ = call()   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(o_e, o_ref)
+
+
+@pytest.mark.parametrize("T", [0, 1, 64])
+def test_empty_single_token_and_one_chunk(T):
+    # T = 0: no chunk at all, the final state is the initial state; T = 1: a
+    # one-token chunk; T = 64: exactly one full chunk
+    w = gi.custom(B=2, T=T, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=79, initial_state=True)
+    inp = gi.make_inputs(w)
+    print(f"[fwd] T={T}", flush=True)
+    o, ht, _, _ = gpu_fwd(inp)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (2, T, 4, 128)
+    if T == 0:
+        assert torch.equal(ht.cpu(), inp["initial_state"])
+        return
+    ro, rht = oracle_fwd(inp)
+    assert rel_err(o, ro) <= TOL["bf16"]["o"] and rel_err(ht, rht) <= TOL["bf16"]["final_state"]
+
+
+def test_zero_beta_state_only_decays():
+    # beta = 0 writes nothing: S_t = exp(g_1 + .. + g_t) S_0, so the closed form
+    # o_t = scale exp(sum_{u<=t} g_u) S_0^T q_t and final S = exp(sum g) S_0 fix
+    # the outputs without the oracle (fp32: bf16 q, k, v are exact inputs here)
+    w = gi.custom(B=1, T=64 * 3 + 10, Hq=2, Hv=4, K=64, V=64, dtype="f32", seed=80, initial_state=True)
+    inp = gi.make_inputs(w)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    print(f"[fwd] beta = 0, T={w.T}", flush=True)
+    o, ht, _, _ = gpu_fwd(inp)
+    torch.cuda.synchronize()
+    q, g, s0 = f64(inp["q"])[0], f64(inp["g"])[0], f64(inp["initial_state"])[0]   # [T,Hq,K], [T,Hv], [Hv,K,V]
+    G = w.Hv // w.Hq
+    decay = np.exp(np.cumsum(g, axis=0))                                          # [T, Hv]
+    qv = np.repeat(q, G, axis=1)                                                  # [T, Hv, K]
+    ro = inp["scale"] * decay[:, :, None] * np.einsum("thk,hkv->thv", qv, s0)
+    rht = decay[-1][:, None, None] * s0
+    assert rel_err(o[0], ro) <= TOL["f32"]["o"]
+    assert rel_err(ht[0], rht) <= TOL["f32"]["final_state"]
