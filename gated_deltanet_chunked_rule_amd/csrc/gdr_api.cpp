@@ -23,6 +23,7 @@ gdr_status fail(gdr_status s, const std::string& msg) {
 }
 
 constexpr int kChunk = 64;
+constexpr int kMaxOrderedSegs = 1024;   // segments the plan kernel ranks for the dispatch order
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kStateWgPerCU = 1;   // fused state workgroups (8 waves) resident per CU
 constexpr size_t kAlign = 256;
@@ -43,7 +44,7 @@ struct Problem {
 
 struct Layout {
   size_t cu = 0, chunk_off = 0, seg_off = 0, gcum = 0, cert = 0, W = 0, U = 0, vnew = 0, hbuf = 0;
-  size_t A = 0, dhbuf = 0, dvn = 0, segtr = 0, hstart = 0, Au = 0, total = 0;
+  size_t A = 0, dhbuf = 0, dvn = 0, segtr = 0, hstart = 0, Au = 0, seg_order = 0, total = 0;
 };
 
 // bf16 stages A diag(beta) per chunk and V, and forms Vnew (and, in the
@@ -190,6 +191,7 @@ Layout layout(const Problem& P, bool bwd) {
   Lo.cu = take(nn * 4);
   Lo.chunk_off = take(nn * 4);
   Lo.seg_off = take(nn * 4);
+  Lo.seg_order = take(kMaxOrderedSegs * 4);
   Lo.gcum = take(hv * tt * 4);
   Lo.cert = take(hv * nt * 4);
   if (apath(P)) {
@@ -214,6 +216,20 @@ Layout layout(const Problem& P, bool bwd) {
   return Lo;
 }
 
+// Packed batches of unequal sequences dispatch their state segments longest
+// first (ranked on the device by k_plan, at most kMaxOrderedSegs of them): the
+// number of segments for segment length L, or 0 when no order is used.
+int ordered_segs(const Problem& P, int L) {
+  if (!P.packed || P.chunks.empty()) return 0;
+  int segs = 0;
+  bool equal = true;
+  for (int c : P.chunks) {
+    segs += std::max(1, (c + std::max(L, 1) - 1) / std::max(L, 1));
+    equal = equal && c == P.chunks[0];
+  }
+  return (equal || segs > kMaxOrderedSegs) ? 0 : segs;
+}
+
 // L: the CP segment length of the passes that read the segment offsets.
 gdr::SeqTables tables(const Problem& P, const Layout& Lo, char* ws, int L) {
   gdr::SeqTables s;
@@ -226,6 +242,8 @@ gdr::SeqTables tables(const Problem& P, const Layout& Lo, char* ws, int L) {
   s.T_uniform = P.packed ? 0 : P.T;
   const int ntu = (P.T + kChunk - 1) / kChunk;
   s.segs_uniform = std::max(1, (ntu + std::max(L, 1) - 1) / std::max(L, 1));
+  const int segs = ordered_segs(P, L);
+  s.seg_order = segs > 0 ? reinterpret_cast<const int32_t*>(ws + Lo.seg_order) : nullptr;
   return s;
 }
 
@@ -251,6 +269,9 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
   pp.chunk_off = reinterpret_cast<int32_t*>(ws + Lo.chunk_off);
   pp.seg_off = reinterpret_cast<int32_t*>(ws + Lo.seg_off);
   const gdr::SeqTables s = tables(P, Lo, ws, L);
+  pp.seg_order = const_cast<int32_t*>(s.seg_order);
+  pp.total_segs = ordered_segs(P, L);
+  pp.warmup = P.W;
   // uniform rows need no tables: every kernel derives them arithmetically
   if (s.T_uniform <= 0 && (e = gdr::launch_plan(pp, st)) != hipSuccess) return hip_fail(e, "plan launch");
   if (P.NTtot > 0) {

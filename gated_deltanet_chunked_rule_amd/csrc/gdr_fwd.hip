@@ -77,6 +77,29 @@ __global__ __launch_bounds__(1024) void k_plan(PlanParams p) {
     p.chunk_off[N] = sc[buf][1023];
     p.seg_off[N] = ss[buf][1023];
   }
+  if (p.seg_order) {
+    // Segments by decreasing work (its chunks plus the warmup chunks before
+    // it; ties by index): the state passes dispatch the longest first.
+    __shared__ int swork[1024];
+    const int S = min(p.total_segs, 1024);
+    __syncthreads();   // the offset tables above are complete
+    for (int i = tid; i < S; i += 1024) {
+      int lo = 0, hi = N - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.seg_off[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      const int ps = i - p.seg_off[lo], ch = p.chunk_off[lo + 1] - p.chunk_off[lo], L = p.seg_chunks;
+      swork[i] = max(0, min(L, ch - ps * L)) + (ps > 0 ? min(p.warmup, ps * L) : 0);
+    }
+    __syncthreads();
+    for (int i = tid; i < S; i += 1024) {
+      const int wi = swork[i];
+      int r = 0;
+      for (int j = 0; j < S; ++j) r += (swork[j] > wi || (swork[j] == wi && j < i)) ? 1 : 0;
+      p.seg_order[r] = i;
+    }
+  }
 }
 
 // Locates chunk c: sequence n, first token t0 and valid length; false if the
@@ -984,10 +1007,24 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   auto tix = [](int r, int c) { return (r * NCH + ((c / VEC) ^ stage_swz<NCH>(r))) * VEC + (c % VEC); };
 
   const SeqTables& s = p.s;
-  const int u = xcd_remap(blockIdx.x, total_items);
-  if (u >= total_items) return;
-  const int h = u % p.Hv;
-  const int item2 = u / p.Hv;
+  int h, item2;
+  if (!TRANS && s.seg_order) {
+    // Unequal segments: groups of the G value heads that share q and k, in
+    // decreasing segment work, go round-robin over the 8 XCDs (block b runs
+    // on XCD b mod 8); a group's heads take consecutive slots of one XCD.
+    const int G = p.Hv / p.Hq;
+    const int x = (int)blockIdx.x & 7, pos = (int)blockIdx.x >> 3;
+    const int kg = (pos / G) * 8 + x;
+    if (kg >= p.total_segs * p.Hq) return;
+    const int r = kg / p.Hq;
+    item2 = s.seg_order[r];
+    h = (kg - r * p.Hq) * G + pos % G;
+  } else {
+    const int u = xcd_remap(blockIdx.x, total_items);
+    if (u >= total_items) return;
+    h = u % p.Hv;
+    item2 = u / p.Hv;
+  }
   const int part = TRANS ? (item2 & 1) : 1;   // transition pass: 0 M, 1 b
   const int item = TRANS ? (item2 >> 1) : item2;
   const int n = s.seq_of_seg(item);
@@ -1664,11 +1701,15 @@ static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t s
   // (with no token at all the pass only writes the final states: nothing is read)
   if (p.s.Ttot > 0 && (apath ? (p.Au == nullptr || p.v == nullptr) : (p.W == nullptr || p.U == nullptr)))
     return hipErrorInvalidValue;
+  // with a segment order: 8 XCDs x G slots per round of head groups
+  const unsigned grid = (!p.trans && p.s.seg_order)
+      ? (unsigned)(8 * (p.Hv / p.Hq) * (((long)total_segs * p.Hq + 7) / 8)) : padded_grid(total);
+  if (!p.trans && p.s.seg_order && total_segs > 1024) return hipErrorInvalidValue;
   timing_before(p.trans ? "cp_transition" : states ? "chunk_states" : "chunk_fused", st);
-  if (p.trans && apath) hipLaunchKernelGGL((k_fused<T, KD, 2>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
-  else if (p.trans) hipLaunchKernelGGL((k_fused<T, KD, 3>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
-  else if (states) hipLaunchKernelGGL((k_fused<T, KD, 1>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
-  else hipLaunchKernelGGL((k_fused<T, KD, 0>), dim3(padded_grid(total)), dim3(FNT), 0, st, p, total);
+  if (p.trans && apath) hipLaunchKernelGGL((k_fused<T, KD, 2>), dim3(grid), dim3(FNT), 0, st, p, total);
+  else if (p.trans) hipLaunchKernelGGL((k_fused<T, KD, 3>), dim3(grid), dim3(FNT), 0, st, p, total);
+  else if (states) hipLaunchKernelGGL((k_fused<T, KD, 1>), dim3(grid), dim3(FNT), 0, st, p, total);
+  else hipLaunchKernelGGL((k_fused<T, KD, 0>), dim3(grid), dim3(FNT), 0, st, p, total);
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;

@@ -32,6 +32,8 @@ struct SeqTables {
   int NTtot;                 // chunks (host count; device tables must agree)
   int T_uniform;             // > 0: N rows of T_uniform tokens (no cu_seqlens); the
   int segs_uniform;          //   tables are then arithmetic (segments per row) and never read
+  const int32_t* seg_order;  // nullable (packed batches of unequal sequences): the state
+                             //   segments by decreasing chunk steps, for the dispatch order
 
   __device__ __forceinline__ int nt_uniform() const { return (T_uniform + 63) / 64; }
   __device__ __forceinline__ int cu_at(int n) const { return T_uniform > 0 ? n * T_uniform : cu[n]; }
@@ -59,6 +61,8 @@ struct PlanParams {
   const int32_t* cu_in;      // nullable: uniform rows of T tokens
   int N, T, seg_chunks;
   int32_t *cu, *chunk_off, *seg_off;
+  int32_t* seg_order;        // nullable: also rank the segments by work (at most 1024 of them)
+  int total_segs, warmup;
 };
 
 struct IntraParams {
