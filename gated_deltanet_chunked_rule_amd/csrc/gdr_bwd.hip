@@ -236,10 +236,23 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   auto tix = [](int r, int c) { return (r * NCH + ((c / VEC) ^ stage_swz<NCH>(r))) * VEC + (c % VEC); };
 
   const SeqTables& s = p.s;
-  const int u = xcd_remap(blockIdx.x, total_items);
-  if (u >= total_items) return;
-  const int h = u % p.Hv;
-  const int item = u / p.Hv;
+  int h, item;
+  if (!TRANS && s.seg_order) {
+    // unequal segments: longest first, head groups round-robin over the XCDs
+    // (the forward state passes' order)
+    const int G = p.Hv / p.Hq;
+    const int x = (int)blockIdx.x & 7, pos = (int)blockIdx.x >> 3;
+    const int kg = (pos / G) * 8 + x;
+    if (kg >= p.total_segs * p.Hq) return;
+    const int r = kg / p.Hq;
+    item = s.seg_order[r];
+    h = (kg - r * p.Hq) * G + pos % G;
+  } else {
+    const int u = xcd_remap(blockIdx.x, total_items);
+    if (u >= total_items) return;
+    h = u % p.Hv;
+    item = u / p.Hv;
+  }
   const int n = s.seq_of_seg(item);
   const int pseg = item - s.seg_at(n);
   const int nseg = s.seg_at(n + 1) - s.seg_at(n);
@@ -973,9 +986,13 @@ hipError_t launch_dstate(DType dt, int KD, int BV, const DStateParams& p, int to
 template <int KD>
 static hipError_t dfused_impl(const DFusedParams& p, int total_segs, hipStream_t st) {
   const int total = total_segs * p.Hv;
+  if (!p.trans && p.s.seg_order && (total_segs > 1024 || total_segs != p.total_segs)) return hipErrorInvalidValue;
+  // with a segment order: 8 XCDs x G slots per round of head groups
+  const unsigned grid = (!p.trans && p.s.seg_order)
+      ? (unsigned)(8 * (p.Hv / p.Hq) * (((long)total_segs * p.Hq + 7) / 8)) : padded_grid_b(total);
   timing_before(p.trans ? "cp_rev_transition" : "chunk_dfused", st);
-  if (p.trans) hipLaunchKernelGGL((k_dfused<KD, true>), dim3(padded_grid_b(total)), dim3(FNT), 0, st, p, total);
-  else hipLaunchKernelGGL((k_dfused<KD, false>), dim3(padded_grid_b(total)), dim3(FNT), 0, st, p, total);
+  if (p.trans) hipLaunchKernelGGL((k_dfused<KD, true>), dim3(grid), dim3(FNT), 0, st, p, total);
+  else hipLaunchKernelGGL((k_dfused<KD, false>), dim3(grid), dim3(FNT), 0, st, p, total);
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;
