@@ -586,9 +586,9 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * i + 4 * q + e, cc = 16 * j + t;
-        if (i == j && r == cc && r < len) {
+        if (i == j) {   // diagonal of K K^T: branch-free range check of b |k|^2
           const float bn = brow[e] * a[e];
-          if (!(bn >= 0.f && bn <= 2.f)) bad = 1;
+          bad |= (r == cc && r < len && !(bn >= 0.f && bn <= 2.f)) ? 1 : 0;
         }
         const float lv = brow[e] * __expf(grow[e] - gcol) * a[e];
         a[e] = (i > j || r > cc) ? lv : 0.f;
@@ -634,13 +634,16 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   auto emit = [&](int i, int j, f32x4 v) __attribute__((always_inline)) {
     store_a(i, j, v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 4; e += 2) {   // two rows per conversion
       const int r = 16 * i + 4 * q + e;
+      const bf16x2 av = __builtin_convertvector((f32x2){v[e] * su[j], v[e + 1] * su[j]}, bf16x2);
+      const int ra = two ? (r & 31) : r;
+      sa[ra * SP + 16 * j + t] = av[0];
+      sa[(ra + 1) * SP + 16 * j + t] = av[1];
       if (two) {
-        sa[(r & 31) * SP + 16 * j + t] = from_f<bf16>(v[e] * su[j]);
-        sa[(32 + (r & 31)) * SP + 16 * j + t] = from_f<bf16>(v[e]);
-      } else {
-        sa[r * SP + 16 * j + t] = from_f<bf16>(v[e] * su[j]);
+        const bf16x2 au = __builtin_convertvector((f32x2){v[e], v[e + 1]}, bf16x2);
+        sa[(32 + ra) * SP + 16 * j + t] = au[0];
+        sa[(33 + ra) * SP + 16 * j + t] = au[1];
       }
     }
   };
