@@ -1235,11 +1235,15 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           for (int e = 0; e < 4; ++e) hb[(long)(16 * rb + acc_row(e)) * VD + vcol(0)] = hs[rb][0][e];
       } else {
         // A 4x4 transpose within each lane quad gives a lane one K row over
-        // the quad's four columns: one 8-byte store per tile.
+        // the quad's four columns, staged (8 bytes per tile) in the Q
+        // buffers, which the states pass does not use; the rows leave as
+        // 16-byte pieces after the mid-chunk barrier.
 #pragma unroll
-        for (int rb = 0; rb < NKB; ++rb)
-          *reinterpret_cast<uint2*>(hb + (long)krow(rb, t & 3) * VD + 16 * w + 4 * (t >> 2)) =
+        for (int rb = 0; rb < NKB; ++rb) {
+          const int r = krow(rb, t & 3);
+          *reinterpret_cast<uint2*>((r < CH ? sQ0 : sQ1) + tix(r & (CH - 1), 16 * w + 4 * (t >> 2))) =
               pack4_bf16(quad_t(hs[rb][0]));
+        }
       }
     }
 
@@ -1420,13 +1424,11 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
               const int r = 16 * tt + acc_row(e);
               if (r < len) vb[(long)r * VD + vcol(0)] = vn[tt][0][e];
             }
-        } else {   // quad transposes as for the entry state: 8-byte row pieces
+        } else {   // quad transposes as for the entry state, staged in sO
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const uint2 u = pack4_bf16(quad_t(vn[tt][0]));
-            const int r = 16 * tt + 4 * q + (t & 3);
-            if (r < len) *reinterpret_cast<uint2*>(vb + (long)r * VD + 16 * w + 4 * (t >> 2)) = u;
-          }
+          for (int tt = 0; tt < 4; ++tt)
+            *reinterpret_cast<uint2*>(sO + tix(16 * tt + 4 * q + (t & 3), 16 * w + 4 * (t >> 2))) =
+                pack4_bf16(quad_t(vn[tt][0]));
         }
       }
       // h' = Gamma_n h + K^T (d * Vnew).
@@ -1471,6 +1473,22 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     }
     if (prev_out) store_o(prev_t0, prev_len);
     lds_barrier();  // P complete; the previous chunk's output rows are out of LDS
+    if (!F32 && keep) {   // the staged entry state and Vnew rows, 16-byte pieces
+      T* hb = (T*)p.hbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD;
+#pragma unroll
+      for (int i = threadIdx.x; i < KD * NCH; i += FNT) {
+        const int r = i / NCH, c = i % NCH;
+        const T* src = (r < CH ? sQ0 : sQ1) + ((r & (CH - 1)) * NCH + (c ^ stage_swz<NCH>(r))) * VEC;
+        *reinterpret_cast<uint4*>(hb + (long)r * VD + c * VEC) = *reinterpret_cast<const uint4*>(src);
+      }
+      const rsrc_t vr = make_rsrc((T*)p.vnew + ((long)h * s.Ttot + t0) * VD, (long)len * VD * (long)sizeof(T));
+#pragma unroll
+      for (int i = threadIdx.x; i < CH * NCH; i += FNT) {
+        const int r = i / NCH, c = i % NCH;
+        buf_store16(vr, (uint32_t)(r * VD + c * VEC) * (uint32_t)sizeof(T),
+                    *reinterpret_cast<const uint4*>(sO + (r * NCH + (c ^ stage_swz<NCH>(r))) * VEC));
+      }
+    }
 
     if (!warm && owner) {  // O += P Vnew
       if constexpr (F32) {
