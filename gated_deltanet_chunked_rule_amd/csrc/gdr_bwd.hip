@@ -222,6 +222,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   static_assert(NCB <= FNW && NKB % 2 == 0, "one column tile per wave, paired row tiles");
   __shared__ __align__(16) T sW0[CH * CH], sQ0[TE], sK0[TE], sO0[TE], sW1[CH * CH], sQ1[TE], sK1[TE], sO1[TE];
   __shared__ __align__(16) T sP[CH * PP];
+  __shared__ __align__(16) T sDh[TRANS ? 8 : KD * KD];   // staged dh rows of a chunk
   __shared__ __align__(16) float sG0[CH], sG1[CH], sD0[3 * CH], sD1[3 * CH];
   if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
     const T z = from_f<T>(0.f);
@@ -381,12 +382,15 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
     const float* sD = cur.D;
     const float* sM = cur.D + CH;
     const float glast = sG[len - 1];
-    if (keep && owner) {   // gradient of the state leaving the chunk, [K][V] rows
-      // 4x4 transposes within lane quads: one 8-byte row piece per lane and tile.
-      T* db = (T*)p.dhbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD + 16 * w + 4 * (t >> 2);
+    if constexpr (!TRANS) {
+      if (keep && owner) {   // gradient of the state leaving the chunk, [K][V] rows
+        // 4x4 transposes within lane quads give one 8-byte row piece per lane
+        // and tile, staged in LDS; the rows leave as 16-byte pieces after the
+        // P^T barrier.
 #pragma unroll
-      for (int rb = 0; rb < NKB; ++rb)
-        *reinterpret_cast<uint2*>(db + (long)krow(rb, t & 3) * VD) = pack4_bf16(quad_t(ds[rb]));
+        for (int rb = 0; rb < NKB; ++rb)
+          *reinterpret_cast<uint2*>(sDh + tix(krow(rb, t & 3), 16 * w + 4 * (t >> 2))) = pack4_bf16(quad_t(ds[rb]));
+      }
     }
     {  // P tiles (the ten lower ones and the masked (0,1), (2,3)), stored transposed
       constexpr int TI[12] = {3, 3, 2, 2, 3, 3, 2, 1, 1, 0, 0, 2};
@@ -467,6 +471,17 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
       }
     }
     lds_barrier();   // P^T complete
+    if constexpr (!TRANS) {
+      if (keep) {   // the staged dh rows to memory
+        T* db = (T*)p.dhbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD;
+#pragma unroll
+        for (int i = threadIdx.x; i < KD * NCH; i += FNT) {
+          const int r = i / NCH, c = i % NCH;
+          *reinterpret_cast<uint4*>(db + (long)r * VD + c * VEC) =
+              *reinterpret_cast<const uint4*>(sDh + (r * NCH + (c ^ stage_swz<NCH>(r))) * VEC);
+        }
+      }
+    }
     if (owner) {
       f32x4 dv[4];
 #pragma unroll
