@@ -166,8 +166,8 @@ SWEEP_TOKENS = (8192, 16384, 32768, 65536)   # tokens per update step, as 8192-t
 
 def train_step_sweep(torch, gdr, dev):
     """Training-step latency against tokens per update step for each value-head
-    count: one forward + backward through the autograd wrapper (the forward's
-    A reused by the backward), and the backward entry point alone.  Hq = Hv/2,
+    count: one forward + backward through the autograd wrapper (the backward
+    recomputes A), and the backward entry point alone (given the forward's A).  Hq = Hv/2,
     K = V = 128, bf16; inputs drawn on the device (q, k L2-normalised N(0,1),
     v and do N(0,1), g = log U(0.85, 1), beta = sigmoid(N(0,1)), no initial
     state), median of 5 calls with a cache flush before each."""

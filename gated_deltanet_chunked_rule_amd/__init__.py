@@ -306,18 +306,21 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, in
 class _GDRFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, options):
-        o, ht, _, A = gdr_chunk_fwd(q, k, v, g, beta, scale, initial_state, cu_seqlens,
-                                    output_final_state=True, output_A=True, options=options)
-        ctx.save_for_backward(q, k, v, g, beta, A, initial_state)
+        # A is not saved: the backward recomputes it (bitwise the same), which is
+        # faster than storing and reloading it and keeps 256 B per token and
+        # value head out of the saved activations
+        o, ht, _, _ = gdr_chunk_fwd(q, k, v, g, beta, scale, initial_state, cu_seqlens,
+                                    output_final_state=True, options=options)
+        ctx.save_for_backward(q, k, v, g, beta, initial_state)
         ctx.scale, ctx.cu_seqlens, ctx.options = scale, cu_seqlens, options
         return o, ht
 
     @staticmethod
     def backward(ctx, do, dht):
-        q, k, v, g, beta, A, h0 = ctx.saved_tensors
+        q, k, v, g, beta, h0 = ctx.saved_tensors
         do = torch.zeros_like(v) if do is None else do.contiguous().to(v.dtype)
         dht = None if dht is None else dht.contiguous().float()
-        dq, dk, dv, db, dg, dh0 = gdr_chunk_bwd(q, k, v, g, beta, A, do, dht, ctx.scale, h0,
+        dq, dk, dv, db, dg, dh0 = gdr_chunk_bwd(q, k, v, g, beta, None, do, dht, ctx.scale, h0,
                                                 ctx.cu_seqlens, options=ctx.options)
         return dq, dk, dv, dg, db, (dh0 if h0 is not None else None), None, None, None
 
