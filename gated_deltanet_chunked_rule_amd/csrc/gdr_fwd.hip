@@ -493,7 +493,9 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
 //      blocks from M and the A_ii as in k_intra.  A product's left factor must
 //      be in MFMA A layout (lane t holds row t): accumulator tiles get there
 //      through a per-wave LDS tile (written by columns, read by rows).
-//   4. A'' = A diag(b) rows in bf16 (and, with XA, A itself).
+//   4. A'' = A diag(b) rows in bf16 (and, with XA, A itself), staged as
+//      rows in the wave's LDS area (over the tiles of step 3) and written
+//      as 16-byte row pieces.
 // XA: 0 A'' only; 1 also A in fp32 (A_ws and/or A_out, element stores); 2 also
 // A in bf16 (A_bf, staged through LDS like A'').
 template <int KD, int XA>
