@@ -7,8 +7,8 @@ context-parallel split.  One step = one full forward pass (plan, intra-chunk
 WY, serial state, output) through the C ABI on resident device buffers.
 
 Prints ONE JSON line: tokens/s and ms per step (K steps between device
-syncs, nothing else in the timed region, after enough warmup steps for the
-GPU clocks to settle; with --graph the step is also captured once in a HIP
+syncs, nothing else in the timed region, after about 0.25 s of untimed
+steps and the W warmup steps so that the GPU clocks have settled; with --graph the step is also captured once in a HIP
 graph, checked bitwise against an eager step and replayed, and the replay
 rate is the value), the roofline of the dominant
 kernel (its mean HIP-event duration on the launch stream over K more steps,
@@ -238,6 +238,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration report")
     ap.add_argument("--no-sweep", action="store_true", help="skip the training-step sweep")
+    ap.add_argument("--settle-s", type=float, default=0.25,
+                    help="untimed steps for this many seconds before the warmup steps (GPU clocks)")
     ap.add_argument("--graph", action="store_true",
                     help="also time a HIP-graph replay of the step and report it as the value (default: eager launches)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -266,6 +268,14 @@ def main():
     def step():
         return gdr.gdr_chunk_fwd(q, k, v, g, beta, scale, workspace=ws)
 
+    # untimed clock settle (about 0.25 s of steps) before the W warmup steps:
+    # right after a cold start every kernel runs ~20 % slow until the GPU
+    # clocks reach their sustained state
+    settle0 = time.perf_counter()
+    while time.perf_counter() - settle0 < args.settle_s:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -381,7 +391,7 @@ def main():
                    "V": w.V, "chunk": 64, "cp_segment_chunks": plan["segment_chunks"],
                    "cp_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"],
                    "launch": "hip_graph" if args.graph else "eager"},
-        "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+        "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms, "settle_s": args.settle_s,
         "kernels_us": {n: 1e3 * t / c for n, (t, c) in kern.items()},
         "roofline": roof,
         "method_roofline": method_roof,
