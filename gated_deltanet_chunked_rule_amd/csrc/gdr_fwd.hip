@@ -1186,12 +1186,18 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   };
 
   if (cstart < cend) copy_chunk(cstart, ic<0>());
+  // The upper tiles (0,1) and (2,3) that the 32-token contraction steps of
+  // P Vnew read are always zero: written once here (published by the
+  // barrier below), never recomputed.
+  if constexpr (MODE == 0) {
+    for (int i = threadIdx.x; i < CH * PP; i += FNT) sP[i] = from_f<T>(0.f);
+  }
   wait_copies(cstart, ic<0>());
 
   // P tiles of this wave (rows of tile ti, columns of tile tj): the ten
-  // lower tiles and the upper tiles (0,1), (2,3) that the 32-token
-  // contraction steps read (masked to zero); waves 0-3 take two, waves 4-7 one.
-  const int pcnt = w < 4 ? 2 : 1;
+  // lower tiles; waves 0-3 take two, waves 4 and 5 one (the two zero tiles
+  // in the table's last places belong to no wave).
+  const int pcnt = w < 4 ? 2 : (w < 6 ? 1 : 0);
   int pti[2], ptj[2];
   {
     constexpr int TI[12] = {3, 3, 2, 2, 3, 3, 2, 1, 1, 0, 0, 2};
@@ -1249,7 +1255,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
     }
 
-    if (!warm) {  // P tiles of this wave
+    if (!warm && pcnt > 0) {  // P tiles of this wave
       // Masked scaled decays first (they do not depend on the products); the
       // gate cumsums of the lane's four rows are one 16-byte read.
       f32x4 dec[2];
@@ -1269,7 +1275,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           for (int m = 0; m < 2; ++m)
             pa[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[tix(16 * pti[m] + t, k0 + q)], sK[tix(16 * ptj[m] + t, k0 + q)],
                                                          pa[m], 0, 0, 0);
-      } else {
+      } else if (pcnt > 1) {
 #pragma unroll
         for (int k0 = 0; k0 < KD; k0 += 32) {
           bf16x8 fa[2], fb[2];
@@ -1280,6 +1286,13 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           }
 #pragma unroll
           for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[m], pa[m], 0, 0, 0);
+        }
+      } else {   // one tile
+#pragma unroll
+        for (int k0 = 0; k0 < KD; k0 += 32) {
+          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * pti[0] + t, k0 + 8 * q));
+          const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sK + tix(16 * ptj[0] + t, k0 + 8 * q));
+          pa[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, pa[0], 0, 0, 0);
         }
       }
 #pragma unroll
