@@ -360,6 +360,9 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   };
 
   if (crs >= cbeg) copy_chunk(crs, ic<0>());
+  // the upper P tiles (0,1) and (2,3) are always zero: written once here
+  // (published by the barrier below), never recomputed
+  for (int i = threadIdx.x; i < CH * PP; i += FNT) sP[i] = from_f<T>(0.f);
   wait_copies(crs, ic<0>());
 
   auto step = [&](auto bc, int jc) __attribute__((always_inline)) -> bool {
@@ -392,10 +395,10 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
           *reinterpret_cast<uint2*>(sDh + tix(krow(rb, t & 3), 16 * w + 4 * (t >> 2))) = pack4_bf16(quad_t(ds[rb]));
       }
     }
-    {  // P tiles (the ten lower ones and the masked (0,1), (2,3)), stored transposed
+    {  // P tiles (the ten lower ones; the masked (0,1), (2,3) stay zero from the start), stored transposed
       constexpr int TI[12] = {3, 3, 2, 2, 3, 3, 2, 1, 1, 0, 0, 2};
       constexpr int TJ[12] = {0, 1, 0, 1, 2, 3, 2, 0, 1, 0, 1, 3};
-      const int cnt = w < 4 ? 2 : 1;
+      const int cnt = w < 4 ? 2 : (w < 6 ? 1 : 0);
       int ti[2], tj[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -404,16 +407,25 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
         tj[m] = TJ[idx];
       }
       f32x4 pa[2] = {zero4(), zero4()};
+      if (cnt > 1) {
 #pragma unroll
-      for (int k0 = 0; k0 < KD; k0 += 32) {
-        bf16x8 fa[2], fb[2];
+        for (int k0 = 0; k0 < KD; k0 += 32) {
+          bf16x8 fa[2], fb[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          fa[m] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * ti[m] + t, k0 + 8 * q));
-          fb[m] = *reinterpret_cast<const bf16x8*>(sK + tix(16 * tj[m] + t, k0 + 8 * q));
+          for (int m = 0; m < 2; ++m) {
+            fa[m] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * ti[m] + t, k0 + 8 * q));
+            fb[m] = *reinterpret_cast<const bf16x8*>(sK + tix(16 * tj[m] + t, k0 + 8 * q));
+          }
+#pragma unroll
+          for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[m], pa[m], 0, 0, 0);
         }
+      } else if (cnt > 0) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[m], pa[m], 0, 0, 0);
+        for (int k0 = 0; k0 < KD; k0 += 32) {
+          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * ti[0] + t, k0 + 8 * q));
+          const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sK + tix(16 * tj[0] + t, k0 + 8 * q));
+          pa[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, pa[0], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
