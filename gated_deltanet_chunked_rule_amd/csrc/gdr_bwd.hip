@@ -278,7 +278,8 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
     crs = cend - 1;
     if (pseg == nseg - 1) ginit = p.dht ? p.dht + hbase : nullptr;
   } else if (certified) {
-    crs = min(cend + p.warmup, nch) - 1;
+    const int wu = short_warmup(p.cert + (long)h * s.NTtot + c0, cend, 1, nch - cend, p.warmup, p.log_eps);
+    crs = min(cend + wu, nch) - 1;
     if (crs == nch - 1) ginit = p.dht ? p.dht + hbase : nullptr;
   } else if (p.dhstart) {
     crs = cend - 1;

@@ -616,4 +616,29 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return x;
 }
 
+// Shortest warmup of a segment of a certified head: the fewest chunks (at
+// most W) whose gate mass already reaches log_eps, taking the window chunks
+// first, first + step, ... (step -1: the chunks before a segment start, for
+// the forward recurrence; +1: those after a segment end, for the reverse
+// pass), of which only `avail` exist.  The state error the warmup leaves is
+// bounded by e^(gate mass of the window) times the state's norm whatever the
+// window's length, so a shorter window that meets the threshold keeps the
+// certificate's bound.  Returns W when no shorter window does (the head
+// certificate holds for W, or the window reaches the sequence edge and runs
+// exactly).  Called by every lane of a wave, uniform arguments.
+__device__ __forceinline__ int short_warmup(const float* cert, int first, int step, int avail, int W,
+                                            float log_eps) {
+  const int l = lane_id();
+  const int n = min(W, avail);
+  float carry = 0.f;
+  for (int b = 0; b < n; b += 64) {
+    const int i = b + l;
+    const float x = wave_inclusive_scan(i < n ? cert[first + step * i] : 0.f) + carry;
+    const unsigned long long hit = __ballot(i < n && x <= log_eps);
+    if (hit) return b + __ffsll((long long)hit);   // lowest hitting lane, 1-based
+    carry = __shfl(x, 63, 64);
+  }
+  return W;
+}
+
 }  // namespace gdr

@@ -1059,7 +1059,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   } else if (certified) {
     cbeg = pseg * L;
     cend = min(cbeg + L, nch);
-    cstart = (pseg == 0) ? 0 : max(0, cbeg - p.warmup);
+    const int wu = short_warmup(p.cert + (long)h * s.NTtot + c0, cbeg - 1, -1, cbeg, p.warmup, p.log_eps);
+    cstart = (pseg == 0) ? 0 : max(0, cbeg - wu);
     write_final = (pseg == nseg - 1);
   } else if (exact) {
     cbeg = cstart = pseg * L;

@@ -84,7 +84,9 @@ typedef struct {
  * the `cp_warmup_chunks` chunks before it, which is exact up to a factor
  * exp(sum of g over those chunks).  A head whose every warmup window has
  * sum(g) <= cp_log_eps (and beta |k|^2 in [0, 2]) is certified and uses the
- * segments.  Any other head (for example one with g = 0) gets its segment
+ * segments; each segment of it then warms up over the fewest of those chunks
+ * (counted back from its start) whose sum(g) already reaches cp_log_eps, which
+ * keeps the same bound.  Any other head (for example one with g = 0) gets its segment
  * start states exactly instead: the map from a segment's start state to its
  * end state is affine, h_out = M h_in + b (the correction matrix the Tongyi
  * page describes for CP), so every segment's (M, b) is computed in parallel,
@@ -93,9 +95,9 @@ typedef struct {
  * never depend on an uncertified warmup.  The bf16 backward uses the same
  * segments for both of its serial passes: the recomputed chunk states as
  * above, and the reverse pass over the state gradient, whose segments start
- * at their ends after up to cp_warmup_chunks chunks of warmup (the reverse
- * map is the transposed M plus an offset); its certificate also covers the
- * windows after every segment end.  The fp32 backward runs each head whole.
+ * at their ends after up to cp_warmup_chunks chunks of warmup, again the
+ * fewest that reach cp_log_eps (the reverse map is the transposed M plus an
+ * offset); its certificate also covers the windows after every segment end.  The fp32 backward runs each head whole.
  * Pass NULL for the defaults; a zero-initialised struct also gives the
  * defaults. */
 typedef enum { GDR_CP_AUTO = 0, GDR_CP_OFF = 1, GDR_CP_FORCE = 2 } gdr_cp_mode;
@@ -103,7 +105,7 @@ typedef enum { GDR_CP_AUTO = 0, GDR_CP_OFF = 1, GDR_CP_FORCE = 2 } gdr_cp_mode;
 typedef struct {
   gdr_cp_mode cp_mode;       /* default GDR_CP_AUTO */
   int32_t cp_segment_chunks; /* GDR_CP_FORCE: chunks per segment (>= 1) */
-  int32_t cp_warmup_chunks;  /* warmup chunks before each segment; default 8 */
+  int32_t cp_warmup_chunks;  /* most warmup chunks before each segment; default 8 */
   float cp_log_eps;          /* certificate threshold on sum(g); default ln(1e-6) */
   int32_t cp_serial_fallback;/* 1: uncertified heads run serially; 0 (default): exact segment states */
 } gdr_options;
@@ -115,7 +117,7 @@ typedef struct {
   int32_t max_chunks;        /* longest sequence, in chunks */
   int32_t v_blocks;          /* state column blocks per workgroup of the state pass */
   int32_t segment_chunks;    /* chunks per CP segment (>= max_chunks: no CP) */
-  int32_t warmup_chunks;     /* warmup chunks per segment (0 without CP) */
+  int32_t warmup_chunks;     /* most warmup chunks per segment (0 without CP) */
   int32_t total_segments;    /* sum over sequences of ceil(chunks / segment_chunks) */
   int32_t state_workgroups;  /* workgroups of the state pass */
 } gdr_plan_info;
