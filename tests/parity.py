@@ -65,3 +65,14 @@ def head_slice(x, lo, hi, axis):
     idx = [slice(None)] * x.ndim
     idx[axis] = slice(lo, hi)
     return x[tuple(idx)]
+
+
+def set_chunk_gate_mass(inp, mass_of_chunk, chunk=64):
+    """Replace g by a per-chunk constant: every token of chunk c gets
+    mass_of_chunk(c) / chunk, so each full chunk's gate sum is mass_of_chunk(c)."""
+    g = inp["g"].clone()
+    T = g.shape[1]
+    for c in range((T + chunk - 1) // chunk):
+        g[:, c * chunk:(c + 1) * chunk, :] = mass_of_chunk(c) / chunk
+    inp["g"] = g
+    return inp

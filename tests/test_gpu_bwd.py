@@ -9,7 +9,7 @@ import torch
 
 import gated_deltanet_chunked_rule_amd as gdr
 import gdr_inputs as gi
-from parity import TOL, dev, f64, gpu_bwd, gpu_fwd, oracle_bwd, rel_err
+from parity import TOL, dev, f64, gpu_bwd, gpu_fwd, oracle_bwd, rel_err, set_chunk_gate_mass
 
 pytestmark = pytest.mark.gpu
 NAMES = ["dq", "dk", "dv", "dbeta", "dg", "dh0"]
@@ -163,6 +163,20 @@ def test_many_chunks_per_workgroup():
     w = gi.custom(B=1, T=64 * 600 + 17, Hq=2, Hv=4, K=128, V=128, dtype="bf16", seed=94, initial_state=True,
                   backward=True, gate=(0.9, 0.999))
     check_bwd(gi.make_inputs(w), qk_heads=(1, 2), label="many chunks per workgroup")
+
+
+def test_short_warmup_takes_enough_chunks_backward():
+    # Gate masses repeating (-0.5, -20, -1) per chunk: both the state pass
+    # (chunks before a segment start) and the reverse pass (chunks after a
+    # segment end) need exactly two warmup chunks; one leaves e^-1 or e^-0.5.
+    w = gi.custom(B=1, T=64 * 12 + 5, Hq=1, Hv=2, K=128, V=128, dtype="bf16", seed=44, initial_state=True,
+                  backward=True)
+    inp = set_chunk_gate_mass(gi.make_inputs(w), lambda c: (-0.5, -20.0, -1.0)[c % 3])
+    check_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 3, 4), label="stepped gates, warmup <= 4")
+    ref = oracle_bwd(inp)
+    loose = gpu_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 3, 1, -0.1))
+    torch.cuda.synchronize()
+    assert max(rel_err(x, r) for x, r in zip(loose, ref)) > 5e-2
 
 
 @pytest.mark.parametrize("K", [64, 128])

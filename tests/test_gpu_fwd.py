@@ -9,7 +9,7 @@ import torch
 import gated_deltanet_chunked_rule_amd as gdr
 import gdr_inputs as gi
 import oracle
-from parity import TOL, dev, f64, gpu_fwd, oracle_fwd, rel_err
+from parity import TOL, dev, f64, gpu_fwd, oracle_fwd, rel_err, set_chunk_gate_mass
 
 pytestmark = pytest.mark.gpu
 
@@ -160,6 +160,24 @@ def test_context_parallel_warmup_is_really_used():
     assert rel_err(o_ok, ro) <= TOL["bf16"]["o"]
     o_bad, _, _, _ = gpu_fwd(inp, gdr.Options(gdr.CP_FORCE, 4, 1, -1e-4))
     assert rel_err(o_bad, ro) > 5e-2
+
+
+# Per-chunk gate masses repeating (-0.5, -20, -1): the chunk just before each
+# segment start (and the first after each segment end) decays weakly, the one
+# beyond it strongly, so every segment needs a warmup of exactly two chunks
+# to meet ln(1e-6).  A one-chunk warmup leaves an error of e^-1 (forward) or
+# e^-0.5 (reverse) times the state: the loosened run shows that size.
+STEPPED_MASS = (-0.5, -20.0, -1.0)
+
+
+def test_short_warmup_takes_enough_chunks():
+    w = gi.custom(B=1, T=64 * 12 + 5, Hq=1, Hv=2, K=128, V=128, dtype="bf16", seed=43, initial_state=True)
+    inp = set_chunk_gate_mass(gi.make_inputs(w), lambda c: STEPPED_MASS[c % 3])
+    check_fwd(inp, gdr.Options(gdr.CP_FORCE, 3, 4), label="stepped gates, warmup <= 4")
+    ro, _ = oracle_fwd(inp)
+    o_one, _, _, _ = gpu_fwd(inp, gdr.Options(gdr.CP_FORCE, 3, 1, -0.1))
+    torch.cuda.synchronize()
+    assert rel_err(o_one, ro) > 5e-2
 
 
 @pytest.mark.parametrize("dtype,K,spread", [("bf16", 128, 0.3), ("f32", 64, 0.05)])
