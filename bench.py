@@ -389,7 +389,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "long_context", "B": w.B, "T": w.T, "Hq": w.Hq, "Hv": w.Hv, "K": w.K,
                    "V": w.V, "chunk": 64, "cp_segment_chunks": plan["segment_chunks"],
-                   "cp_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"],
+                   "cp_max_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"],
                    "launch": "hip_graph" if args.graph else "eager"},
         "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms, "settle_s": args.settle_s,
         "kernels_us": {n: 1e3 * t / c for n, (t, c) in kern.items()},
