@@ -180,6 +180,25 @@ def test_short_warmup_takes_enough_chunks():
     assert rel_err(o_one, ro) > 5e-2
 
 
+def test_short_warmup_longer_than_a_wave():
+    # Segment 1 starts at chunk 80, with up to 100 warmup chunks allowed.  In
+    # chunks 16..79 beta = 0 (the state only decays) with a gate mass of -0.02
+    # per chunk, and chunk 15 carries -13: the shortest window that meets
+    # ln(1e-6) is 65 chunks (-14.28), which spans two 64-lane blocks of the
+    # window scan; 64 chunks would leave e^-1.28 of the state.  The control
+    # certifies a 50-chunk window (mass -1) and must miss.
+    w = gi.custom(B=1, T=64 * 160, Hq=1, Hv=1, K=64, V=64, dtype="bf16", seed=45, initial_state=True)
+    inp = set_chunk_gate_mass(gi.make_inputs(w), lambda c: -0.02 if 16 <= c < 80 else (-13.0 if c == 15 else -1.0))
+    beta = inp["beta"].clone()
+    beta[:, 16 * 64:80 * 64, :] = 0.0
+    inp["beta"] = beta
+    check_fwd(inp, gdr.Options(gdr.CP_FORCE, 80, 100), label="65-chunk warmup")
+    ro, _ = oracle_fwd(inp)
+    o_short, _, _, _ = gpu_fwd(inp, gdr.Options(gdr.CP_FORCE, 80, 64, -1.0))
+    torch.cuda.synchronize()
+    assert rel_err(o_short, ro) > 5e-2
+
+
 @pytest.mark.parametrize("dtype,K,spread", [("bf16", 128, 0.3), ("f32", 64, 0.05)])
 def test_nearly_parallel_keys_without_decay(dtype, K, spread):
     # Strongly coupled intra-chunk systems (I + L): keys share one direction
