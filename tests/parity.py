@@ -76,3 +76,21 @@ def set_chunk_gate_mass(inp, mass_of_chunk, chunk=64):
         g[:, c * chunk:(c + 1) * chunk, :] = mass_of_chunk(c) / chunk
     inp["g"] = g
     return inp
+
+
+# Per-value-head gate mass per full chunk; with ln(1e-6) the shortest warmup
+# is 7, 3, -, 1, 5, 2, -, 6 chunks (two heads would need more than 8 and take
+# the exact path), so the heads of one q/k group start their segments at
+# different chunks.
+HEAD_MASS = (2.0, 5.0, 1.5, 14.0, 3.0, 7.0, 0.5, 2.5)
+
+
+def head_mass_inputs(backward=False):
+    import gdr_inputs as gi
+    w = gi.custom(B=1, Hq=2, Hv=8, K=128, V=128, dtype="bf16", seed=46, initial_state=True, backward=backward)
+    inp = gi.packed_from_lengths(w, [64 * 9 + 7, 64 * 5, 64 * 12 + 3, 30])
+    g = torch.empty_like(inp["g"])
+    for h, m in enumerate(HEAD_MASS):
+        g[..., h] = -m / 64
+    inp["g"] = g
+    return inp

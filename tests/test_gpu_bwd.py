@@ -9,7 +9,7 @@ import torch
 
 import gated_deltanet_chunked_rule_amd as gdr
 import gdr_inputs as gi
-from parity import TOL, dev, f64, gpu_bwd, gpu_fwd, oracle_bwd, rel_err, set_chunk_gate_mass
+from parity import TOL, dev, f64, gpu_bwd, gpu_fwd, head_mass_inputs, oracle_bwd, rel_err, set_chunk_gate_mass
 
 pytestmark = pytest.mark.gpu
 NAMES = ["dq", "dk", "dv", "dbeta", "dg", "dh0"]
@@ -177,6 +177,13 @@ def test_short_warmup_takes_enough_chunks_backward():
     loose = gpu_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 3, 1, -0.1))
     torch.cuda.synchronize()
     assert max(rel_err(x, r) for x, r in zip(loose, ref)) > 5e-2
+
+
+def test_warmup_length_differs_per_head_varlen_backward():
+    # per-value-head gate masses (shortest warmups 7, 3, -, 1, 5, 2, -, 6
+    # chunks; two heads exact), packed sequences, four value heads per q/k head
+    check_bwd(head_mass_inputs(backward=True), options=gdr.Options(gdr.CP_FORCE, 3, 8),
+              label="per-head warmups, varlen, G=4")
 
 
 @pytest.mark.parametrize("K", [64, 128])

@@ -9,7 +9,7 @@ import torch
 import gated_deltanet_chunked_rule_amd as gdr
 import gdr_inputs as gi
 import oracle
-from parity import TOL, dev, f64, gpu_fwd, oracle_fwd, rel_err, set_chunk_gate_mass
+from parity import TOL, dev, f64, gpu_fwd, head_mass_inputs, oracle_fwd, rel_err, set_chunk_gate_mass
 
 pytestmark = pytest.mark.gpu
 
@@ -197,6 +197,10 @@ def test_short_warmup_longer_than_a_wave():
     o_short, _, _, _ = gpu_fwd(inp, gdr.Options(gdr.CP_FORCE, 80, 64, -1.0))
     torch.cuda.synchronize()
     assert rel_err(o_short, ro) > 5e-2
+
+
+def test_warmup_length_differs_per_head_varlen():
+    check_fwd(head_mass_inputs(), gdr.Options(gdr.CP_FORCE, 3, 8), label="per-head warmups, varlen, G=4")
 
 
 @pytest.mark.parametrize("dtype,K,spread", [("bf16", 128, 0.3), ("f32", 64, 0.05)])
