@@ -170,8 +170,9 @@ def test_context_parallel_warmup_is_really_used():
 STEPPED_MASS = (-0.5, -20.0, -1.0)
 
 
-def test_short_warmup_takes_enough_chunks():
-    w = gi.custom(B=1, T=64 * 12 + 5, Hq=1, Hv=2, K=128, V=128, dtype="bf16", seed=43, initial_state=True)
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 64)])
+def test_short_warmup_takes_enough_chunks(dtype, K):
+    w = gi.custom(B=1, T=64 * 12 + 5, Hq=1, Hv=2, K=K, V=K, dtype=dtype, seed=43, initial_state=True)
     inp = set_chunk_gate_mass(gi.make_inputs(w), lambda c: STEPPED_MASS[c % 3])
     check_fwd(inp, gdr.Options(gdr.CP_FORCE, 3, 4), label="stepped gates, warmup <= 4")
     ro, _ = oracle_fwd(inp)
