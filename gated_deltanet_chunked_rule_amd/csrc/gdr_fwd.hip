@@ -1223,10 +1223,6 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const bool keep = st_mode && jc >= cbeg;             // store the entry state and Vnew
     const bool more = jc + 1 < cend;
     const FusedBufs<T> cur = bufs(bc);
-    if (more) {
-      copy_part(jc + 1, ic<1 - b>(), 0);
-      copy_part(jc + 1, ic<1 - b>(), 1);
-    }
     const T* sW = cur.W;
     const T* sQ = cur.Q;
     const T* sK = cur.K;
@@ -1316,9 +1312,9 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
     }
 
-    if (more) {
-      copy_part(jc + 1, ic<1 - b>(), 2);
-      copy_part(jc + 1, ic<1 - b>(), 3);
+    if (more) {   // the next chunk's tiles, issued once this wave's P reads are out
+#pragma unroll
+      for (int piece = 0; piece < 4; ++piece) copy_part(jc + 1, ic<1 - b>(), piece);
     }
     f32x4 vn[4][CBW], oa[4][CBW];
 #pragma unroll
