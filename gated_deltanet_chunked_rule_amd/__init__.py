@@ -166,6 +166,22 @@ def _shape(q, v, cu_host):
     return _Shape(B, T, Hq, Hv, K, V, N, _dtype_code(q.dtype)), N
 
 
+def _check_shapes(q, k, v, g, beta, N, initial_state=None, A=None, do=None, dht=None):
+    """Shape agreement of every tensor argument with q [B,T,Hq,K] and v
+    [B,T,Hv,V], checked before anything reaches the library (whose C ABI sees
+    bare pointers and would read past a wrongly shaped tensor)."""
+    if q.dim() != 4 or v.dim() != 4:
+        raise GdrError("q and v must be 4-D: [B, T, Hq, K] and [B, T, Hv, V]")
+    B, T, Hq, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    want = {"k": (k, (B, T, Hq, K)), "v": (v, (B, T, Hv, V)), "g": (g, (B, T, Hv)),
+            "beta": (beta, (B, T, Hv)), "initial_state": (initial_state, (N, Hv, K, V)),
+            "A": (A, (B, T, Hv, 64)), "do": (do, (B, T, Hv, V)), "dht": (dht, (N, Hv, K, V))}
+    for name, (t, shape) in want.items():
+        if t is not None and tuple(t.shape) != shape:
+            raise GdrError(f"shape mismatch: {name} is {tuple(t.shape)}, expected {shape}")
+
+
 def _host_ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -214,19 +230,18 @@ def gdr_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=N
     """Forward chunked prefill.  Returns (o, final_state, g_cum, A); the last
     three are None unless requested."""
     lib = load_library()
+    cu_host = None if cu_seqlens is None else torch.as_tensor(cu_seqlens).detach().to("cpu", torch.int32)
+    _check_shapes(q, k, v, g, beta, q.shape[0] if cu_host is None else cu_host.numel() - 1,
+                  initial_state=initial_state)
     _need(q, "q"); _need(k, "k", q.dtype); _need(v, "v", q.dtype)
     _need(g, "g", torch.float32); _need(beta, "beta", torch.float32)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32)
     dev = q.device
     cu_dev, cu_host = _cu_pair(cu_seqlens, dev)
     sh, N = _shape(q, v, cu_host)
     B, T, Hq, K = q.shape
     Hv, V = v.shape[2], v.shape[3]
-    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
-        raise GdrError("shape mismatch among q, k, v, g, beta")
-    if initial_state is not None:
-        _need(initial_state, "initial_state", torch.float32)
-        if initial_state.shape != (N, Hv, K, V):
-            raise GdrError(f"initial_state must be {(N, Hv, K, V)}")
     scale = K ** -0.5 if scale is None else float(scale)
     o = torch.empty_like(v)
     ht = torch.empty((N, Hv, K, V), device=dev, dtype=torch.float32) if output_final_state else None
@@ -251,6 +266,9 @@ def gdr_chunk_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=N
                   cu_seqlens=None, *, options=None, workspace=None, stream=None):
     """Backward of gdr_chunk_fwd.  Returns (dq, dk, dv, dbeta, dg, dh0)."""
     lib = load_library()
+    cu_host = None if cu_seqlens is None else torch.as_tensor(cu_seqlens).detach().to("cpu", torch.int32)
+    _check_shapes(q, k, v, g, beta, q.shape[0] if cu_host is None else cu_host.numel() - 1,
+                  initial_state=initial_state, A=A, do=do, dht=dht)
     _need(q, "q"); _need(k, "k", q.dtype); _need(v, "v", q.dtype); _need(do, "do", q.dtype)
     _need(g, "g", torch.float32); _need(beta, "beta", torch.float32)
     dev = q.device
@@ -258,8 +276,6 @@ def gdr_chunk_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=N
     sh, N = _shape(q, v, cu_host)
     B, T, Hq, K = q.shape
     Hv, V = v.shape[2], v.shape[3]
-    if do.shape != v.shape:
-        raise GdrError("do must have the shape of v")
     if A is not None:
         _need(A, "A", torch.float32)
     if dht is not None:

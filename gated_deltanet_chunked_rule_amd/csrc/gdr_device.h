@@ -549,16 +549,22 @@ __device__ __forceinline__ uint2 pack4_bf16(f32x4 x) {
 }
 
 // CP certificate of one head, called by every thread of the workgroup; cert
-// points at the head's first chunk of the sequence.  Each warmup window must
-// carry a gate mass of at most log_eps (and keys inside the contraction
-// range, which the per-chunk value encodes as +inf otherwise): forward
-// windows are the W chunks before a segment start that does not reach back
-// to the sequence start; with rev, also the W chunks after each segment end
-// that do not reach the sequence end (the reverse pass of the backward starts
-// there from zero).
+// points at the head's first chunk of the sequence.  The per-chunk value is
+// the chunk's gate mass, or +inf when a token of the chunk has g > 0 or
+// beta |k|^2 outside [0, 2].  With more than one segment, every chunk of the
+// sequence must be finite, so that every token transition (forward, and
+// transposed in the reverse pass) is a contraction and a warmup error never
+// grows after its window; and each warmup window must carry a gate mass of
+// at most log_eps: forward windows are the W chunks before a segment start
+// that does not reach back to the sequence start; with rev, also the W chunks
+// after each segment end that do not reach the sequence end (the reverse pass
+// of the backward starts there from zero).
 __device__ __forceinline__ bool head_certified(const float* cert, int nseg, int nch, int L, int W,
                                                float log_eps, bool rev) {
   int ok = 1;
+  if (nseg > 1)
+    for (int cc = (int)threadIdx.x; cc < nch; cc += (int)blockDim.x)
+      if (!(cert[cc] <= 0.f)) ok = 0;
   for (int qq = 1 + (int)threadIdx.x; qq < nseg; qq += (int)blockDim.x) {
     const int ws = qq * L - W;
     if (ws > 0) {

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
   constexpr int NKV = 2;                      // staged row tiles: K and V
   __shared__ __align__(16) char smem[NKV * SZ_K + SZ_F + SZ_X];
   __shared__ float sG[CH], sB[CH];
-  __shared__ int sFlag[NWAVE];
+  __shared__ int sFlag[NWAVE + 1];   // per-wave key-range flags, then the gate-sign flag
   T* sK = reinterpret_cast<T*>(smem);
   T* sV = reinterpret_cast<T*>(smem + (NKV - 1) * SZ_K);
   float* sF = reinterpret_cast<float*>(smem + NKV * SZ_K);
@@ -255,6 +255,9 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
       const float gc = wave_inclusive_scan((l < len) ? gvc : 0.f);
       sG[l] = gc;
       sB[l] = (l < len) ? bvc : 0.f;
+      // a token with g > 0 (or a NaN gate) voids the certificate
+      const bool gpos = __builtin_amdgcn_ballot_w64(l < len && !(gvc <= 0.f)) != 0;
+      if (l == 0) sFlag[NWAVE] = gpos ? 1 : 0;
       if (l < len) {
         p.gcum[(long)h * s.Ttot + t0 + l] = gc;
         if (p.g_cum_out) p.g_cum_out[(long)(t0 + l) * p.Hv + h] = gc;
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(NTHR, 3) void k_intra(IntraParams p, int total_item
     }
     lds_barrier();
     if (tid == 0) {
-      const int any_bad = sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3];
+      const int any_bad = sFlag[0] | sFlag[1] | sFlag[2] | sFlag[3] | sFlag[NWAVE];
       p.cert[(long)h * s.NTtot + it.c] = any_bad ? INFINITY : sG[len - 1];
     }
 
@@ -597,6 +600,9 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
       }
     }
   }
+  // a token with g > 0 (or a NaN gate) also voids the certificate: the
+  // contraction bound of the warmup error needs every gate in (0, 1]
+  bad |= (l < len && !(gv <= 0.f)) ? 1 : 0;
   const bool any_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
   if (l == 0) p.cert[(long)h * s.NTtot + c] = any_bad ? INFINITY : sG[len - 1];
 

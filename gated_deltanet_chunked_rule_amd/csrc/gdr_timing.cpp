@@ -3,8 +3,11 @@
 // When enabled, each launch is bracketed by two events recorded on the launch
 // stream.  gdr_timing_collect() waits for the pending pairs and folds their
 // elapsed times into per-kernel totals.  Event objects are pooled and reused.
+// With timing off (the default) a launch reads one atomic flag and takes no
+// lock: the registry below is touched only while timing is on.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -26,7 +29,7 @@ struct Totals {
 };
 
 std::mutex g_mu;
-bool g_enabled = false;
+std::atomic<bool> g_enabled{false};
 std::vector<hipEvent_t> g_pool;
 std::vector<Pending> g_pending;
 std::vector<std::pair<std::string, Totals>> g_totals;
@@ -49,17 +52,17 @@ hipEvent_t get_event() {
 namespace gdr {
 
 void timing_before(const char* name, hipStream_t st) {
-  std::lock_guard<std::mutex> lk(g_mu);
   t_start = nullptr;
-  if (!g_enabled) return;
+  if (!g_enabled.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_mu);
   t_start = get_event();
   t_name = name;
   if (t_start) (void)hipEventRecord(t_start, st);
 }
 
 void timing_after(hipStream_t st) {
+  if (!t_start) return;   // timing was off when this launch began
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_enabled || !t_start) return;
   hipEvent_t end = get_event();
   if (!end) return;
   (void)hipEventRecord(end, st);
@@ -71,10 +74,7 @@ void timing_after(hipStream_t st) {
 
 extern "C" {
 
-void gdr_timing_enable(int enable) {
-  std::lock_guard<std::mutex> lk(g_mu);
-  g_enabled = enable != 0;
-}
+void gdr_timing_enable(int enable) { g_enabled.store(enable != 0, std::memory_order_relaxed); }
 
 int gdr_timing_collect(void) {
   std::vector<Pending> todo;

@@ -36,7 +36,9 @@
  *   cu_seqlens        [N + 1] int32 token offsets (packed mode, B must be 1)
  *   N = B without cu_seqlens, N = shape->num_seqs with it.
  * Heads: value head h reads query/key head h / (Hv / Hq) (contiguous groups).
- * Gate: g is the per-token log-gate (decay exp(g)); g <= 0 is expected.
+ * Gate: g is the per-token log-gate (decay exp(g)); g <= 0 is expected.  A
+ *   head with any g > 0 is still computed exactly, but never from a warmup
+ *   (see the context-parallel options below).
  * Chunks: 64 tokens, restarting at every sequence start; the last chunk of a
  *   sequence may be short.
  * Supported: K, V in {32, 64, 128} with K == V; Hv a multiple of Hq;
@@ -82,9 +84,11 @@ typedef struct {
  * too few to fill the GPU, each sequence is cut into segments of
  * `cp_segment_chunks` chunks; a segment's start state is rebuilt from zero over
  * the `cp_warmup_chunks` chunks before it, which is exact up to a factor
- * exp(sum of g over those chunks).  A head whose every warmup window has
- * sum(g) <= cp_log_eps (and beta |k|^2 in [0, 2]) is certified and uses the
- * segments; each segment of it then warms up over the fewest of those chunks
+ * exp(sum of g over those chunks) as long as every token transition is a
+ * contraction (g <= 0 and 0 <= beta |k|^2 <= 2).  A head is certified, and
+ * uses the segments, when every token of the sequence meets those two
+ * conditions and every warmup window has sum(g) <= cp_log_eps; each segment
+ * of it then warms up over the fewest of those chunks
  * (counted back from its start) whose sum(g) already reaches cp_log_eps, which
  * keeps the same bound.  Any other head (for example one with g = 0) gets its segment
  * start states exactly instead: the map from a segment's start state to its

@@ -150,3 +150,53 @@ def test_bwd_fp32_k64_unsupported():
     sh = shape(K=64, V=64)
     assert lib.gdr_chunk_bwd_workspace_size(ctypes.byref(sh), None, None) == 0
     assert "fp32 backward" in last_error()
+
+
+def _bwd_args(B=1, T=130, Hq=2, Hv=4, K=64, N=None):
+    """CPU tensors of matching shapes for gdr_chunk_bwd (never launched)."""
+    N = B if N is None else N
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(s, dtype=dt)
+    return dict(q=z(B, T, Hq, K), k=z(B, T, Hq, K), v=z(B, T, Hv, K), g=z(B, T, Hv, dt=torch.float32),
+                beta=z(B, T, Hv, dt=torch.float32), A=z(B, T, Hv, 64, dt=torch.float32), do=z(B, T, Hv, K),
+                dht=z(N, Hv, K, K, dt=torch.float32), initial_state=z(N, Hv, K, K, dt=torch.float32))
+
+
+def _call_bwd(a, cu_seqlens=None):
+    return gdr.gdr_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A"], a["do"], a["dht"], None,
+                             a["initial_state"], cu_seqlens)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("k", (1, 130, 2, 32)), ("k", (1, 130, 1, 64)), ("v", (1, 129, 4, 64)), ("g", (1, 130, 2)),
+    ("beta", (1, 130, 4, 1)), ("A", (1, 130, 4, 32)), ("do", (1, 130, 4, 32)), ("dht", (2, 4, 64, 64)),
+    ("initial_state", (1, 4, 64, 32)),
+])
+def test_bwd_binding_rejects_mismatched_shapes(name, bad):
+    # Every tensor's shape is checked against q and v before anything reaches
+    # the library (whose C ABI sees bare pointers); CPU tensors show the order:
+    # a shape error comes first, and matching shapes only then fail on the
+    # device check, so no call here gets near a launch.
+    a = _bwd_args()
+    a[name] = torch.zeros(bad, dtype=a[name].dtype)
+    with pytest.raises(gdr.GdrError, match=f"shape mismatch: {name} "):
+        _call_bwd(a)
+
+
+def test_bwd_binding_checks_states_against_packed_sequences():
+    a = _bwd_args(T=200, N=3)
+    cu = torch.tensor([0, 70, 70, 200], dtype=torch.int32)
+    with pytest.raises(gdr.GdrError, match="must be a device tensor"):
+        _call_bwd(a, cu)                    # N = 3 sequences: states [3, Hv, K, V] match
+    a["dht"] = torch.zeros((1, 4, 64, 64))
+    with pytest.raises(gdr.GdrError, match="shape mismatch: dht "):
+        _call_bwd(a, cu)
+
+
+def test_fwd_binding_rejects_mismatched_shapes():
+    a = _bwd_args()
+    with pytest.raises(gdr.GdrError, match="must be a device tensor"):
+        gdr.gdr_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], None, a["initial_state"])
+    with pytest.raises(gdr.GdrError, match="shape mismatch: beta "):
+        gdr.gdr_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"][:, :5], None, a["initial_state"])
+    with pytest.raises(gdr.GdrError, match="shape mismatch: initial_state "):
+        gdr.gdr_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], None, a["initial_state"][:, :2])

@@ -114,9 +114,85 @@ def test_deterministic():
         assert torch.equal(a, b)
 
 
-def test_backward_workload_full_size_sampled_heads():
+def test_backward_workload_full_size_all_heads():
+    # the backward workload (B=2, T=16384, Hq=16, Hv=32) with every head
+    # compared: dq, dk, dv, dbeta, dg, dh0 element by element
     inp = gi.make_inputs(gi.WORKLOADS["backward"])
-    check_bwd(inp, qk_heads=(0, 1), label="backward heads 0-1")
+    check_bwd(inp, label="backward workload, all heads")
+
+
+def _autograd_vs_oracle(inp, label):
+    # o, final_state and the gradients of <o, do> + <final_state, dht> through
+    # the differentiable wrapper (the training-step path: forward, autograd,
+    # backward with A recomputed), against the oracle's recurrence and reverse
+    # mode on the same inputs
+    w = inp["workload"]
+    print(f"[autograd] {label} T={inp['q'].shape[1]} Hq={w.Hq} Hv={w.Hv} B={w.B}", flush=True)
+    leaves = [dev(inp[n]).requires_grad_(True) for n in ("q", "k", "v", "g", "beta")]
+    h0 = dev(inp["initial_state"])
+    if h0 is not None:
+        h0.requires_grad_(True)
+    cu = inp["cu_seqlens"]
+    o, ht = gdr.chunk_gated_delta_rule(*leaves, inp["scale"], h0, output_final_state=True,
+                                       cu_seqlens=None if cu is None else dev(cu))
+    wrt = leaves + ([h0] if h0 is not None else [])
+    grads = torch.autograd.grad([o, ht], wrt, [dev(inp["do"]), dev(inp["dht"])])
+    torch.cuda.synchronize()
+    ro, rht = oracle_fwd(inp)
+    rdq, rdk, rdv, rdb, rdg, rdh0 = oracle_bwd(inp)
+    errs = {"o": rel_err(o.detach(), ro), "final_state": rel_err(ht.detach(), rht)}
+    for name, x, r in zip(("dq", "dk", "dv", "dg", "dbeta"), grads, (rdq, rdk, rdv, rdg, rdb)):
+        errs[name] = rel_err(x, r)
+    if h0 is not None:
+        errs["dh0"] = rel_err(grads[5], rdh0)
+    print("      " + " ".join(f"err({k})={v:.3e}" for k, v in errs.items()), flush=True)
+    for name, e in errs.items():
+        bound = TOL["bf16"]["o"] if name == "o" else TOL["bf16"]["grad"]
+        if name in ("final_state", "dh0"):
+            bound = TOL["bf16"]["final_state"]
+        assert np.isfinite(e) and e <= bound, (name, e)
+
+
+def test_training_step_through_autograd_matches_oracle():
+    # one training-step shape of the value-head sweep (Hv = 24, the TP-style
+    # share; Hq = Hv / 2; two 8192-token sequences; no initial state)
+    w = gi.custom(B=2, T=8192, Hq=12, Hv=24, K=128, V=128, dtype="bf16", seed=95, backward=True)
+    _autograd_vs_oracle(gi.make_inputs(w), "sweep shape Hv=24")
+
+
+def test_training_step_through_autograd_packed_with_state():
+    # Hv = 48 with packed sequences of unequal length and per-sequence initial
+    # states (dh0 through autograd)
+    w = gi.custom(B=1, Hq=24, Hv=48, K=128, V=128, dtype="bf16", seed=96, initial_state=True, backward=True)
+    _autograd_vs_oracle(gi.packed_from_lengths(w, [3000, 4096, 96, 1000]), "packed Hv=48")
+
+
+def test_certificate_excludes_positive_gates_and_expanding_keys_backward():
+    # As in the forward test: fast decay (-7.5 per chunk) would certify every
+    # head on 2-chunk windows, before each segment start (chunks 4-5, 10-11)
+    # and after each segment end (chunks 6-7, 12-13); head 1 has g > 0 and
+    # head 2 one beta |k|^2 = 3 token in chunks 8-9, inside no window.  With
+    # the serial fallback those heads run whole in both serial passes, so
+    # their gradients equal the unsegmented call's bitwise (G = 1: dq and dk
+    # of a q/k head come from its one value head), while a certified head's
+    # per-token gradients next to a segment boundary carry the warmup error.
+    w = gi.custom(B=1, T=64 * 16 + 9, Hq=4, Hv=4, K=128, V=128, dtype="bf16", seed=48, initial_state=True,
+                  backward=True)
+    inp = set_chunk_gate_mass(gi.make_inputs(w), lambda c: -7.5)
+    g, beta = inp["g"].clone(), inp["beta"].clone()
+    g[0, 8 * 64 + 10:8 * 64 + 13, 1] = 0.2
+    beta[0, 9 * 64 + 20, 2] = 3.0
+    inp["g"], inp["beta"] = g, beta
+    check_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 6, 2), label="g > 0 and beta |k|^2 > 2 in segment bodies")
+    off = gpu_bwd(inp, options=gdr.Options(gdr.CP_OFF))
+    ser = gpu_bwd(inp, options=gdr.Options(gdr.CP_FORCE, 6, 2, 0.0, 1))
+    torch.cuda.synchronize()
+    for h in (1, 2):
+        for name, a, b in zip(NAMES, ser, off):
+            x, y = (a[:, h], b[:, h]) if name == "dh0" else (a[:, :, h], b[:, :, h])
+            assert torch.equal(x, y), (name, h)
+    for h in (0, 3):   # fp32 dg and dbeta of a certified head differ somewhere
+        assert not (torch.equal(ser[4][:, :, h], off[4][:, :, h]) and torch.equal(ser[3][:, :, h], off[3][:, :, h])), h
 
 
 # CP segments in the backward (bf16): both serial passes (the recomputed

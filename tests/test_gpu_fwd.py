@@ -109,8 +109,13 @@ def test_auxiliary_outputs_g_cum_and_A():
     cu = inp["cu_seqlens"].numpy()
     rg = oracle.chunk_gcum(f64(inp["g"]), cu)
     rA = oracle.chunk_A(f64(inp["k"]), f64(inp["g"]), f64(inp["beta"]), 4, cu)
-    assert np.max(np.abs(f64(gc) - rg)) <= 1e-5
-    assert rel_err(A, rA) <= 1e-3
+    eg, eA = float(np.max(np.abs(f64(gc) - rg))), rel_err(A, rA)
+    print(f"[fwd] g_cum max abs err {eg:.3e}, A err {eA:.3e}", flush=True)
+    # fp32 outputs of bf16 inputs: exact up to fp32 rounding (K K^T of bf16
+    # keys is exact in fp32 products; the cumsum, the decays and the blocked
+    # inverse add a few ulps), so a half-precision A would fail by far
+    assert eg <= 1e-5
+    assert eA <= 1e-5
 
 
 def test_deterministic():
@@ -133,17 +138,30 @@ def test_long_context_workload_full_size():
     check_fwd(inp)
 
 
-def test_varlen_workload_full_size_sampled_heads():
+def test_varlen_workload_full_size_all_heads():
+    # Every value head of the packed workload (16 sequences, 131072 tokens,
+    # Hv = 64) against the oracle, o and final_state element by element.  The
+    # oracle runs one q/k head group at a time (4 q/k heads = 16 value heads,
+    # sliced consistently with the head map) to bound host memory.
     inp = gi.make_inputs(gi.WORKLOADS["varlen"])
     w = inp["workload"]
+    G = w.Hv // w.Hq
     print(f"[fwd] varlen lengths={np.diff(inp['cu_seqlens'].numpy()).tolist()}", flush=True)
     o, ht, _, _ = gpu_fwd(inp)
     torch.cuda.synchronize()
-    for lo, hi in ((0, 2), (37, 39)):
-        ro, rht = oracle_fwd(inp, heads=(lo, hi))
-        eo, eh = rel_err(o, ro), rel_err(ht, rht)
-        print(f"      heads [{lo},{hi}) err(o)={eo:.3e} err(final_state)={eh:.3e}", flush=True)
-        assert eo <= TOL["bf16"]["o"] and eh <= TOL["bf16"]["final_state"]
+    o, ht = o.cpu(), ht.cpu()
+    worst_o = worst_h = 0.0
+    for a in range(0, w.Hq, 4):
+        b = min(w.Hq, a + 4)
+        part = dict(inp, q=inp["q"][:, :, a:b], k=inp["k"][:, :, a:b], v=inp["v"][:, :, a * G:b * G],
+                    g=inp["g"][:, :, a * G:b * G], beta=inp["beta"][:, :, a * G:b * G],
+                    initial_state=inp["initial_state"][:, a * G:b * G])
+        ro, rht = oracle_fwd(part)
+        eo, eh = rel_err(o[:, :, a * G:b * G], ro), rel_err(ht[:, a * G:b * G], rht)
+        print(f"      value heads [{a * G},{b * G}) err(o)={eo:.3e} err(final_state)={eh:.3e}", flush=True)
+        assert eo <= TOL["bf16"]["o"] and eh <= TOL["bf16"]["final_state"], (a, eo, eh)
+        worst_o, worst_h = max(worst_o, eo), max(worst_h, eh)
+    print(f"      all 64 value heads: worst err(o)={worst_o:.3e} err(final_state)={worst_h:.3e}", flush=True)
 
 
 def test_context_parallel_warmup_is_really_used():
@@ -334,3 +352,32 @@ def test_zero_beta_state_only_decays():
     rht = decay[-1][:, None, None] * s0
     assert rel_err(o[0], ro) <= TOL["f32"]["o"]
     assert rel_err(ht[0], rht) <= TOL["f32"]["final_state"]
+
+
+def test_certificate_excludes_positive_gates_and_expanding_keys():
+    # Every head decays fast (gate mass -7.5 per chunk: a 2-chunk warmup meets
+    # ln(1e-6)), so by its windows alone every head would take the warmup
+    # path.  Head 1 has three tokens with g > 0 and head 2 one token with
+    # beta |k|^2 = 3 (a transition that expands the state), both in chunks
+    # that lie in no warmup window (segments of 6 chunks, windows of 2: chunks
+    # 4-5 and 10-11).  Such heads must not be certified: a warmup error could
+    # grow there.  With the serial fallback an uncertified head runs whole,
+    # so its outputs equal the unsegmented call bitwise, while a certified
+    # head's outputs at a segment start carry the warmup's e^-15 relative
+    # error and differ in fp32.  The default (exact segment states) matches
+    # the oracle on every head.
+    w = gi.custom(B=1, T=64 * 16 + 9, Hq=4, Hv=4, K=64, V=64, dtype="f32", seed=47, initial_state=True)
+    inp = set_chunk_gate_mass(gi.make_inputs(w), lambda c: -7.5)
+    g, beta = inp["g"].clone(), inp["beta"].clone()
+    g[0, 8 * 64 + 10:8 * 64 + 13, 1] = 0.2
+    beta[0, 9 * 64 + 20, 2] = 3.0
+    inp["g"], inp["beta"] = g, beta
+    check_fwd(inp, gdr.Options(gdr.CP_FORCE, 6, 2), label="g > 0 and beta |k|^2 > 2 in segment bodies")
+    o_off, h_off, _, _ = gpu_fwd(inp, gdr.Options(gdr.CP_OFF))
+    o_ser, h_ser, _, _ = gpu_fwd(inp, gdr.Options(gdr.CP_FORCE, 6, 2, 0.0, 1))
+    torch.cuda.synchronize()
+    for h in (1, 2):
+        assert torch.equal(o_ser[:, :, h], o_off[:, :, h]) and torch.equal(h_ser[:, h], h_off[:, h]), h
+    seg1 = slice(6 * 64, 7 * 64)   # first chunk of segment 1
+    for h in (0, 3):
+        assert not torch.equal(o_ser[:, seg1, h], o_off[:, seg1, h]), h
