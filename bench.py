@@ -10,10 +10,13 @@ Prints ONE JSON line: tokens/s and ms per step (K steps between device
 syncs, nothing else in the timed region, after about 0.25 s of untimed
 steps and the W warmup steps so that the GPU clocks have settled; with --graph the step is also captured once in a HIP
 graph, checked bitwise against an eager step and replayed, and the replay
-rate is the value), the roofline of the dominant
-kernel (its mean HIP-event duration on the launch stream over K more steps,
-against the algorithmic bytes or flops per launch) and the fp64 CPU
-oracle's throughput on the host.
+rate is the value), the same step timed one call at a time after a 1 GiB
+cache flush ("flushed"), the roofline of the dominant kernel (its mean
+HIP-event duration on the launch stream over K more steps, against the
+method's algorithmic bytes and flops for the workload: q, k, v, g, beta in,
+o and the final state out, and the chunk GEMMs) as HBM and MFMA fractions of
+the published peaks and of peaks measured in the same run by a copy kernel
+and an MFMA loop, and the fp64 CPU oracle's throughput on the host.
 The line also carries "configs_report": the other parity configurations (tiny
 fp32, edge prefill, varlen forward and the backward), each timed per call
 with a cache flush between calls and set against the method's roofline
@@ -60,7 +63,7 @@ def sources_sha256() -> str:
     d = os.path.join(ROOT, "gated_deltanet_chunked_rule_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h", ".cpp")) and name != "gdr_peaks.hip":
             h.update(name.encode())
             h.update(open(os.path.join(d, name), "rb").read())
     return h.hexdigest()
@@ -142,17 +145,19 @@ def config_report(torch, gdr, gi, dev):
         nseq = len(cu) - 1 if cu is not None else w.B
         if h0 is not None:
             state_bytes += nseq * w.Hv * w.K * w.V * 4
-        state_bytes += nseq * w.Hv * w.K * w.V * 4 * (3 if backward else 1)  # final_state / dht, dh0
+        state_bytes += nseq * w.Hv * w.K * w.V * 4 * (2 if backward else 1)  # final_state / dht, dh0
         flops, nbytes = flops_tv * tv, bytes_tv * tv + state_bytes
         peak = MFMA_F32_PEAK_TFS if w.dtype == "f32" else MFMA_BF16_PEAK_TFS
         t_mfma, t_hbm = flops / (peak * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
         t_roof = max(t_mfma, t_hbm)
+        t = ms * 1e-3
         out[name] = {
             "pass": "bwd" if backward else "fwd", "tokens": tokens, "ms": round(ms, 4),
-            "tokens_per_s": round(tokens / (ms * 1e-3)),
+            "tokens_per_s": round(tokens / t),
             "roof": {"bound": "mfma" if t_mfma > t_hbm else "hbm", "t_roof_us": round(t_roof * 1e6, 2),
-                     "frac": round(t_roof / (ms * 1e-3), 4), "gflop": round(flops / 1e9, 3),
-                     "mbytes": round(nbytes / 1e6, 2)},
+                     "frac": round(t_roof / t, 4), "mfma_frac": round(t_mfma / t, 4),
+                     "hbm_frac": round(t_hbm / t, 4), "mfma_peak_tfs": peak,
+                     "gflop": round(flops / 1e9, 3), "mbytes": round(nbytes / 1e6, 2)},
             "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in kern.items()},
         }
         del d, inp
@@ -227,6 +232,49 @@ def train_step_sweep(torch, gdr, dev):
     return rows
 
 
+def measure_peaks(torch, dev):
+    """Peaks measured on this device by the probes of libgdr_peaks.so: a 1 GiB
+    device copy (2 GiB of HBM traffic per kernel) and a loop of independent
+    bf16 MFMA instructions over 2048 workgroups (8 waves per SIMD)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_deltanet_chunked_rule_amd", "libgdr_peaks.so"))
+    lib.gdr_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    lib.gdr_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, device=dev, dtype=torch.uint8).fill_(1)
+    dst = torch.empty_like(src)
+    ms = ctypes.c_float()
+    if lib.gdr_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, 10, st,
+                         ctypes.byref(ms)) != 0:
+        raise RuntimeError("copy probe failed")
+    copy_gbs = 2 * nbytes / (ms.value * 1e-3) / 1e9
+    del src, dst
+    wgs, iters = 2048, 20000
+    sink = torch.empty(wgs * 256, device=dev, dtype=torch.float32)
+    if lib.gdr_peak_mfma_bf16(ctypes.c_void_p(sink.data_ptr()), iters, wgs, 5, st, ctypes.byref(ms)) != 0:
+        raise RuntimeError("MFMA probe failed")
+    mfma_tfs = wgs * 4 * 8 * iters * 16384 / (ms.value * 1e-3) / 1e12
+    return {"hbm_copy_GBs": round(copy_gbs, 1), "mfma_bf16_TFs": round(mfma_tfs, 1),
+            "how": "1 GiB device copy, 16-byte accesses (read + write bytes); "
+                   "V_MFMA_F32_16X16X32_BF16 loop, 2048 workgroups x 4 waves x 8 independent chains"}
+
+
+def host_cpu():
+    """CPU model and core count of the host the oracle ran on."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +290,9 @@ def main():
                     help="untimed steps for this many seconds before the warmup steps (GPU clocks)")
     ap.add_argument("--graph", action="store_true",
                     help="also time a HIP-graph replay of the step and report it as the value (default: eager launches)")
+    ap.add_argument("--flushed-steps", type=int, default=50,
+                    help="steps timed one at a time after a 1 GiB cache flush")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the copy and MFMA peak probes")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -334,24 +385,65 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    # roofline of the dominant kernel
+    # the same step one call at a time, each after a 1 GiB cache flush (the
+    # inputs are then read from HBM, not from the 256 MB last-level cache)
+    flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+    flushed = []
+    for _ in range(args.flushed_steps):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        flushed.append(e0.elapsed_time(e1))
+    del flush
+    flushed_ms = sorted(flushed)[len(flushed) // 2] if flushed else None
+
+    # Roofline of the dominant kernel against the method's work for the whole
+    # workload: its essential bytes (q and k shared by the G value heads, v,
+    # g, beta in; o out; the final state) and its chunk-GEMM flops, divided by
+    # the kernel's mean duration, as fractions of the published HBM and bf16
+    # MFMA peaks (and of the peaks measured below).  The kernel's own bytes
+    # (with the A diag(beta) intermediate and the re-reads of the two-kernel
+    # split) are reported separately under "kernel_own".
     work = per_kernel_work(w, G)
     tv = w.B * w.T * w.Hv
     dom = max((n for n in kern if n in work), key=lambda n: kern[n][0])
     avg_ms = kern[dom][0] / kern[dom][1]
-    bytes_tv, flops_tv = work[dom]
-    t_hbm = bytes_tv * tv / (HBM_PEAK_GBS * 1e9)
-    t_mfma = flops_tv * tv / (MFMA_BF16_PEAK_TFS * 1e12)
+    mflops_tv, mbytes_tv = method_work(w.K, w.V, G, 2, False)
+    state_bytes = w.B * w.Hv * w.K * w.V * 4                         # final_state out
+    m_bytes, m_flops = mbytes_tv * tv + state_bytes, mflops_tv * tv
+    t_hbm = m_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = m_flops / (MFMA_BF16_PEAK_TFS * 1e12)
+    gbs, tfs = m_bytes / (avg_ms * 1e-3) / 1e9, m_flops / (avg_ms * 1e-3) / 1e12
     if t_hbm >= t_mfma:
-        roof = {"bound": "hbm", "achieved": bytes_tv * tv / (avg_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops_tv * tv / (avg_ms * 1e-3) / 1e12,
-                "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["kernel_avg_us"] = avg_ms * 1e3
+    roof["work"] = {"bytes": m_bytes, "flops": m_flops, "bytes_per_tv": mbytes_tv, "flops_per_tv": mflops_tv,
+                    "basis": "method: q, k (shared by the G value heads), v, g, beta in, o and final_state out; "
+                             "chunk GEMMs 6KV + 6CK + 4CV + C^2/3 per token x value head"}
+    roof["hbm_frac"] = gbs / HBM_PEAK_GBS
+    roof["mfma_frac"] = tfs / MFMA_BF16_PEAK_TFS
+    kb_tv, kf_tv = work[dom]
+    roof["kernel_own"] = {"bytes_per_tv": kb_tv, "flops_per_tv": kf_tv,
+                          "hbm_frac": kb_tv * tv / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "mfma_frac": kf_tv * tv / (avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS}
+    step_s = ms_per_step * 1e-3
+    roof["step"] = {"hbm_frac": m_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+                    "mfma_frac": m_flops / step_s / 1e12 / MFMA_BF16_PEAK_TFS,
+                    "flushed_hbm_frac": None if flushed_ms is None else m_bytes / (flushed_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks(torch, dev)
+        roof["measured_peaks"] = peaks
+        roof["vs_measured"] = {"hbm_frac": gbs / peaks["hbm_copy_GBs"], "mfma_frac": tfs / peaks["mfma_bf16_TFs"],
+                               "step_hbm_frac": m_bytes / step_s / 1e9 / peaks["hbm_copy_GBs"]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -366,13 +458,13 @@ def main():
         cpu = {"value": t_sample / (c1 - c0), "unit": "tokens/s", "cores": min(threads, w.Hv),
                "kind": "oracle",
                "sample": f"fp64 token recurrence over the whole workload ({t_sample} tokens x {w.Hv} "
-                         f"value heads), one thread per head"}
+                         f"value heads), one thread per head",
+               **host_cpu()}
 
-    # the method's own roofline for this workload (essential I/O, chunk-GEMM flops)
-    mf, mb = method_work(w.K, w.V, G, 2, False)
-    t_m, t_b = mf * tv / (MFMA_BF16_PEAK_TFS * 1e12), mb * tv / (HBM_PEAK_GBS * 1e9)
-    method_roof = {"bound": "mfma" if t_m > t_b else "hbm", "t_roof_us": round(max(t_m, t_b) * 1e6, 2),
-                   "frac": round(max(t_m, t_b) / (ms_per_step * 1e-3), 4)}
+    # the whole step against the method's roofline time for this workload
+    method_roof = {"bound": "mfma" if t_mfma > t_hbm else "hbm", "t_roof_us": round(max(t_mfma, t_hbm) * 1e6, 2),
+                   "frac": round(max(t_mfma, t_hbm) / (ms_per_step * 1e-3), 4),
+                   "frac_flushed": None if flushed_ms is None else round(max(t_mfma, t_hbm) / (flushed_ms * 1e-3), 4)}
 
     configs = None
     if not args.no_configs:
@@ -392,6 +484,9 @@ def main():
                    "cp_max_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"],
                    "launch": "hip_graph" if args.graph else "eager"},
         "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms, "settle_s": args.settle_s,
+        "flushed": None if flushed_ms is None else {
+            "ms_per_step": flushed_ms, "tokens_per_s": tokens / (flushed_ms * 1e-3), "steps": args.flushed_steps,
+            "how": "median of single steps, each timed with events after rewriting a 1 GiB buffer"},
         "kernels_us": {n: 1e3 * t / c for n, (t, c) in kern.items()},
         "roofline": roof,
         "method_roofline": method_roof,

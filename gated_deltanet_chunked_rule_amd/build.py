@@ -1,8 +1,11 @@
 """Builds libgdr.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
 Each source is compiled to an object in parallel, then linked into
-``gated_deltanet_chunked_rule_amd/libgdr.so``.  Packed-fp32 VALU instructions
-are disabled for the device code (``-packed-fp32-ops``).
+``gated_deltanet_chunked_rule_amd/libgdr.so``.  The peak probes
+(``include/gdr_peaks.h``: a copy kernel and an MFMA loop, used to state
+roofline fractions against measured peaks) are linked into their own
+``libgdr_peaks.so``.  Packed-fp32 VALU instructions are disabled for the device
+code (``-packed-fp32-ops``).
 """
 from __future__ import annotations
 
@@ -17,6 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdr.so")
 SOURCES = ["gdr_api.cpp", "gdr_timing.cpp", "gdr_fwd.hip", "gdr_bwd.hip", "gdr_grads.hip"]
+PEAK_SOURCES = ["gdr_peaks.hip"]
+PEAK_LIB = os.path.join(HERE, "libgdr_peaks.so")
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 
@@ -44,19 +49,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAK_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAK_LIB}")
     return LIB
 
 

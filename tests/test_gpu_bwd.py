@@ -9,7 +9,8 @@ import torch
 
 import gated_deltanet_chunked_rule_amd as gdr
 import gdr_inputs as gi
-from parity import TOL, dev, f64, gpu_bwd, gpu_fwd, head_mass_inputs, oracle_bwd, rel_err, set_chunk_gate_mass
+from parity import (TOL, dev, f64, gpu_bwd, gpu_fwd, head_mass_inputs, oracle_bwd, oracle_fwd, rel_err,
+                    set_chunk_gate_mass)
 
 pytestmark = pytest.mark.gpu
 NAMES = ["dq", "dk", "dv", "dbeta", "dg", "dh0"]
