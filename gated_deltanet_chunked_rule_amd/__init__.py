@@ -32,7 +32,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["gdr_chunk_fwd", "gdr_chunk_bwd", "gdr_chunk_fwd_plan", "fwd_workspace_bytes",
+__all__ = ["gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_chunk_bwd", "gdr_chunk_fwd_plan", "fwd_workspace_bytes",
            "bwd_workspace_bytes", "chunk_gated_delta_rule",
            "chunk_gated_delta_rule_fwd", "chunk_gated_delta_rule_bwd", "Options", "lib_path",
            "load_library", "GdrError", "timing"]
@@ -97,6 +97,9 @@ def load_library():
     lib.gdr_chunk_bwd.argtypes = [sp, op, vp, vp, vp, fp, fp, fp, vp, fp, ctypes.c_float, fp, ip, ip,
                                   vp, vp, vp, fp, fp, fp, vp, ctypes.c_size_t, vp]
     lib.gdr_chunk_bwd.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_noalloc.argtypes = [sp, op, vp, vp, vp, fp, fp, ctypes.c_float, fp, ip, ip,
+                                          vp, fp, fp, fp, vp]
+    lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdr_chunk_fwd_plan.argtypes = [sp, op, ip, ctypes.POINTER(_PlanInfo)]
     lib.gdr_chunk_fwd_plan.restype = ctypes.c_int
     lib.gdr_last_error.argtypes = []
@@ -260,6 +263,40 @@ def gdr_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=N
                              _ptr(o), _ptr(ht), _ptr(gc), _ptr(A), _ptr(workspace),
                              ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(st)))
     return o, ht, gc, A
+
+
+def gdr_chunk_fwd_noalloc(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, *,
+                          o=None, final_state=None, output_final_state=True, options=None, stream=None):
+    """gdr_chunk_fwd on the library's own device scratch (no workspace): for
+    callers that cannot allocate device memory.  Pass preallocated ``o`` (and
+    ``final_state``, and cu_seqlens as a device int32 tensor) for a call that
+    allocates nothing; missing outputs are allocated here.  Returns
+    (o, final_state)."""
+    lib = load_library()
+    cu_host = None if cu_seqlens is None else torch.as_tensor(cu_seqlens).detach().to("cpu", torch.int32)
+    _check_shapes(q, k, v, g, beta, q.shape[0] if cu_host is None else cu_host.numel() - 1,
+                  initial_state=initial_state, do=o, dht=final_state)
+    _need(q, "q"); _need(k, "k", q.dtype); _need(v, "v", q.dtype)
+    _need(g, "g", torch.float32); _need(beta, "beta", torch.float32)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32)
+    dev = q.device
+    cu_dev, cu_host = _cu_pair(cu_seqlens, dev)
+    sh, N = _shape(q, v, cu_host)
+    K = q.shape[3]
+    scale = K ** -0.5 if scale is None else float(scale)
+    o = torch.empty_like(v) if o is None else _need(o, "o", q.dtype)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, v.shape[2], K, v.shape[3]), device=dev, dtype=torch.float32)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32)
+    op = _opts(options)
+    st = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    _check(lib.gdr_chunk_fwd_noalloc(ctypes.byref(sh), None if op is None else ctypes.byref(op), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(g), _ptr(beta), ctypes.c_float(scale),
+                                     _ptr(initial_state), _ptr(cu_dev), _host_ptr(cu_host), _ptr(o),
+                                     _ptr(final_state), None, None, ctypes.c_void_p(st)))
+    return o, final_state
 
 
 def gdr_chunk_bwd(q, k, v, g, beta, A, do, dht=None, scale=None, initial_state=None,

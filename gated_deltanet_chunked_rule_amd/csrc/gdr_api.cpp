@@ -4,14 +4,22 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/gdr.h"
 #include "gdr_kernels.h"
+
+// Workspace of gdr_chunk_fwd_noalloc: device memory owned by the library, one
+// copy per device (each device that loads the library holds it until the
+// process ends).  Host code never uses this name as an address: it is a
+// host-side stand-in; the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[GDR_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -332,6 +340,32 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
   return GDR_OK;
 }
 
+// Device address of `scratch` on each device, looked up once per device (with
+// that device current) on the first gdr_chunk_fwd_noalloc call there.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+gdr_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDR_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p) return fail(GDR_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -397,6 +431,39 @@ gdr_status gdr_chunk_fwd(const gdr_shape* shape, const gdr_options* opts, const 
   return run_forward_chain(P, Lo, ws, q, k, v, g, beta, scale, initial_state, cu_seqlens, o,
                            final_state, g_cum_out, A_out, nullptr, nullptr, nullptr, P.L, false,
                            static_cast<hipStream_t>(stream));
+}
+
+gdr_status gdr_chunk_fwd_noalloc(const gdr_shape* shape, const gdr_options* opts, const void* q,
+                                 const void* k, const void* v, const float* g, const float* beta,
+                                 float scale, const float* initial_state, const int32_t* cu_seqlens,
+                                 const int32_t* cu_seqlens_host, void* o, float* final_state,
+                                 float* g_cum_out, float* A_out, void* stream) {
+  if (cu_seqlens_host && !cu_seqlens)
+    return fail(GDR_ERR_INVALID_ARG, "cu_seqlens_host given without cu_seqlens");
+  Problem P;
+  gdr_status st = analyze(shape, opts, cu_seqlens_host, cu_seqlens != nullptr, P);
+  if (st != GDR_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(GDR_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (P.Ttot > 0 && (!q || !k || !v || !g || !beta || !o))
+    return fail(GDR_ERR_INVALID_ARG, "q, k, v, g, beta and o must be non-NULL");
+  const void* ptrs[] = {q, k, v, g, beta, o, initial_state, cu_seqlens, final_state, g_cum_out, A_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(GDR_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const Layout Lo = layout(P, false);
+  if (Lo.total > (size_t)GDR_NOALLOC_SCRATCH_BYTES)
+    return fail(GDR_ERR_WORKSPACE, "problem needs " + std::to_string(Lo.total) +
+                                       " bytes of workspace, beyond the library scratch of " +
+                                       std::to_string((size_t)GDR_NOALLOC_SCRATCH_BYTES) +
+                                       " bytes: use gdr_chunk_fwd with a caller workspace");
+  // Every workspace element the forward reads is written by an earlier kernel
+  // of the same call (nothing needs clearing), so the scratch's previous
+  // contents do not matter.
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != GDR_OK) return st;
+  return run_forward_chain(P, Lo, static_cast<char*>(ws), q, k, v, g, beta, scale, initial_state,
+                           cu_seqlens, o, final_state, g_cum_out, A_out, nullptr, nullptr, nullptr, P.L,
+                           false, static_cast<hipStream_t>(stream));
 }
 
 gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const void* q,

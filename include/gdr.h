@@ -153,6 +153,32 @@ gdr_status gdr_chunk_fwd(const gdr_shape* shape, const gdr_options* opts,
                          void* o, float* final_state, float* g_cum_out, float* A_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the library-owned scratch that gdr_chunk_fwd_noalloc uses as its
+ * workspace (128 MiB, held on every device that loads the library until the
+ * process ends). */
+#define GDR_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* gdr_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is the library's own
+ * scratch on the current device, and the call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  Arguments, layouts and
+ * results are those of gdr_chunk_fwd; `stream` must belong to the current
+ * device.  Problems whose gdr_chunk_fwd_workspace_size() exceeds
+ * GDR_NOALLOC_SCRATCH_BYTES are rejected with GDR_ERR_WORKSPACE (for example
+ * the long-context shape B=1, T=65536, Hv=8, K=V=128 needs 114 MiB and fits).
+ * Every call on one device shares that device's scratch: calls that overlap
+ * in time on one device (concurrent streams or host threads) race and must
+ * be serialised by the caller; calls in stream order are safe.  The first
+ * call on a device looks up the scratch's device address there. */
+gdr_status gdr_chunk_fwd_noalloc(const gdr_shape* shape, const gdr_options* opts,
+                                 const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, float scale,
+                                 const float* initial_state,
+                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                 void* o, float* final_state, float* g_cum_out, float* A_out,
+                                 void* stream);
+
 /* Planner decision for the forward (host only, nothing is enqueued). */
 gdr_status gdr_chunk_fwd_plan(const gdr_shape* shape, const gdr_options* opts,
                               const int32_t* cu_seqlens_host, gdr_plan_info* out);

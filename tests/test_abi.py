@@ -200,3 +200,18 @@ def test_fwd_binding_rejects_mismatched_shapes():
         gdr.gdr_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"][:, :5], None, a["initial_state"])
     with pytest.raises(gdr.GdrError, match="shape mismatch: initial_state "):
         gdr.gdr_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], None, a["initial_state"][:, :2])
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch():
+    # The packed workload shape (131072 tokens, Hv = 64) needs about 1.1 GiB
+    # of workspace, beyond the no-allocation entry point's 128 MiB scratch:
+    # rejected on the host, before the scratch is looked up or anything is
+    # enqueued (fake, never dereferenced pointers).
+    lib = gdr.load_library()
+    sh = shape(B=1, T=131072, Hq=16, Hv=64, K=128, V=128, dtype=gdr.GDR_BF16)
+    p = [_fake(i) for i in range(8)]
+    rc = lib.gdr_chunk_fwd_noalloc(ctypes.byref(sh), None, p[0], p[1], p[2], p[3], p[4], ctypes.c_float(1.0),
+                                   None, None, None, p[5], None, None, None, None)
+    assert rc == -3 and "beyond the library scratch" in last_error()
+    sh = shape(B=1, T=65536, Hq=4, Hv=8, K=128, V=128, dtype=gdr.GDR_BF16)
+    assert ws_size(sh) <= (128 << 20)    # the long-context shape fits
