@@ -234,13 +234,15 @@ def train_step_sweep(torch, gdr, dev):
 
 def measure_peaks(torch, dev):
     """Peaks measured on this device by the probes of libgdr_peaks.so: a 1 GiB
-    device copy (2 GiB of HBM traffic per kernel) and a loop of independent
-    bf16 MFMA instructions over 2048 workgroups (8 waves per SIMD)."""
+    device copy (2 GiB of HBM traffic per kernel, non-temporal 16-byte
+    accesses) and loops of independent bf16 MFMA instructions over 2048
+    workgroups (8 waves per SIMD), in the 32x32x16 form (the one that reaches
+    the published rate) and the 16x16x32 form (about half of it on gfx950)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "gated_deltanet_chunked_rule_amd", "libgdr_peaks.so"))
     lib.gdr_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                   ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
-    lib.gdr_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    lib.gdr_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
     st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     nbytes = 1 << 30
@@ -254,12 +256,15 @@ def measure_peaks(torch, dev):
     del src, dst
     wgs, iters = 2048, 20000
     sink = torch.empty(wgs * 256, device=dev, dtype=torch.float32)
-    if lib.gdr_peak_mfma_bf16(ctypes.c_void_p(sink.data_ptr()), iters, wgs, 5, st, ctypes.byref(ms)) != 0:
-        raise RuntimeError("MFMA probe failed")
-    mfma_tfs = wgs * 4 * 8 * iters * 16384 / (ms.value * 1e-3) / 1e12
-    return {"hbm_copy_GBs": round(copy_gbs, 1), "mfma_bf16_TFs": round(mfma_tfs, 1),
-            "how": "1 GiB device copy, 16-byte accesses (read + write bytes); "
-                   "V_MFMA_F32_16X16X32_BF16 loop, 2048 workgroups x 4 waves x 8 independent chains"}
+    tfs = {}
+    for tile in (32, 16):
+        if lib.gdr_peak_mfma_bf16(ctypes.c_void_p(sink.data_ptr()), tile, iters, wgs, 5, st, ctypes.byref(ms)) != 0:
+            raise RuntimeError("MFMA probe failed")
+        tfs[tile] = wgs * 4 * iters * 131072 / (ms.value * 1e-3) / 1e12
+    return {"hbm_copy_GBs": round(copy_gbs, 1), "mfma_bf16_TFs": round(tfs[32], 1),
+            "mfma_bf16_16x16x32_TFs": round(tfs[16], 1),
+            "how": "1 GiB device copy, non-temporal 16-byte accesses (read + write bytes); bf16 MFMA loops, "
+                   "2048 workgroups x 4 waves, independent chains (32x32x16 and 16x16x32 forms)"}
 
 
 def host_cpu():

@@ -28,12 +28,14 @@ extern "C" {
  * written once, 16 bytes per lane access.  HBM traffic per kernel = 2 bytes. */
 int gdr_peak_copy(const void* src, void* dst, size_t bytes, int reps, void* stream, float* ms_out);
 
-/* A loop of independent V_MFMA_F32_16X16X32_BF16 instructions: `workgroups`
- * workgroups of 4 waves, each wave issuing 8 independent accumulation chains
- * for `iters` iterations (16384 flop per instruction).  sink: device buffer of
- * workgroups * 256 floats (written so the work is not optimised away).
- * Flops per kernel = workgroups * 4 * 8 * iters * 16384. */
-int gdr_peak_mfma_bf16(float* sink, int iters, int workgroups, int reps, void* stream, float* ms_out);
+/* A loop of independent bf16 MFMA instructions: `workgroups` workgroups of
+ * 4 waves, each wave issuing independent accumulation chains for `iters`
+ * iterations: tile 16 = eight chains of V_MFMA_F32_16X16X32_BF16 per
+ * iteration, tile 32 = four chains of V_MFMA_F32_32X32X16_BF16 (both 131072
+ * flop per wave and iteration).  sink: device buffer of workgroups * 256
+ * floats (written so the work is not optimised away).
+ * Flops per kernel = workgroups * 4 * iters * 131072. */
+int gdr_peak_mfma_bf16(float* sink, int tile, int iters, int workgroups, int reps, void* stream, float* ms_out);
 
 #ifdef __cplusplus
 }

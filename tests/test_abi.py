@@ -215,3 +215,23 @@ def test_noalloc_rejects_problems_beyond_the_scratch():
     assert rc == -3 and "beyond the library scratch" in last_error()
     sh = shape(B=1, T=65536, Hq=4, Hv=8, K=128, V=128, dtype=gdr.GDR_BF16)
     assert ws_size(sh) <= (128 << 20)    # the long-context shape fits
+
+
+def test_peak_probe_library_exports_its_header():
+    # the measured-peak probes (copy kernel, MFMA loops) live in their own
+    # library; every function its header declares is exported, and invalid
+    # arguments are refused on the host
+    path = os.path.join(ROOT, "gated_deltanet_chunked_rule_amd", "libgdr_peaks.so")
+    lib = ctypes.CDLL(path)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gdr_peaks.h")).read(), flags=re.S)
+    syms = sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", text)))
+    assert syms == ["gdr_peak_copy", "gdr_peak_mfma_bf16"]
+    for s in syms:
+        assert hasattr(lib, s), s
+    ms = ctypes.c_float()
+    lib.gdr_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    assert lib.gdr_peak_copy(_fake(1), _fake(2), 100, 1, None, ctypes.byref(ms)) == -1   # not a multiple of 16
+    lib.gdr_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]
+    assert lib.gdr_peak_mfma_bf16(_fake(1), 8, 10, 1, 1, None, ctypes.byref(ms)) == -1  # tile 8 does not exist
