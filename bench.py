@@ -47,12 +47,13 @@ def per_kernel_work(w, G):
     Returns {kernel: (bytes, flops)} per token*value-head."""
     K, V, C, e = w.K, w.V, 64, 2
     return {
-        # k, g, beta in; A diag(beta) rows and g_cum out; K K^T and the inverse
-        "intra_wy": (K * e / G + 8 + C * e + 4,
+        # k, g, beta in; A diag(beta) rows (compact: the 10 lower 16 x 16
+        # blocks, 80 of 128 bytes per row on average) and g_cum out; K K^T and the inverse
+        "intra_wy": (K * e / G + 8 + C * e * 5 / 8 + 4,
                      2 * C * K + C * C // 3),
-        # A diag(beta), v, k, q, g_cum in; o out (states and Vnew stay on chip);
-        # K h, A''(V - Gamma K h), K^T Vnew, Q h, Q K^T, P Vnew
-        "chunk_fused": (C * e + V * e + 2 * K * e / G + 4 + V * e,
+        # A diag(beta) (compact), v, k, q, g_cum in; o out (states and Vnew
+        # stay on chip); K h, A''(V - Gamma K h), K^T Vnew, Q h, Q K^T, P Vnew
+        "chunk_fused": (C * e * 5 / 8 + V * e + 2 * K * e / G + 4 + V * e,
                         4 * K * V + 2 * K * V + 2 * C * K + 4 * C * V),
     }
 

@@ -312,7 +312,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   {  // the 64-wide A'' tile: eight 1 KB blocks, one per wave
     const int pidx = 64 * w + l;
     const int r = pidx >> 3, c = (pidx & 7) ^ stage_swz<8>(r);
-    off_a[0] = (uint32_t)(r * CH * 2 + c * 16);
+    off_a[0] = apack_src(r, c);   // from compact rows
   }
   auto tix8 = [](int r, int c) { return (r * 8 + ((c >> 3) ^ stage_swz<8>(r))) * 8 + (c & 7); };
   auto copy_part = [&](int jc, auto bc, int piece) __attribute__((always_inline)) {
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
     const int len = min(CH, seq1 - t0);
     const long rbytes = (long)len * KD * (long)sizeof(T);
     if (piece == 0)
-      lds_copy_tile<1, 8, FNW, 8>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, (long)len * CH * 2), off_a, w);
+      lds_copy_tile<1, 8, FNW, 8>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, apack_bytes(len)), off_a, w);
     if (piece == 1)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.O, rsrc_words((const T*)p.d_o + ((long)t0 * p.Hv + h) * VD, rbytes * p.Hv), off_o, w);
     if (piece == 2)

@@ -436,6 +436,24 @@ __device__ __forceinline__ void acc_store_t(T* lds, int row0, int col0, const f3
   }
 }
 
+// A'' = A diag(beta) of a chunk (64 x 64 bf16, lower triangular in 16 x 16
+// blocks) is stored compactly: row r keeps only its first 32 (r / 16 + 1)
+// columns, the blocks on and left of the diagonal, rows one after another
+// (5 KB per chunk instead of 8; the zero blocks above the diagonal are not
+// stored).  Byte offset of the 16-byte piece pc (< 2 (r / 16 + 1)) of row r,
+// and the bytes of the first len rows.
+__device__ __forceinline__ uint32_t apack_off(int r, int pc) {
+  const int b = r >> 4;
+  return (uint32_t)(16 * (16 * b * (b + 1) + (r & 15) * 2 * (b + 1) + pc));
+}
+__device__ __forceinline__ long apack_bytes(int len) { return (long)apack_off(len, 0); }
+// Source offset for a copy of LDS piece pc of row r from the compact rows:
+// pieces above the diagonal blocks get an offset past any buffer range, so
+// the buffer load returns zeros for them.
+__device__ __forceinline__ uint32_t apack_src(int r, int pc) {
+  return pc < 2 * ((r >> 4) + 1) ? apack_off(r, pc) : 0x80000000u;
+}
+
 // Hardware workgroup id -> logical work index such that each of the 8 XCDs
 // (workgroups are dispatched round-robin over them) receives one contiguous
 // range of logical indices, run in increasing order: neighbouring work items

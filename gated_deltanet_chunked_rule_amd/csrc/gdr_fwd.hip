@@ -613,7 +613,7 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
   float su[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) su[j] = sB[16 * j + t];
-  const rsrc_t ar = make_rsrc((bf16*)p.Au + ((long)h * s.Ttot + t0) * CH, (long)len * CH * 2);
+  const rsrc_t ar = make_rsrc((bf16*)p.Au + ((long)h * s.Ttot + t0) * CH, apack_bytes(len));   // compact rows
   // A itself (XA): fp32 or bf16 head-major rows, or fp32 token-major rows
   // (a null pointer gets an empty range: its stores are dropped)
   const long hrow = ((long)h * s.Ttot + t0) * CH;
@@ -655,8 +655,10 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
       }
     }
   };
-  // 16-byte row pieces from the staging rows to memory (zero above the
-  // diagonal blocks); half < 0: all 64 A'' rows, else one half of A'' and A.
+  // 16-byte row pieces from the staging rows to memory: A'' as compact rows
+  // (the pieces above the diagonal blocks get an out-of-range offset, so
+  // their stores are dropped), A with zeros there; half < 0: all 64 A''
+  // rows, else one half of A'' and A.
   auto flush = [&](int half) __attribute__((always_inline)) {
     wave_sync();
     const int pc = l & 7;   // 16-byte piece of a row: columns 8pc .. 8pc + 7
@@ -664,18 +666,17 @@ __global__ __launch_bounds__(NTHR, 4) void k_intra_w(IntraParams p, int total_it
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int r = (l >> 3) + 8 * k;
-        uint4 v = *reinterpret_cast<const uint4*>(sa + r * SP + 8 * pc);
-        if (pc >= 2 * ((r >> 4) + 1)) v = make_uint4(0u, 0u, 0u, 0u);
-        buf_store16(ar, (uint32_t)(r * CH + 8 * pc) * 2u, v);
+        const uint4 v = *reinterpret_cast<const uint4*>(sa + r * SP + 8 * pc);
+        buf_store16(ar, apack_src(r, pc), v);
       }
     } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int rl = (l >> 3) + 8 * k, r = 32 * half + rl;
-        uint4 v = *reinterpret_cast<const uint4*>(sa + rl * SP + 8 * pc);
+        const uint4 v = *reinterpret_cast<const uint4*>(sa + rl * SP + 8 * pc);
         uint4 u = *reinterpret_cast<const uint4*>(sa + (32 + rl) * SP + 8 * pc);
-        if (pc >= 2 * ((r >> 4) + 1)) v = u = make_uint4(0u, 0u, 0u, 0u);
-        buf_store16(ar, (uint32_t)(r * CH + 8 * pc) * 2u, v);
+        if (pc >= 2 * ((r >> 4) + 1)) u = make_uint4(0u, 0u, 0u, 0u);
+        buf_store16(ar, apack_src(r, pc), v);
         buf_store16(xb, (uint32_t)(r * CH + 8 * pc) * 2u, u);
       }
       wave_sync();   // the half's rows are read before the next half is staged
@@ -1123,10 +1124,10 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     off_qk[j] = (uint32_t)(r * p.Hq * KD * (int)sizeof(T) + c * 16);
     off_v[j] = (uint32_t)(r * p.Hv * VD * (int)sizeof(T) + c * 16);
   }
-  {  // the 64-wide A'' tile: eight 1 KB blocks, one per wave
+  {  // the 64-wide A'' tile: eight 1 KB blocks, one per wave, from compact rows
     const int pidx = 64 * w + l;
     const int r = pidx >> 3, c = (pidx & 7) ^ stage_swz<8>(r);
-    off_a[0] = (uint32_t)(r * CH * 2 + c * 16);
+    off_a[0] = apack_src(r, c);
   }
   auto tix8 = [](int r, int c) { return (r * 8 + ((c >> 3) ^ stage_swz<8>(r))) * 8 + (c & 7); };
   auto copy_part = [&](int jc, auto bc, int piece) __attribute__((always_inline)) {
@@ -1136,7 +1137,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const long wbytes = (long)len * KD * (long)sizeof(T), qbytes = wbytes * p.Hq;
     if constexpr (AP) {
       if (piece == 0)
-        lds_copy_tile<1, 8, FNW, 8>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, (long)len * CH * 2), off_a, w);
+        lds_copy_tile<1, 8, FNW, 8>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, apack_bytes(len)), off_a, w);
       if (piece == 1 && !no_u)
         lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, rsrc_words((const T*)p.v + ((long)t0 * p.Hv + h) * VD, wbytes * p.Hv), off_v, w);
     } else {
