@@ -496,8 +496,12 @@ __device__ __forceinline__ i32x4v rsrc_words(const void* base, long bytes) {
   v[3] = kBufWord3;
   return v;
 }
+// LDS byte address of a pointer into LDS: the low 32 bits of its flat address
+// (the shared aperture is 4 GB aligned).  Truncating, rather than casting to
+// the LDS address space, keeps the compiler from emitting a null check and a
+// 64-bit address per copy (scalar registers it would otherwise spill).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
 }
 __device__ __forceinline__ void lds_copy16(i32x4v rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
@@ -536,6 +540,51 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Sixteen row sums at once: on exit lane t of each DPP row holds the sum over
+// the row's 16 lanes of x[t].  Four exchange steps with the partners
+// t ^ 15 (row mirror), t ^ 7 (half-row mirror), t ^ 2 and t ^ 1 (quad
+// swaps); at each step a lane keeps the half of its values whose index bit
+// (8, 4, 2, 1) equals its own lane bit and adds the partner's copy of that
+// half.  The four masks span all 16 lanes, so every sum has each lane once:
+// 45 VALU operations instead of 16 separate reductions (64 DPP adds).
+__device__ __forceinline__ float row16_sums16(const float (&x)[16]) {
+  const int t = lane_id() & 15;
+  float y[8], z[4], u[2];
+  {
+    const bool b = (t & 8) != 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = (b ? x[j + 8] : x[j]) + dpp_f<0x140>(b ? x[j] : x[j + 8]);
+  }
+  {
+    const bool b = (t & 4) != 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = (b ? y[j + 4] : y[j]) + dpp_f<0x141>(b ? y[j] : y[j + 4]);
+  }
+  {
+    const bool b = (t & 2) != 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) u[j] = (b ? z[j + 2] : z[j]) + dpp_f<0x4E>(b ? z[j] : z[j + 2]);
+  }
+  const bool b = (t & 1) != 0;
+  return (b ? u[1] : u[0]) + dpp_f<0xB1>(b ? u[0] : u[1]);
+}
+// Four row sums at once: on exit lane t holds the sum over its DPP row of
+// x[t >> 2] (the first two exchange steps of row16_sums16, then plain adds).
+__device__ __forceinline__ float row16_sums4(const float (&x)[4]) {
+  const int t = lane_id() & 15;
+  float y[2];
+  {
+    const bool b = (t & 8) != 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) y[j] = (b ? x[j + 2] : x[j]) + dpp_f<0x140>(b ? x[j] : x[j + 2]);
+  }
+  const bool b = (t & 4) != 0;
+  float v = (b ? y[1] : y[0]) + dpp_f<0x141>(b ? y[0] : y[1]);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0xB1>(v);
+  return v;
+}
+
 // 4 x 4 transpose within each quad of lanes: on entry lane 4k + i holds
 // x[e] = M[e][i]; on exit x[c] = M[i][c].  Accumulator tiles then give each
 // lane four consecutive columns of one row (8-byte bf16 stores).
@@ -555,6 +604,28 @@ __device__ __forceinline__ f32x4 quad_t(f32x4 x) {
     s1 = dpp_f<0x4E>(s1);
     if (hi) { x[0] = s0; x[1] = s1; } else { x[2] = s0; x[3] = s1; }
   }
+  return x;
+}
+// The same transpose with the exchanged values taken straight from the DPP
+// source operands (each output a select between an own value and a
+// partner's), which lets the compiler fold each DPP move into its select.
+__device__ __forceinline__ f32x4 quad_t_sel(f32x4 x) {
+  const int i = lane_id() & 3;
+  f32x4 y;
+  {
+    const bool odd = (i & 1) != 0;
+    const float p0 = dpp_f<0xB1>(x[0]), p1 = dpp_f<0xB1>(x[1]), p2 = dpp_f<0xB1>(x[2]), p3 = dpp_f<0xB1>(x[3]);
+    y[0] = odd ? p1 : x[0];
+    y[1] = odd ? x[1] : p0;
+    y[2] = odd ? p3 : x[2];
+    y[3] = odd ? x[3] : p2;
+  }
+  const bool hi = (i & 2) != 0;
+  const float p0 = dpp_f<0x4E>(y[0]), p1 = dpp_f<0x4E>(y[1]), p2 = dpp_f<0x4E>(y[2]), p3 = dpp_f<0x4E>(y[3]);
+  x[0] = hi ? p2 : y[0];
+  x[1] = hi ? p3 : y[1];
+  x[2] = hi ? y[2] : p0;
+  x[3] = hi ? y[3] : p1;
   return x;
 }
 __device__ __forceinline__ uint2 pack4_bf16(f32x4 x) {

@@ -53,8 +53,22 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     sGc[threadIdx.x >> 8][threadIdx.x & 63] = 0.f;
     sBe[threadIdx.x >> 8][threadIdx.x & 63] = 0.f;
   }
-  const SeqTables& s = p.s;
-  const int G = p.Hv / p.Hq;
+  // Pointers and tables are re-read from the kernel argument segment where
+  // they are used (scalar loads after an opaque copy of its address), so the
+  // compiler does not keep them in scalar registers across the unit loop,
+  // where it would spill them into VGPR lanes.
+  typedef const __attribute__((address_space(4))) GradParams KArgs;
+  const uint64_t kargs = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+  auto prm = [&]() __attribute__((always_inline)) -> KArgs* {
+    uint64_t a = kargs;
+    asm volatile("" : "+s"(a));
+    return (KArgs*)a;
+  };
+  const int Hq = p.Hq, Hv = p.Hv;
+  const float scale = p.scale;
+  const long Ttot = p.s.Ttot;
+  const int NTtot = p.s.NTtot;
+  const int G = Hv / Hq;
   const int i0 = (int)blockIdx.x * per_wg;
   const int i1 = min(total_items, i0 + per_wg);
   if (i0 >= i1) return;
@@ -110,19 +124,16 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   // Row sums of per-lane partials x[tt][e] (rows 16tt + 4q + e); lane t
   // receives the sum for tt = t / 4, e = t % 4, i.e. row 16(t/4) + 4q + t%4.
   auto own_rows = [&](const f32x4 (&x)[4]) __attribute__((always_inline)) {
-    float own = 0.f;
+    float v[16];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = row16_sum(x[tt][e]);
-        own = (t == 4 * tt + e) ? v : own;
-      }
-    return own;
+      for (int e = 0; e < 4; ++e) v[4 * tt + e] = x[tt][e];
+    return row16_sums16(v);
   };
   // accumulator tile (row block rb, column block cb) of a 64 x 64 LDS matrix, 8-byte writes
   auto st_tile8 = [&](T* X, int rb, int cb, f32x4 v) __attribute__((always_inline)) {
-    *reinterpret_cast<uint2*>(X + t8(16 * rb + 4 * q + (t & 3), 16 * cb + 4 * (t >> 2))) = pack4_bf16(quad_t(v));
+    *reinterpret_cast<uint2*>(X + t8(16 * rb + 4 * q + (t & 3), 16 * cb + 4 * (t >> 2))) = pack4_bf16(quad_t_sel(v));
   };
   auto mf = [](bf16x8 a, bf16x8 b, f32x4 c) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -134,8 +145,8 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   for (int j = 0; j < 2; ++j) {
     const int pidx = 64 * (w + FNW * j) + l;
     const int r = pidx >> 4, c = (pidx & 15) ^ stage_swz<16>(r);
-    off_qk[j] = (uint32_t)(r * p.Hq * KD * 2 + c * 16);
-    off_hv[j] = (uint32_t)(r * p.Hv * VD * 2 + c * 16);
+    off_qk[j] = (uint32_t)(r * Hq * KD * 2 + c * 16);
+    off_hv[j] = (uint32_t)(r * Hv * VD * 2 + c * 16);
     off_ws[j] = (uint32_t)(r * VD * 2 + c * 16);
   }
   {
@@ -143,65 +154,91 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     const int r = pidx >> 3, c = (pidx & 7) ^ stage_swz<8>(r);
     off_a[0] = (uint32_t)(r * CH * 2 + c * 16);
   }
+  // Units in order: value head gi of q/k head hk of chunk c, items
+  // (chunk, q/k head) i0 .. i1 - 1, the next unit derived from the current.
   struct Unit { int c, hk, h, gi, t0, len; };
   int cc = -1, ct0 = 0, clen = 0;   // the last chunk looked up (the chunk changes every Hq items)
-  auto unit = [&](int j, Unit& u) __attribute__((always_inline)) -> bool {
-    const int it = i0 + j / G;
-    u.gi = j % G;
-    u.c = it / p.Hq;
-    u.hk = it % p.Hq;
+  auto locate = [&](Unit& u) __attribute__((always_inline)) -> bool {
     u.h = u.hk * G + u.gi;
     if (u.c != cc) {
+      KArgs* pa = prm();
+      SeqTables st;
+      st.cu = pa->s.cu;
+      st.chunk_off = pa->s.chunk_off;
+      st.seg_off = pa->s.seg_off;
+      st.N = pa->s.N;
+      st.Ttot = pa->s.Ttot;
+      st.NTtot = pa->s.NTtot;
+      st.T_uniform = pa->s.T_uniform;
+      st.segs_uniform = pa->s.segs_uniform;
+      st.seg_order = pa->s.seg_order;
       int n;
-      if (!locate_chunk_b(s, u.c, n, ct0, clen)) return false;
+      if (!locate_chunk_b(st, u.c, n, ct0, clen)) return false;
       cc = u.c;
     }
     u.t0 = ct0;
     u.len = clen;
     return true;
   };
+  auto advance = [&](const Unit& a, Unit& u) __attribute__((always_inline)) {
+    u = a;
+    if (++u.gi == G) {
+      u.gi = 0;
+      if (++u.hk == Hq) { u.hk = 0; ++u.c; }
+    }
+  };
+  int wsc = w;   // the wave id in a scalar register, made opaque at every unit (see body)
   auto tile = [&](T* dst, const void* base, long elem0, long row_elems, int len, const uint32_t* off)
       __attribute__((always_inline)) {
-    lds_copy_tile<2, 16, FNW, 8>(dst, rsrc_words((const T*)base + elem0, (long)len * row_elems * 2), off, w);
+    lds_copy_tile<2, 16, FNW, 8>(dst, rsrc_words((const T*)base + elem0, (long)len * row_elems * 2), off, wsc);
   };
   auto copy_dO_Vn = [&](const Unit& u) __attribute__((always_inline)) {
-    tile(sdO, p.d_o, ((long)u.t0 * p.Hv + u.h) * VD, (long)p.Hv * VD, u.len, off_hv);
-    tile(sVn, p.vnew, ((long)u.h * s.Ttot + u.t0) * VD, VD, u.len, off_ws);
+    KArgs* pa = prm();
+    tile(sdO, pa->d_o, ((long)u.t0 * Hv + u.h) * VD, (long)Hv * VD, u.len, off_hv);
+    tile(sVn, pa->vnew, ((long)u.h * Ttot + u.t0) * VD, VD, u.len, off_ws);
   };
   auto copy_Q = [&](const Unit& u) __attribute__((always_inline)) {
-    tile(sQ, p.q, ((long)u.t0 * p.Hq + u.hk) * KD, (long)p.Hq * KD, u.len, off_qk);
+    tile(sQ, prm()->q, ((long)u.t0 * Hq + u.hk) * KD, (long)Hq * KD, u.len, off_qk);
   };
   auto copy_K = [&](const Unit& u) __attribute__((always_inline)) {
-    tile(sK, p.k, ((long)u.t0 * p.Hq + u.hk) * KD, (long)p.Hq * KD, u.len, off_qk);
+    tile(sK, prm()->k, ((long)u.t0 * Hq + u.hk) * KD, (long)Hq * KD, u.len, off_qk);
   };
   auto copy_dVn_V = [&](const Unit& u) __attribute__((always_inline)) {
-    tile(sdVn, p.dvn, ((long)u.h * s.Ttot + u.t0) * VD, VD, u.len, off_ws);
-    tile(sV, p.v, ((long)u.t0 * p.Hv + u.h) * VD, (long)p.Hv * VD, u.len, off_hv);
+    KArgs* pa = prm();
+    tile(sdVn, pa->dvn, ((long)u.h * Ttot + u.t0) * VD, VD, u.len, off_ws);
+    tile(sV, pa->v, ((long)u.t0 * Hv + u.h) * VD, (long)Hv * VD, u.len, off_hv);
   };
   auto copy_A_gates = [&](const Unit& u, auto abc) __attribute__((always_inline)) {   // into buffer ab
     constexpr int ab = decltype(abc)::value;
+    KArgs* pa = prm();
     lds_copy_tile<1, 8, FNW, 8>(&sA2[ab][0],
-                                rsrc_words((const T*)p.A_bf + ((long)u.h * s.Ttot + u.t0) * CH, (long)u.len * CH * 2),
-                                off_a, w);
+                                rsrc_words((const T*)pa->A_bf + ((long)u.h * Ttot + u.t0) * CH, (long)u.len * CH * 2),
+                                off_a, wsc);
     if (w == 0) {
-      const i32x4v gr = rsrc_words(p.gcum + (long)u.h * s.Ttot + u.t0, (long)u.len * 4);
+      const i32x4v gr = rsrc_words(pa->gcum + (long)u.h * Ttot + u.t0, (long)u.len * 4);
       lds_copy4(gr, (uint32_t)l * 4u, lds_addr(&sGc[ab][0]));
-      const i32x4v br = rsrc_words(p.beta + (long)u.t0 * p.Hv + u.h, ((long)(u.len - 1) * p.Hv + 1) * 4);
-      lds_copy4(br, (uint32_t)(l * p.Hv * 4), lds_addr(&sBe[ab][0]));
+      const i32x4v br = rsrc_words(pa->beta + (long)u.t0 * Hv + u.h, ((long)(u.len - 1) * Hv + 1) * 4);
+      lds_copy4(br, (uint32_t)(l * Hv * 4), lds_addr(&sBe[ab][0]));
     }
   };
   // rows 16w..16w+15 of h and dh as B fragments (contraction over V)
   auto load_hd = [&](const Unit& u, bf16x8 (&hf)[4], bf16x8 (&df)[4]) __attribute__((always_inline)) {
-    const long base = (((long)u.h * s.NTtot + u.c) * KD + dcol) * VD + 8 * q;
+    const long base = (((long)u.h * NTtot + u.c) * KD + dcol) * VD + 8 * q;
+    KArgs* pa = prm();
+    const T* hb = (const T*)pa->hbuf + base;
+    const T* db = (const T*)pa->dhbuf + base;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      hf[ks] = *reinterpret_cast<const bf16x8*>((const T*)p.hbuf + base + 32 * ks);
-      df[ks] = *reinterpret_cast<const bf16x8*>((const T*)p.dhbuf + base + 32 * ks);
+      hf[ks] = *reinterpret_cast<const bf16x8*>(hb + 32 * ks);
+      df[ks] = *reinterpret_cast<const bf16x8*>(db + 32 * ks);
     }
   };
 
   Unit cu;
-  if (!unit(0, cu)) return;
+  cu.c = i0 / Hq;
+  cu.hk = i0 - cu.c * Hq;
+  cu.gi = 0;
+  if (!locate(cu)) return;
   copy_Q(cu);
   copy_K(cu);
   copy_dO_Vn(cu);
@@ -219,8 +256,11 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   auto body = [&](auto abc, int j) __attribute__((always_inline)) -> bool {
     constexpr int ab = decltype(abc)::value;
     asm volatile("" : "+v"(q), "+v"(t), "+v"(dcol));
+    wsc = w;
+    asm volatile("" : "+s"(wsc));
     Unit nu;
-    const bool has_next = j + 1 < nunits && unit(j + 1, nu);
+    advance(cu, nu);
+    const bool has_next = j + 1 < nunits && locate(nu);
     const bool new_item = cu.gi == 0;
     const bool next_new = has_next && nu.gi == 0;
     const T* sA = &sA2[ab][0];
@@ -276,7 +316,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * ti + 4 * q + e;
-          const float v = (r >= c && r < len) ? p.scale * __expf(sGam[r] - sGam[c]) * dP[m][e] : 0.f;
+          const float v = (r >= c && r < len) ? scale * __expf(sGam[r] - sGam[c]) * dP[m][e] : 0.f;
           const float x = v * Sqk[m][e];
           rx[e] += x;
           cx += x;
@@ -286,13 +326,8 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
         cx = col_group_sum(cx);
         if (q == 0) sColP[w][c] -= cx;
       }
-      float own = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = row16_sum(rx[e]);
-        own = (t == e) ? v : own;
-      }
-      if (t < 4) sRowP[w][16 * ti + 4 * q + t] += own;
+      const float own = row16_sums4(rx);   // the sum for row 16 ti + 4q + t/4
+      if ((t & 3) == 0) sRowP[w][16 * ti + 4 * q + (t >> 2)] += own;
     }
     // Three passes over h and dh (rows 16w..16w+15 as B fragments), each
     // folded right away: s Gamma_t dO h^T into dq, -dVnew h^T (dW) into LDS
@@ -308,6 +343,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
         for (int st = 0; st < 4; ++st) vb[st] = mf(rb8(sA, ks, 16 * st), bd, vb[st]);
       }
       f32x4 dbL[4];
+      void* dvp = prm()->dv;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const f32x4 bt = fac4(sBt, st), ve = rows4(sV, st);
@@ -318,8 +354,8 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
           o[e] = bt[e] * vb[st][e];
         }
         const int r = 16 * st + 4 * q + (t & 3);   // after the transpose: row r, columns 16w + 4(t/4) ..
-        const uint2 u = pack4_bf16(quad_t(o));
-        if (r < len) *reinterpret_cast<uint2*>((T*)p.dv + ((long)(t0 + r) * p.Hv + h) * VD + 16 * w + 4 * (t >> 2)) = u;
+        const uint2 u = pack4_bf16(quad_t_sel(o));
+        if (r < len) *reinterpret_cast<uint2*>((T*)dvp + ((long)(t0 + r) * Hv + h) * VD + 16 * w + 4 * (t >> 2)) = u;
       }
       sDbP[w][16 * (t >> 2) + 4 * q + (t & 3)] += own_rows(dbL);
     }
@@ -339,11 +375,11 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) acc[tt] = mf(ra16(X, 16 * tt + t, ks), b, acc[tt]);
         if (pass == 2) {
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          struct Pairs { bf16x2 v[4]; };
+          const Pairs hp = __builtin_bit_cast(Pairs, Hf[ks]), dp = __builtin_bit_cast(Pairs, Df[ks]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const bf16 hv = Hf[ks][i], dv = Df[ks][i];
-            hdp += to_f(hv) * to_f(dv);
-          }
+          for (int i = 0; i < 4; ++i) hdp = __builtin_amdgcn_fdot2_f32_bf16(hp.v[i], dp.v[i], hdp, false);
         }
       }
 #pragma unroll
@@ -352,12 +388,12 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
           const f32x4 gm = fac4(sGm, tt), qe = rows4(sQ, tt);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float vq = p.scale * gm[e] * acc[tt][e];   // s Gamma_t (dO h^T)
+            const float vq = scale * gm[e] * acc[tt][e];   // s Gamma_t (dO h^T)
             dq[tt][e] += vq;
             rowL[tt][e] += vq * qe[e];
           }
         } else if (pass == 1) {   // dW rows
-          const uint2 u = pack4_bf16(quad_t(-acc[tt]));
+          const uint2 u = pack4_bf16(quad_t_sel(-acc[tt]));
           *reinterpret_cast<uint2*>(sW + t16(16 * tt + 4 * q + (t & 3), 16 * w + 4 * (t >> 2))) = u;
         } else {
           const f32x4 dc = fac4(sDec, tt), ke = rows4(sK, tt);
@@ -506,16 +542,10 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
         cx = col_group_sum(cx);
         if (q == 0) sColP[w][c] -= cx;
       }
-      float orow = 0.f, odb = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float vr = row16_sum(rx[e]), vb = row16_sum(bs[e]);
-        orow = (t == e) ? vr : orow;
-        odb = (t == e) ? vb : odb;
-      }
-      if (t < 4) {
-        sRowP[w][16 * ti + 4 * q + t] += orow;
-        sDbP[w][16 * ti + 4 * q + t] += odb;
+      const float orow = row16_sums4(rx), odb = row16_sums4(bs);   // row 16 ti + 4q + t/4
+      if ((t & 3) == 0) {
+        sRowP[w][16 * ti + 4 * q + (t >> 2)] += orow;
+        sDbP[w][16 * ti + 4 * q + (t >> 2)] += odb;
       }
     }
     lds_barrier();   // E complete; every partial sum is in
@@ -544,19 +574,22 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       const float sc = wave_inclusive_scan(rev);
       const float dgv = __shfl(sc, 63 - l, 64);
       if (l < len) {
-        p.dg[(long)(t0 + l) * p.Hv + h] = dgv;
-        p.dbeta[(long)(t0 + l) * p.Hv + h] = db;
+        KArgs* pa = prm();
+        pa->dg[(long)(t0 + l) * Hv + h] = dgv;
+        pa->dbeta[(long)(t0 + l) * Hv + h] = db;
       }
     }
     if (cu.gi == G - 1) {   // the group's dq and dk rows
+      KArgs* pa = prm();
+      void *dqp = pa->dq, *dkp = pa->dk;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int r = 16 * tt + 4 * q + (t & 3);
-        const uint2 uq = pack4_bf16(quad_t(dq[tt])), uk = pack4_bf16(quad_t(dk[tt]));
+        const uint2 uq = pack4_bf16(quad_t_sel(dq[tt])), uk = pack4_bf16(quad_t_sel(dk[tt]));
         if (r < len) {
-          const long o = ((long)(t0 + r) * p.Hq + cu.hk) * KD + 16 * w + 4 * (t >> 2);
-          *reinterpret_cast<uint2*>((T*)p.dq + o) = uq;
-          *reinterpret_cast<uint2*>((T*)p.dk + o) = uk;
+          const long o = ((long)(t0 + r) * Hq + cu.hk) * KD + 16 * w + 4 * (t >> 2);
+          *reinterpret_cast<uint2*>((T*)dqp + o) = uq;
+          *reinterpret_cast<uint2*>((T*)dkp + o) = uk;
         }
       }
     }
