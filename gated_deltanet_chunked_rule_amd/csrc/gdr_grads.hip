@@ -272,8 +272,11 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     load_hd(cu, Hf, Df);
 
     // ---- unit start: this unit's copies have landed (waited at the end of
-    // the previous unit); gate factors and zeroed per-wave partial sums
-    if (w == 0) {
+    // the previous unit); gate factors and zeroed per-wave partial sums.
+    // Every wave writes the same factor values, so each wave reads what it
+    // wrote itself and no barrier is needed here: the previous unit's final
+    // barrier already keeps these writes after every read of the old values.
+    {
       const float gl = gcb[len - 1], gv = gcb[l];
       const float gam = l < len ? gv : gl;
       sGam[l] = gam;
@@ -284,7 +287,6 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     sRowP[w][l] = 0.f;
     sColP[w][l] = 0.f;
     sDbP[w][l] = 0.f;
-    lds_barrier();
     if (new_item) {   // cached K fragments, zero dq and dk
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
