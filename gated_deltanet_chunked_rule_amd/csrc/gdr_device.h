@@ -587,29 +587,10 @@ __device__ __forceinline__ float row16_sums4(const float (&x)[4]) {
 
 // 4 x 4 transpose within each quad of lanes: on entry lane 4k + i holds
 // x[e] = M[e][i]; on exit x[c] = M[i][c].  Accumulator tiles then give each
-// lane four consecutive columns of one row (8-byte bf16 stores).
+// lane four consecutive columns of one row (8-byte bf16 stores).  Two
+// exchange steps (partners i ^ 1, then i ^ 2); each output is a select
+// between an own value and a partner's, read with a DPP quad permute.
 __device__ __forceinline__ f32x4 quad_t(f32x4 x) {
-  const int i = lane_id() & 3;
-  {
-    const bool odd = (i & 1) != 0;
-    float s0 = odd ? x[0] : x[1], s1 = odd ? x[2] : x[3];
-    s0 = dpp_f<0xB1>(s0);
-    s1 = dpp_f<0xB1>(s1);
-    if (odd) { x[0] = s0; x[2] = s1; } else { x[1] = s0; x[3] = s1; }
-  }
-  {
-    const bool hi = (i & 2) != 0;
-    float s0 = hi ? x[0] : x[2], s1 = hi ? x[1] : x[3];
-    s0 = dpp_f<0x4E>(s0);
-    s1 = dpp_f<0x4E>(s1);
-    if (hi) { x[0] = s0; x[1] = s1; } else { x[2] = s0; x[3] = s1; }
-  }
-  return x;
-}
-// The same transpose with the exchanged values taken straight from the DPP
-// source operands (each output a select between an own value and a
-// partner's), which lets the compiler fold each DPP move into its select.
-__device__ __forceinline__ f32x4 quad_t_sel(f32x4 x) {
   const int i = lane_id() & 3;
   f32x4 y;
   {

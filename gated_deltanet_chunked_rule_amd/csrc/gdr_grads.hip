@@ -133,7 +133,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   };
   // accumulator tile (row block rb, column block cb) of a 64 x 64 LDS matrix, 8-byte writes
   auto st_tile8 = [&](T* X, int rb, int cb, f32x4 v) __attribute__((always_inline)) {
-    *reinterpret_cast<uint2*>(X + t8(16 * rb + 4 * q + (t & 3), 16 * cb + 4 * (t >> 2))) = pack4_bf16(quad_t_sel(v));
+    *reinterpret_cast<uint2*>(X + t8(16 * rb + 4 * q + (t & 3), 16 * cb + 4 * (t >> 2))) = pack4_bf16(quad_t(v));
   };
   auto mf = [](bf16x8 a, bf16x8 b, f32x4 c) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
           o[e] = bt[e] * vb[st][e];
         }
         const int r = 16 * st + 4 * q + (t & 3);   // after the transpose: row r, columns 16w + 4(t/4) ..
-        const uint2 u = pack4_bf16(quad_t_sel(o));
+        const uint2 u = pack4_bf16(quad_t(o));
         if (r < len) *reinterpret_cast<uint2*>((T*)dvp + ((long)(t0 + r) * Hv + h) * VD + 16 * w + 4 * (t >> 2)) = u;
       }
       sDbP[w][16 * (t >> 2) + 4 * q + (t & 3)] += own_rows(dbL);
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
             rowL[tt][e] += vq * qe[e];
           }
         } else if (pass == 1) {   // dW rows
-          const uint2 u = pack4_bf16(quad_t_sel(-acc[tt]));
+          const uint2 u = pack4_bf16(quad_t(-acc[tt]));
           *reinterpret_cast<uint2*>(sW + t16(16 * tt + 4 * q + (t & 3), 16 * w + 4 * (t >> 2))) = u;
         } else {
           const f32x4 dc = fac4(sDec, tt), ke = rows4(sK, tt);
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int r = 16 * tt + 4 * q + (t & 3);
-        const uint2 uq = pack4_bf16(quad_t_sel(dq[tt])), uk = pack4_bf16(quad_t_sel(dk[tt]));
+        const uint2 uq = pack4_bf16(quad_t(dq[tt])), uk = pack4_bf16(quad_t(dk[tt]));
         if (r < len) {
           const long o = ((long)(t0 + r) * Hq + cu.hk) * KD + 16 * w + 4 * (t >> 2);
           *reinterpret_cast<uint2*>((T*)dqp + o) = uq;
