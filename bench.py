@@ -105,8 +105,8 @@ def config_report(torch, gdr, gi, dev):
     served from the last-level cache."""
     flush = torch.empty(1 << 28, device=dev, dtype=torch.float32)
     out = {}
-    for name, backward, iters in (("tiny_fp32", False, 20), ("edge_prefill", False, 10),
-                                  ("varlen", False, 5), ("backward", True, 5)):
+    for name, backward, iters in (("tiny_fp32", False, 50), ("edge_prefill", False, 50),
+                                  ("varlen", False, 50), ("backward", True, 50)):
         w = gi.WORKLOADS[name]
         inp = gi.make_inputs(w)
         d = {n: (x.to(dev) if hasattr(x, "to") and n != "cu_seqlens" else x) for n, x in inp.items()}
@@ -117,7 +117,7 @@ def config_report(torch, gdr, gi, dev):
             call = lambda: gdr.gdr_chunk_bwd(*args)
         else:
             call = lambda: gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], h0, cu)
-        for _ in range(3):
+        for _ in range(10):
             call()
         torch.cuda.synchronize()
         times = []
