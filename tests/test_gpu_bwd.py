@@ -48,6 +48,15 @@ def test_ragged_bf16(K):
     check_bwd(gi.make_inputs(w))
 
 
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("bf16", 64), ("f32", 32)])
+def test_strong_decay_gates_backward(dtype, K):
+    # gates alpha = e^g in (1e-6, 1e-2): e^gamma underflows fp32 within a
+    # chunk; the gradients' decay factors must come from differences of gamma
+    w = gi.custom(B=1, T=64 * 4 + 21, Hq=2, Hv=4, K=K, V=K, dtype=dtype, seed=48, initial_state=True,
+                  gate=(1e-6, 1e-2), backward=True)
+    check_bwd(gi.make_inputs(w), label=f"strong decay {dtype} K={K}")
+
+
 def test_fp32_k32():
     w = gi.custom(B=1, T=64 * 4 + 7, Hq=2, Hv=2, K=32, V=32, dtype="f32", seed=71, initial_state=True,
                   backward=True)

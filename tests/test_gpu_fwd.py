@@ -93,6 +93,18 @@ def test_context_parallel_split_matches_oracle(seg, warm):
     assert rel_err(ocp, f64(ooff)) <= TOL["bf16"]["o"]
 
 
+@pytest.mark.parametrize("dtype,K,cp", [("bf16", 128, False), ("bf16", 128, True), ("f32", 32, False)])
+def test_strong_decay_gates(dtype, K, cp):
+    # gates alpha = e^g in (1e-6, 1e-2): the in-chunk decay e^gamma underflows
+    # fp32 within a chunk (gamma reaches several hundred below zero), so every
+    # factor of the chunk form must come from differences of gamma; the state
+    # forgets within a few tokens and o is dominated by the intra-chunk terms
+    w = gi.custom(B=2, T=64 * 5 + 13, Hq=2, Hv=4, K=K, V=K, dtype=dtype, seed=46, initial_state=True,
+                  gate=(1e-6, 1e-2))
+    inp = gi.make_inputs(w)
+    check_fwd(inp, gdr.Options(gdr.CP_FORCE, 2, 1) if cp else None, label=f"strong decay cp={cp}")
+
+
 def test_context_parallel_uncertified_heads_fall_back():
     # g == 0 on some heads: warmup from zero is not accurate there, so those
     # heads must be computed serially and still match the oracle.
