@@ -54,9 +54,10 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     sBe[threadIdx.x >> 8][threadIdx.x & 63] = 0.f;
   }
   // Pointers and tables are re-read from the kernel argument segment where
-  // they are used (scalar loads after an opaque copy of its address), so the
-  // compiler does not keep them in scalar registers across the unit loop,
-  // where it would spill them into VGPR lanes.
+  // they are used (scalar loads after an opaque copy of its address; p is
+  // the first argument, so it starts the segment), so the compiler does not
+  // keep them in scalar registers across the unit loop, where it would
+  // spill them into VGPR lanes.
   typedef const __attribute__((address_space(4))) GradParams KArgs;
   const uint64_t kargs = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
   auto prm = [&]() __attribute__((always_inline)) -> KArgs* {
