@@ -57,6 +57,13 @@ def test_strong_decay_gates_backward(dtype, K):
     check_bwd(gi.make_inputs(w), label=f"strong decay {dtype} K={K}")
 
 
+def test_odd_head_counts_and_many_short_rows_backward():
+    # three q/k heads (six value heads) and 24 rows of 70 tokens
+    w = gi.custom(B=24, T=70, Hq=3, Hv=6, K=128, V=128, dtype="bf16", seed=50, initial_state=True,
+                  backward=True)
+    check_bwd(gi.make_inputs(w), label="Hq=3 Hv=6 B=24")
+
+
 def test_fp32_k32():
     w = gi.custom(B=1, T=64 * 4 + 7, Hq=2, Hv=2, K=32, V=32, dtype="f32", seed=71, initial_state=True,
                   backward=True)

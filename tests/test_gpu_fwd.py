@@ -150,6 +150,25 @@ def test_long_context_workload_full_size():
     check_fwd(inp)
 
 
+def test_one_head_quarter_million_tokens():
+    # one value head over 262144 tokens (4096 chunks): the automatic split
+    # gives the single head 256 segments, each with its own warmup window
+    w = gi.custom(B=1, T=262144, Hq=1, Hv=1, K=128, V=128, dtype="bf16", seed=47, initial_state=True)
+    inp = gi.make_inputs(w)
+    info = gdr.gdr_chunk_fwd_plan(inp["q"], inp["v"])
+    print(f"      plan: {info}", flush=True)
+    assert info["total_segments"] >= 128 and info["warmup_chunks"] > 0
+    check_fwd(inp, label="one head, 262144 tokens")
+
+
+@pytest.mark.parametrize("dtype,K", [("bf16", 128), ("f32", 64)])
+def test_odd_head_counts_and_many_short_rows(dtype, K):
+    # three q/k heads (six value heads) and 48 rows of 70 tokens: head and row
+    # counts that are not multiples of the XCD count or of two
+    w = gi.custom(B=48, T=70, Hq=3, Hv=6, K=K, V=K, dtype=dtype, seed=49, initial_state=True)
+    check_fwd(gi.make_inputs(w), label="Hq=3 Hv=6 B=48")
+
+
 def test_varlen_workload_full_size_all_heads():
     # Every value head of the packed workload (16 sequences, 131072 tokens,
     # Hv = 64) against the oracle, o and final_state element by element.  The
