@@ -57,6 +57,19 @@ def test_strong_decay_gates_backward(dtype, K):
     check_bwd(gi.make_inputs(w), label=f"strong decay {dtype} K={K}")
 
 
+def test_backward_one_head_131072_tokens():
+    # one value head over 2048 chunks: the states and reverse passes split
+    # it into many CP segments, each warming up before its start (states)
+    # and after its end (reverse pass)
+    w = gi.custom(B=1, T=131072, Hq=1, Hv=1, K=128, V=128, dtype="bf16", seed=51, initial_state=True,
+                  backward=True)
+    inp = gi.make_inputs(w)
+    info = gdr.gdr_chunk_fwd_plan(dev(inp["q"]), dev(inp["v"]))
+    print(f"      plan: {info}", flush=True)
+    assert info["total_segments"] >= 64
+    check_bwd(inp, label="one head, 131072 tokens")
+
+
 def test_odd_head_counts_and_many_short_rows_backward():
     # three q/k heads (six value heads) and 24 rows of 70 tokens
     w = gi.custom(B=24, T=70, Hq=3, Hv=6, K=128, V=128, dtype="bf16", seed=50, initial_state=True,
