@@ -89,7 +89,7 @@ def test_fp32_tiny_workload_backward():
     check_bwd(inp)
 
 
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 8])
 def test_grouped_heads(G):
     w = gi.custom(B=1, T=200, Hq=2, Hv=2 * G, K=128, V=128, dtype="bf16", seed=72 + G, backward=True)
     check_bwd(gi.make_inputs(w))

@@ -39,9 +39,9 @@ def test_ragged_tail_with_initial_state(dtype, K):
     check_fwd(gi.make_inputs(w))
 
 
-@pytest.mark.parametrize("G", [1, 2, 4])
-def test_grouped_heads(G):
-    w = gi.custom(B=1, T=300, Hq=2, Hv=2 * G, K=64, V=64, dtype="bf16", seed=22 + G)
+@pytest.mark.parametrize("G,K", [(1, 64), (2, 64), (4, 64), (8, 64), (8, 128)])
+def test_grouped_heads(G, K):
+    w = gi.custom(B=1, T=300, Hq=2, Hv=2 * G, K=K, V=K, dtype="bf16", seed=22 + G + K)
     check_fwd(gi.make_inputs(w))
 
 
