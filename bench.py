@@ -294,6 +294,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the training-step sweep")
     ap.add_argument("--settle-s", type=float, default=0.25,
                     help="untimed steps for this many seconds before the warmup steps (GPU clocks)")
+    ap.add_argument("--precise-vnew", action="store_true",
+                    help="time the forward with the precise_vnew option (Vnew as two bf16 terms; the default "
+                         "value is measured without it)")
     ap.add_argument("--graph", action="store_true",
                     help="also time a HIP-graph replay of the step and report it as the value (default: eager launches)")
     ap.add_argument("--flushed-steps", type=int, default=50,
@@ -322,8 +325,10 @@ def main():
     # workspace allocated once, outside the timed region
     ws = torch.empty(gdr.fwd_workspace_bytes(q, v), device=dev, dtype=torch.uint8)
 
+    opts = gdr.Options(precise_vnew=1) if args.precise_vnew else None
+
     def step():
-        return gdr.gdr_chunk_fwd(q, k, v, g, beta, scale, workspace=ws)
+        return gdr.gdr_chunk_fwd(q, k, v, g, beta, scale, workspace=ws, options=opts)
 
     # untimed clock settle (about 0.25 s of steps) before the W warmup steps:
     # right after a cold start every kernel runs ~20 % slow until the GPU
@@ -488,7 +493,7 @@ def main():
         "config": {"workload": "long_context", "B": w.B, "T": w.T, "Hq": w.Hq, "Hv": w.Hv, "K": w.K,
                    "V": w.V, "chunk": 64, "cp_segment_chunks": plan["segment_chunks"],
                    "cp_max_warmup_chunks": plan["warmup_chunks"], "state_workgroups": plan["state_workgroups"],
-                   "launch": "hip_graph" if args.graph else "eager"},
+                   "launch": "hip_graph" if args.graph else "eager", "precise_vnew": bool(args.precise_vnew)},
         "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms, "settle_s": args.settle_s,
         "flushed": None if flushed_ms is None else {
             "ms_per_step": flushed_ms, "tokens_per_s": tokens / (flushed_ms * 1e-3), "steps": args.flushed_steps,

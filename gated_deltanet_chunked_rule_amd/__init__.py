@@ -58,7 +58,7 @@ class _Shape(ctypes.Structure):
 class _Options(ctypes.Structure):
     _fields_ = [("cp_mode", ctypes.c_int), ("cp_segment_chunks", ctypes.c_int32),
                 ("cp_warmup_chunks", ctypes.c_int32), ("cp_log_eps", ctypes.c_float),
-                ("cp_serial_fallback", ctypes.c_int32)]
+                ("cp_serial_fallback", ctypes.c_int32), ("precise_vnew", ctypes.c_int32)]
 
 
 class _PlanInfo(ctypes.Structure):
@@ -68,8 +68,8 @@ class _PlanInfo(ctypes.Structure):
 
 
 Options = namedtuple("Options", ["cp_mode", "cp_segment_chunks", "cp_warmup_chunks", "cp_log_eps",
-                                 "cp_serial_fallback"],
-                     defaults=[CP_AUTO, 0, 0, 0.0, 0])
+                                 "cp_serial_fallback", "precise_vnew"],
+                     defaults=[CP_AUTO, 0, 0, 0.0, 0, 0])
 
 
 def lib_path() -> str:
@@ -139,7 +139,7 @@ def _opts(options) -> Optional[_Options]:
         return None
     o = Options(*options) if not isinstance(options, Options) else options
     return _Options(int(o.cp_mode), int(o.cp_segment_chunks), int(o.cp_warmup_chunks),
-                    float(o.cp_log_eps), int(o.cp_serial_fallback))
+                    float(o.cp_log_eps), int(o.cp_serial_fallback), int(o.precise_vnew))
 
 
 def _need(t: torch.Tensor, name: str, dtype=None):

@@ -48,6 +48,7 @@ struct Problem {
   int BV = 0, nvb = 0, L = 1, W = 0, total_segs = 0;
   float log_eps = 0.f;
   bool serial_fallback = false;   // uncertified heads run serially instead of exact segments
+  bool precise_vnew = false;      // bf16 output pass with Vnew as two bf16 terms
 };
 
 struct Layout {
@@ -160,6 +161,8 @@ gdr_status analyze(const gdr_shape* sh, const gdr_options* op, const int32_t* cu
     if (op->cp_serial_fallback != 0 && op->cp_serial_fallback != 1)
       return fail(GDR_ERR_INVALID_ARG, "cp_serial_fallback must be 0 or 1");
     P.serial_fallback = op->cp_serial_fallback == 1;
+    if (op->precise_vnew != 0 && op->precise_vnew != 1) return fail(GDR_ERR_INVALID_ARG, "precise_vnew must be 0 or 1");
+    P.precise_vnew = op->precise_vnew == 1;
   }
   P.BV = (P.K == 128) ? 64 : 32;
   P.nvb = P.V / P.BV;
@@ -309,6 +312,7 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     fp.log_eps = P.log_eps; fp.scale = scale;
     fp.trans = 0; fp.segtr = nullptr; fp.hstart = nullptr;
     fp.rev_cert = bwd ? 1 : 0;
+    fp.split_vnew = (!bwd && P.precise_vnew) ? 1 : 0;
     fp.hbuf = bwd ? ws + Lo.hbuf : nullptr;
     fp.vnew = bwd ? ws + Lo.vnew : nullptr;
     if (exact_cp(P, L)) {

@@ -368,6 +368,16 @@ __device__ __forceinline__ bf16x8 pack_b(const f32x4& x, const f32x4& y) {
   }
   return f;
 }
+// The second bf16 term of pack_b: the rounding remainders x - hi, y - hi.
+__device__ __forceinline__ bf16x8 pack_b_lo(const f32x4& x, const f32x4& y, const bf16x8& hi) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = static_cast<bf16>(x[e] - static_cast<float>(hi[e]));
+    f[4 + e] = static_cast<bf16>(y[e] - static_cast<float>(hi[4 + e]));
+  }
+  return f;
+}
 
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, uint2 u) {
   decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)) v;

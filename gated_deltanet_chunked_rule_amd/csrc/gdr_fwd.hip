@@ -982,11 +982,17 @@ struct FusedBufs {   // one buffer of staged chunk inputs
 };
 
 // MODE: 0 the output pass, 1 the backward's states pass, 2 the forward's
-// segment transitions, 3 the backward's (separate instantiations, so each
+// segment transitions, 3 the backward's, 4 the output pass with Vnew split
+// into two bf16 terms in its products (separate instantiations, so each
 // keeps only its own paths).
 template <typename T, int KD, int MODE>
 __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
-  constexpr bool TRANS = MODE >= 2;
+  constexpr bool TRANS = MODE == 2 || MODE == 3;
+  // Vnew as hi + lo, two bf16 terms (hi = bf16(x), lo = bf16(x - hi)), in
+  // both products that take it as an MFMA operand (P Vnew and the state
+  // update): an error of about 2^-16 of |Vnew| instead of the 2^-9 of one
+  // bf16 rounding, for strongly coupled keys (two MFMAs per product).
+  constexpr bool SPLITV = MODE == 4;
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int VD = KD;
   constexpr int VEC = 16 / (int)sizeof(T);
@@ -1197,7 +1203,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   // The upper tiles (0,1) and (2,3) that the 32-token contraction steps of
   // P Vnew read are always zero: written once here (published by the
   // barrier below), never recomputed.
-  if constexpr (MODE == 0) {
+  if constexpr (MODE == 0 || MODE == 4) {
     for (int i = threadIdx.x; i < CH * PP; i += FNT) sP[i] = from_f<T>(0.f);
   }
   wait_copies(cstart, ic<0>());
@@ -1487,6 +1493,14 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           for (int rb = 0; rb < NKB; ++rb)
 #pragma unroll
             for (int cb = 0; cb < CBW; ++cb) hs[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[rb], vb[cb], hs[rb][cb], 0, 0, 0);
+          if constexpr (SPLITV) {
+#pragma unroll
+            for (int cb = 0; cb < CBW; ++cb) {
+              const bf16x8 vl = pack_b_lo(vd[2 * ks][cb], vd[2 * ks + 1][cb], vb[cb]);
+#pragma unroll
+              for (int rb = 0; rb < NKB; ++rb) hs[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[rb], vl, hs[rb][cb], 0, 0, 0);
+            }
+          }
         }
       }
     }
@@ -1548,6 +1562,14 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
           for (int tt = 2 * ks; tt < 4; ++tt)
 #pragma unroll
             for (int cb = 0; cb < CBW; ++cb) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[ks][tt], vb[cb], oa[tt][cb], 0, 0, 0);
+          if constexpr (SPLITV) {
+#pragma unroll
+            for (int cb = 0; cb < CBW; ++cb) {
+              const bf16x8 vl = pack_b_lo(vn[2 * ks][cb], vn[2 * ks + 1][cb], vb[cb]);
+#pragma unroll
+              for (int tt = 2 * ks; tt < 4; ++tt) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[ks][tt], vl, oa[tt][cb], 0, 0, 0);
+            }
+          }
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
@@ -1749,7 +1771,12 @@ static hipError_t fused_impl(const FusedParams& p, int total_segs, hipStream_t s
   if (p.trans && apath) hipLaunchKernelGGL((k_fused<T, KD, 2>), dim3(grid), dim3(FNT), 0, st, p, total);
   else if (p.trans) hipLaunchKernelGGL((k_fused<T, KD, 3>), dim3(grid), dim3(FNT), 0, st, p, total);
   else if (states) hipLaunchKernelGGL((k_fused<T, KD, 1>), dim3(grid), dim3(FNT), 0, st, p, total);
-  else hipLaunchKernelGGL((k_fused<T, KD, 0>), dim3(grid), dim3(FNT), 0, st, p, total);
+  else if constexpr (!F32) {
+    if (p.split_vnew) hipLaunchKernelGGL((k_fused<T, KD, 4>), dim3(grid), dim3(FNT), 0, st, p, total);
+    else hipLaunchKernelGGL((k_fused<T, KD, 0>), dim3(grid), dim3(FNT), 0, st, p, total);
+  } else {
+    hipLaunchKernelGGL((k_fused<T, KD, 0>), dim3(grid), dim3(FNT), 0, st, p, total);
+  }
   hipError_t err = hipGetLastError();
   timing_after(st);
   return err;

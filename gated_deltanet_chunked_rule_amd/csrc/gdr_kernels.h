@@ -111,6 +111,7 @@ struct FusedParams {         // forward state recurrence fused with the output
   float* segtr;              // transition pass: [Hv][total_segs][2][K][V] {M, b}
   const float* hstart;       // nullable: exact segment start states [Hv][total_segs][K][V]
   int rev_cert;              // 1 (backward): a head certifies only if its reverse windows do too
+  int split_vnew;            // 1: bf16 output pass with Vnew as two bf16 terms (MODE 4)
   void* hbuf;                // non-null (backward recompute): store each chunk's entry state
   void* vnew;                //   and Vnew instead of the output
 };

@@ -112,6 +112,13 @@ typedef struct {
   int32_t cp_warmup_chunks;  /* most warmup chunks before each segment; default 8 */
   float cp_log_eps;          /* certificate threshold on sum(g); default ln(1e-6) */
   int32_t cp_serial_fallback;/* 1: uncertified heads run serially; 0 (default): exact segment states */
+  int32_t precise_vnew;      /* 1: the bf16 forward's output pass takes Vnew = A''(V - Gamma K h) as two
+                              * bf16 terms (hi + lo) in its two products, P Vnew and the state update
+                              * K^T (d * Vnew), instead of one bf16 rounding: for strongly coupled keys
+                              * (nearly parallel keys without decay, where the chunk system I + L is
+                              * badly conditioned), at the cost of one more MFMA per product; see the
+                              * notes on precision.  0 (default): one bf16 operand.  Ignored in fp32
+                              * and by the backward's recomputation. */
 } gdr_options;
 
 /* What the planner chose for a forward call (for tests and reporting). */

@@ -273,6 +273,28 @@ def test_nearly_parallel_keys_without_decay(dtype, K, spread):
     check_fwd(inp, label=f"nearly parallel keys {dtype}")
 
 
+def test_nearly_parallel_keys_precise_vnew():
+    # The same coupled system at spread 0.1, where the single bf16 roundings
+    # of the chunk products' operands reach err(o) of about 0.021: with
+    # precise_vnew the output pass takes Vnew as two bf16 terms in P Vnew and
+    # in the state update (an fp64 emulation of the rounded chunk path puts
+    # err(o) at 0.0167 with Vnew exact and everything else rounded).
+    K, spread = 128, 0.1
+    w = gi.custom(B=1, T=64 * 5 + 9, Hq=2, Hv=4, K=K, V=K, dtype="bf16", seed=70)
+    inp = gi.make_inputs(w)
+    gen = torch.Generator().manual_seed(70)
+    T = inp["k"].shape[1]
+    k = torch.randn(1, 1, 2, K, generator=gen) + spread * torch.randn(1, T, 2, K, generator=gen)
+    inp["k"] = (k / k.norm(dim=-1, keepdim=True)).to(inp["k"].dtype)
+    inp["beta"] = torch.ones_like(inp["beta"])
+    inp["g"] = torch.zeros_like(inp["g"])
+    ro, _ = oracle_fwd(inp)
+    o1, _, _, _ = gpu_fwd(inp)
+    print(f"      one bf16 term: err(o)={rel_err(o1, ro):.3e}", flush=True)
+    o2, _ = check_fwd(inp, gdr.Options(precise_vnew=1), label="nearly parallel keys, precise Vnew")
+    assert rel_err(o2, ro) < rel_err(o1, ro)
+
+
 @pytest.mark.parametrize("dtype,K,seg", [("bf16", 128, 3), ("bf16", 64, 1), ("f32", 32, 2)])
 def test_exact_segments_for_uncertified_heads(dtype, K, seg):
     # g = 0 on every head: no warmup window is certified, so every head takes
