@@ -116,6 +116,14 @@ def plan(B, T, Hq, Hv, K, cu=None, mode=gdr.CP_AUTO, seg=0, warm=0):
     return gdr.gdr_chunk_fwd_plan(q, v, cu, gdr.Options(mode, seg, warm))
 
 
+def test_precise_vnew_option_is_validated():
+    q = torch.empty((1, 256, 2, 128), dtype=torch.bfloat16, device="meta")
+    v = torch.empty((1, 256, 4, 128), dtype=torch.bfloat16, device="meta")
+    assert gdr.gdr_chunk_fwd_plan(q, v, None, gdr.Options(precise_vnew=1))["total_chunks"] == 4
+    with pytest.raises(gdr.GdrError, match="precise_vnew"):
+        gdr.gdr_chunk_fwd_plan(q, v, None, gdr.Options(precise_vnew=2))
+
+
 def test_planner_cp_for_few_heads_long_context():
     info = plan(1, 65536, 4, 8, 128)
     assert info["total_chunks"] == 1024 and info["v_blocks"] == 1
