@@ -266,8 +266,10 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15, sl = l & 15;
   const bool owner = w < NWV;
   const int col = 16 * w + t;
-  const bool certified =
-      head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, true);
+  const float* hcert = p.cert + (long)h * s.NTtot + c0;
+  const int send = min(pseg * L + L, nch);   // the segment's end chunk
+  const float wpre = TRANS ? 0.f : warmup_first(hcert, send, 1, nch - send, p.warmup);
+  const bool certified = head_certified(hcert, nseg, nch, L, p.warmup, p.log_eps, true);
   const int gseg = s.seg_at(n) + pseg;
   const long hbase = ((long)n * p.Hv + h) * KD * VD;
   // chunks crs down to cbeg; those below cend are the segment's own
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
     crs = cend - 1;
     if (pseg == nseg - 1) ginit = p.dht ? p.dht + hbase : nullptr;
   } else if (certified) {
-    const int wu = short_warmup(p.cert + (long)h * s.NTtot + c0, cend, 1, nch - cend, p.warmup, p.log_eps);
+    const int wu = short_warmup(hcert, cend, 1, nch - cend, p.warmup, p.log_eps, wpre);
     crs = min(cend + wu, nch) - 1;
     if (crs == nch - 1) ginit = p.dht ? p.dht + hbase : nullptr;
   } else if (p.dhstart) {
@@ -291,11 +293,15 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
     ginit = p.dht ? p.dht + hbase : nullptr;
   }
   auto krow = [&](int rb, int e) { return 32 * (rb >> 1) + 8 * q + 4 * (rb & 1) + e; };
-  f32x4 ds[NKB];
+  f32x4 ds[NKB];   // one branch around all the loads, so that they are issued together
 #pragma unroll
-  for (int rb = 0; rb < NKB; ++rb)
+  for (int rb = 0; rb < NKB; ++rb) ds[rb] = zero4();
+  if (owner && ginit) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ds[rb][e] = (owner && ginit) ? ginit[(long)krow(rb, e) * VD + col] : 0.f;
+    for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[rb][e] = ginit[(long)krow(rb, e) * VD + col];
+  }
 
   // Copies of chunk jc's tiles into buffer bc in four parts (0 W, 1 dO, 2 K,
   // 3 Q and the gate cumsums); rows past the chunk read as zero.

@@ -711,15 +711,21 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
 // window's length, so a shorter window that meets the threshold keeps the
 // certificate's bound.  Returns W when no shorter window does (the head
 // certificate holds for W, or the window reaches the sequence edge and runs
-// exactly).  Called by every lane of a wave, uniform arguments.
+// exactly).  Called by every lane of a wave, uniform arguments; x0 is this
+// lane's value of the first 64 window chunks, loaded ahead by warmup_first()
+// so that its latency overlaps the head certificate's loads.
+__device__ __forceinline__ float warmup_first(const float* cert, int first, int step, int avail, int W) {
+  const int l = lane_id();
+  return l < min(W, avail) ? cert[first + step * l] : 0.f;
+}
 __device__ __forceinline__ int short_warmup(const float* cert, int first, int step, int avail, int W,
-                                            float log_eps) {
+                                            float log_eps, float x0) {
   const int l = lane_id();
   const int n = min(W, avail);
   float carry = 0.f;
   for (int b = 0; b < n; b += 64) {
     const int i = b + l;
-    const float x = wave_inclusive_scan(i < n ? cert[first + step * i] : 0.f) + carry;
+    const float x = wave_inclusive_scan(b == 0 ? x0 : (i < n ? cert[first + step * i] : 0.f)) + carry;
     const unsigned long long hit = __ballot(i < n && x <= log_eps);
     if (hit) return b + __ffsll((long long)hit);   // lowest hitting lane, 1-based
     carry = __shfl(x, 63, 64);

@@ -1058,8 +1058,9 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   const bool owner = NWV == FNW || w < NWV;   // a constant when every wave owns columns
   auto vcol = [&](int cb) { return CBW == 2 ? 32 * w + 2 * t + cb : 16 * w + t; };
 
-  const bool certified =
-      head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0);
+  const float* hcert = p.cert + (long)h * s.NTtot + c0;
+  const float wpre = TRANS ? 0.f : warmup_first(hcert, pseg * L - 1, -1, pseg * L, p.warmup);
+  const bool certified = head_certified(hcert, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0);
   const int gseg = s.seg_at(n) + pseg;          // global segment index
   const bool exact = !certified && p.hstart != nullptr;
   int cstart, cbeg, cend;
@@ -1072,7 +1073,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   } else if (certified) {
     cbeg = pseg * L;
     cend = min(cbeg + L, nch);
-    const int wu = short_warmup(p.cert + (long)h * s.NTtot + c0, cbeg - 1, -1, cbeg, p.warmup, p.log_eps);
+    const int wu = short_warmup(hcert, cbeg - 1, -1, cbeg, p.warmup, p.log_eps, wpre);
     cstart = (pseg == 0) ? 0 : max(0, cbeg - wu);
     write_final = (pseg == nseg - 1);
   } else if (exact) {
@@ -1098,21 +1099,30 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   } else if (exact) {
     hinit = p.hstart + ((long)h * p.total_segs + gseg) * KD * VD;
   }
+  // One branch around all the loads, so that they are issued together.
   f32x4 hs[NKB][CBW];
 #pragma unroll
   for (int rb = 0; rb < NKB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < CBW; ++cb) {
-      hs[rb][cb] = zero4();
-      if (owner) {
+    for (int cb = 0; cb < CBW; ++cb) hs[rb][cb] = zero4();
+  if (owner && hinit) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = F32 ? 16 * rb + acc_row(e) : krow(rb, e), col = vcol(cb);
-          if (no_u) hs[rb][cb][e] = (row == col) ? 1.f : 0.f;
-          else if (hinit) hs[rb][cb][e] = hinit[(long)row * VD + col];
-        }
-      }
-    }
+    for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hs[rb][cb][e] = hinit[(long)(F32 ? 16 * rb + acc_row(e) : krow(rb, e)) * VD + vcol(cb)];
+  }
+  if (TRANS && no_u && owner) {
+#pragma unroll
+    for (int rb = 0; rb < NKB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hs[rb][cb][e] = ((F32 ? 16 * rb + acc_row(e) : krow(rb, e)) == vcol(cb)) ? 1.f : 0.f;
+  }
 
   // Copies of chunk jc's tiles into buffer b (rows past the chunk read as
   // zero), in four parts (0 W, 1 U, 2 K, 3 Q and the gate cumsums); the
