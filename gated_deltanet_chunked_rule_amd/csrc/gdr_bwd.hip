@@ -215,13 +215,14 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   constexpr int VD = KD;
   constexpr int VEC = 8;
   constexpr int NCH = KD / VEC;
-  constexpr int PP = Pitch<T, CH>::value;
   constexpr int TE = CH * KD;
   constexpr int NKB = KD / 16, NCB = VD / 16;
   constexpr int NWV = NCB < FNW ? NCB : FNW;
   static_assert(NCB <= FNW && NKB % 2 == 0, "one column tile per wave, paired row tiles");
   __shared__ __align__(16) T sW0[CH * CH], sQ0[TE], sK0[TE], sO0[TE], sW1[CH * CH], sQ1[TE], sK1[TE], sO1[TE];
-  __shared__ __align__(16) T sP[CH * PP];
+  // P^T as a swizzled 64-wide tile (16-byte fragment reads without bank conflicts)
+  constexpr int PSZ = CH * CH;
+  __shared__ __align__(16) T sP[PSZ];
   __shared__ __align__(16) T sDh[TRANS ? 8 : KD * KD];   // staged dh rows of a chunk
   __shared__ __align__(16) float sG0[CH], sG1[CH], sD0[3 * CH], sD1[3 * CH];
   if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   if (crs >= cbeg) copy_chunk(crs, ic<0>());
   // the upper P tiles (0,1) and (2,3) are always zero: written once here
   // (published by the barrier below), never recomputed
-  for (int i = threadIdx.x; i < CH * PP; i += FNT) sP[i] = from_f<T>(0.f);
+  for (int i = threadIdx.x; i < PSZ; i += FNT) sP[i] = from_f<T>(0.f);
   wait_copies(crs, ic<0>());
 
   auto step = [&](auto bc, int jc) __attribute__((always_inline)) -> bool {
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
             const int r = 16 * ti[m] + acc_row(e), c = 16 * tj[m] + acc_col();
             const float v = (r >= c && r < len) ? p.scale * __expf(sG[r] - sG[c]) * pa[m][e] : 0.f;
             const int pr = (r & ~31) + 8 * ((r >> 2) & 3) + 4 * ((r >> 4) & 1) + (r & 3);
-            sP[c * PP + pr] = from_f<T>(v);
+            sP[tix8(c, pr)] = from_f<T>(v);
           }
         }
       }
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
       for (int ks = 0; ks < 2; ++ks)   // s P^T dO: row tile tt needs tokens >= 16 tt
 #pragma unroll
         for (int tt = 0; tt <= 2 * ks + 1; ++tt) {
-          const bf16x8 ap = *reinterpret_cast<const bf16x8*>(sP + (16 * tt + t) * PP + 32 * ks + 8 * q);
+          const bf16x8 ap = *reinterpret_cast<const bf16x8*>(sP + tix8(16 * tt + t, 32 * ks + 8 * q));
           dv[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, bo[ks], dv[tt], 0, 0, 0);
         }
 #pragma unroll

@@ -476,12 +476,22 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 
 // ---- staged chunk tiles (the fused state kernels) ----
 // Staged tiles are unpadded: row r holds NCH 16-byte pieces, piece c stored
-// at position c ^ stage_swz(r), which keeps 8-byte fragment reads and the
-// transposing reads free of bank conflicts.
+// at position c ^ stage_swz(r).  The swizzles were chosen by measured LDS
+// throughput on gfx950 for the access patterns of the kernels (8 waves per
+// CU, 16-byte MFMA fragment reads of rows 16i + t, 8-byte and transposing
+// reads of four-row blocks).  A 16-byte read moves at full rate when the
+// pieces that lanes 2m and 2m + 1 read differ only in bit 0, so the row's
+// bit 0 goes to the piece's bit 0; for 128-wide rows the other row bits go
+// to piece bits 2, 3, 1, which also keeps the transposing reads at the rate
+// of the previous layout (row bits 0-2 to piece bits 1-3): fragment reads at
+// 228 instead of 128 B per clock and CU.  For 64-wide rows (two rows a
+// 256-byte bank line) row bits 1, 2, 3 go to piece bits 0, 2, 1: fragment
+// reads at 216 instead of 128, the output pass's 8-byte A'' reads at 172
+// instead of 71, transposing reads at 137 instead of 165.
 template <int NCH>
 __device__ __forceinline__ int stage_swz(int r) {
-  if constexpr (NCH == 16) return 2 * (r & 7) + ((r >> 3) & 1);
-  else if constexpr (NCH == 8) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  if constexpr (NCH == 16) return (r & 1) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 1);
+  else if constexpr (NCH == 8) return ((r >> 1) & 1) | (((r >> 2) & 1) << 2) | (((r >> 3) & 1) << 1);
   else return (r >> 2) & (NCH - 1);
 }
 

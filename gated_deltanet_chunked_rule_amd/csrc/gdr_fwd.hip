@@ -1008,7 +1008,10 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   constexpr bool AP = !F32;
   constexpr int TW = AP ? CH * CH : TE;
   __shared__ __align__(16) T sW0[TW], sQ0[TE], sK0[TE], sU0[TE], sW1[TW], sQ1[TE], sK1[TE], sU1[TE];
-  __shared__ __align__(16) T sP[CH * PP];
+  // P: bf16 as a swizzled 64-wide tile (16-byte fragment reads without bank
+  // conflicts), fp32 row-padded
+  constexpr int PSZ = F32 ? CH * PP : CH * CH;
+  __shared__ __align__(16) T sP[PSZ];
   __shared__ __align__(16) T sO[F32 ? 8 : TE];     // bf16 output rows (fp32 stores directly)
   __shared__ __align__(16) float sG0[CH], sG1[CH], sD0[3 * CH], sD1[3 * CH];
   if (p.Hq < 0) {  // never taken: an ordinary store keeps the copy-only arrays from being folded away
@@ -1214,7 +1217,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
   // P Vnew read are always zero: written once here (published by the
   // barrier below), never recomputed.
   if constexpr (MODE == 0 || MODE == 4) {
-    for (int i = threadIdx.x; i < CH * PP; i += FNT) sP[i] = from_f<T>(0.f);
+    for (int i = threadIdx.x; i < PSZ; i += FNT) sP[i] = from_f<T>(0.f);
   }
   wait_copies(cstart, ic<0>());
 
@@ -1329,7 +1332,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
             // 8-byte store).
             const int rr = r0 + (t & 3), cc = 16 * ptj[m] + 4 * (t >> 2);
             const int pc = (cc & ~31) + 8 * ((cc >> 2) & 3) + 4 * ((cc >> 4) & 1);
-            *reinterpret_cast<uint2*>(sP + rr * PP + pc) = pack4_bf16(quad_t(pv));
+            *reinterpret_cast<uint2*>(sP + tix8(rr, pc)) = pack4_bf16(quad_t(pv));
           }
         }
       }
@@ -1562,7 +1565,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int tt = 2 * ks; tt < 4; ++tt) ap[ks][tt] = *reinterpret_cast<const bf16x8*>(sP + (16 * tt + t) * PP + 32 * ks + 8 * q);
+          for (int tt = 2 * ks; tt < 4; ++tt) ap[ks][tt] = *reinterpret_cast<const bf16x8*>(sP + tix8(16 * tt + t, 32 * ks + 8 * q));
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8 vb[CBW];
