@@ -306,8 +306,8 @@ def main():
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
-              "the path is a single-GPU kernel and has no multi-GPU mode.", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (--gpus {args.gpus} requested); "
+              "its kernels cover one GPU's share and it has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
 
     import torch

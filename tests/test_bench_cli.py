@@ -1,4 +1,4 @@
-"""bench.py's command-line contract that needs no GPU: this build runs on
+"""bench.py's command-line contract that needs no GPU: the library runs on
 one GPU only, so --gpus N with N > 1 exits with a message before touching
 the device."""
 import os
