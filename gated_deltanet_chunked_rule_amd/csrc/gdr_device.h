@@ -82,6 +82,16 @@ constexpr int kBufWord3 = 0x00020000;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
 }
+// The same descriptor for a base and range that are equal across the wave
+// but that the compiler cannot prove uniform: both are taken from the first
+// active lane, so the descriptor lives in scalar registers (a descriptor in
+// vector registers makes every buffer access a loop over distinct values).
+__device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, long bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane((int)bytes));
+}
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   uint4 u;

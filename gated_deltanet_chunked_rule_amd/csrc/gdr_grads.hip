@@ -84,28 +84,42 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 
   // staged-tile element offsets: 128-wide (16 pieces a row) and 64-wide (8)
   auto t16 = [](int r, int c) __attribute__((always_inline)) { return (r * 16 + ((c >> 3) ^ stage_swz<16>(r))) * 8 + (c & 7); };
-  auto t8 = [](int r, int c) __attribute__((always_inline)) { return (r * 8 + ((c >> 3) ^ stage_swz<8>(r))) * 8 + (c & 7); };
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   auto trd = [](const T* a) __attribute__((always_inline)) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
   };
-  // Fragments of V_MFMA_F32_16X16X32_BF16.  ra: row m of X, contraction
+  // Byte offsets of the fragment accesses.  The row swizzles use the low
+  // four row bits only, and every pattern below puts the lane's coordinates
+  // in those bits, so each pattern has a per-lane root offset (set at every
+  // unit, see body); the step's part then adds a multiple of the row-block
+  // size (16 rows of a 128-wide tile: 4096 bytes, of a 64-wide one: 2048)
+  // or XORs a contraction / column block into bits 5-7, which the root's
+  // piece index occupies (the piece index of a block is the XOR of the
+  // block's and the lane's).  With rho = 4q + t/4 and rho' = 4q + t%4:
+  //   B16, B8: row 16i + t, contraction 32ks + 8q (A fragments)
+  //   R16, R8: row 32ks + rho (+16), column 16m + 4(t&3) (transposing reads)
+  //   W16, W8: row 16i + rho', columns 16m + 4(t/4) .. +3 (8-byte tile writes)
+  uint32_t B16, B8, R8, R16w, W8, W16w;
+  auto at = [](const T* X, uint32_t off) __attribute__((always_inline)) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(X) + off);
+  };
+  // Fragments of V_MFMA_F32_16X16X32_BF16.  ra: row 16i + t of X, contraction
   // 32ks + 8q + j.  rb: contraction 32ks + {4q, 16 + 4q} + i over the rows of
-  // X at column c0 + t (the row set of accumulator tiles 2ks, 2ks + 1).
+  // X at column 16m + t (the row set of accumulator tiles 2ks, 2ks + 1).
   // rt: contraction 32ks + 8q + j over the rows of X at column c0 + t.
-  auto ra16 = [&](const T* X, int m, int ks) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8*>(X + t16(m, 32 * ks + 8 * q));
+  auto ra16 = [&](const T* X, int i, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(at(X, 4096 * i + (B16 ^ (64 * ks))));
   };
-  auto ra8 = [&](const T* X, int m, int ks) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8*>(X + t8(m, 32 * ks + 8 * q));
+  auto ra8 = [&](const T* X, int i, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(at(X, 2048 * i + (B8 ^ (64 * ks))));
   };
-  auto rb16 = [&](const T* X, int ks, int c0) __attribute__((always_inline)) {
-    const int r = 32 * ks + 4 * q + (t >> 2), c = c0 + 4 * (t & 3);
-    return cat4(trd(X + t16(r, c)), trd(X + t16(r + 16, c)));
+  auto rb16w = [&](const T* X, int ks) __attribute__((always_inline)) {   // m = w
+    const T* a = at(X, 8192 * ks + R16w);
+    return cat4(trd(a), trd(a + 2048));
   };
-  auto rb8 = [&](const T* X, int ks, int c0) __attribute__((always_inline)) {
-    const int r = 32 * ks + 4 * q + (t >> 2), c = c0 + 4 * (t & 3);
-    return cat4(trd(X + t8(r, c)), trd(X + t8(r + 16, c)));
+  auto rb8 = [&](const T* X, int ks, int m) __attribute__((always_inline)) {
+    const T* a = at(X, 4096 * ks + (R8 ^ (32 * m)));
+    return cat4(trd(a), trd(a + 1024));
   };
   auto rt16 = [&](const T* X, int ks, int c0) __attribute__((always_inline)) {
     const int r = 32 * ks + 8 * q + (t >> 2), c = c0 + 4 * (t & 3);
@@ -113,7 +127,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   };
   // X[16tt + 4q + i][dcol], i < 4 (the rows of this lane's accumulator entries)
   auto rows4 = [&](const T* X, int tt) __attribute__((always_inline)) {
-    const i16x4 v = trd(X + t16(16 * tt + 4 * q + (t >> 2), 16 * w + 4 * (t & 3)));
+    const i16x4 v = trd(at(X, 4096 * tt + R16w));
     f32x4 f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float((uint32_t)(uint16_t)v[i] << 16);
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   };
   // accumulator tile (row block rb, column block cb) of a 64 x 64 LDS matrix, 8-byte writes
   auto st_tile8 = [&](T* X, int rb, int cb, f32x4 v) __attribute__((always_inline)) {
-    *reinterpret_cast<uint2*>(X + t8(16 * rb + 4 * q + (t & 3), 16 * cb + 4 * (t >> 2))) = pack4_bf16(quad_t(v));
+    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(X) + 2048 * rb + (W8 ^ (32 * cb))) = pack4_bf16(quad_t(v));
   };
   auto mf = [](bf16x8 a, bf16x8 b, f32x4 c) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -257,6 +271,15 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   auto body = [&](auto abc, int j) __attribute__((always_inline)) -> bool {
     constexpr int ab = decltype(abc)::value;
     asm volatile("" : "+v"(q), "+v"(t), "+v"(dcol));
+    {
+      const int rho = 4 * q + (t >> 2), rhp = 4 * q + (t & 3);
+      B16 = 256 * t + 16 * (q ^ stage_swz<16>(t));
+      B8 = 128 * t + 16 * (q ^ stage_swz<8>(t));
+      R8 = 128 * rho + 8 * (t & 1) + 16 * (((t >> 1) & 1) ^ stage_swz<8>(rho));
+      W8 = 128 * rhp + 8 * ((t >> 2) & 1) + 16 * ((t >> 3) ^ stage_swz<8>(rhp));
+      R16w = (256 * rho + 8 * (t & 1) + 16 * (((t >> 1) & 1) ^ stage_swz<16>(rho))) ^ (32 * w);
+      W16w = (256 * rhp + 8 * ((t >> 2) & 1) + 16 * ((t >> 3) ^ stage_swz<16>(rhp))) ^ (32 * w);
+    }
     wsc = w;
     asm volatile("" : "+s"(wsc));
     Unit nu;
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         kt1[ks] = rt16(sK, ks, 16 * w);
-        kt2[ks] = rb16(sK, ks, 16 * w);
+        kt2[ks] = rb16w(sK, ks);
       }
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) { dq[tt] = zero4(); dk[tt] = zero4(); }
@@ -303,11 +326,11 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       f32x4 dP[2] = {zero4(), zero4()}, Sqk[2] = {zero4(), zero4()};   // dO Vnew^T and raw Q K^T
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = ra16(sdO, 16 * ti + t, ks), aq = ra16(sQ, 16 * ti + t, ks);
+        const bf16x8 a = ra16(sdO, ti, ks), aq = ra16(sQ, ti, ks);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          dP[m] = mf(a, ra16(sVn, 16 * (tj0 + m) + t, ks), dP[m]);
-          Sqk[m] = mf(aq, ra16(sK, 16 * (tj0 + m) + t, ks), Sqk[m]);
+          dP[m] = mf(a, ra16(sVn, tj0 + m, ks), dP[m]);
+          Sqk[m] = mf(aq, ra16(sK, tj0 + m, ks), Sqk[m]);
         }
       }
       float rx[4] = {0.f, 0.f, 0.f, 0.f};
@@ -341,12 +364,15 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int st = 0; st < 4; ++st) vb[st] = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bd = rb16(sdVn, ks, 16 * w);
+        const bf16x8 bd = rb16w(sdVn, ks);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) vb[st] = mf(rb8(sA, ks, 16 * st), bd, vb[st]);
+        for (int st = 0; st < 4; ++st) vb[st] = mf(rb8(sA, ks, st), bd, vb[st]);
       }
       f32x4 dbL[4];
-      void* dvp = prm()->dv;
+      // dv rows through a descriptor covering the chunk's rows (rows past
+      // the chunk are dropped by the range check)
+      const rsrc_t dvr = make_rsrc_u((const T*)prm()->dv + ((long)t0 * Hv + h) * VD, (long)len * Hv * VD * 2);
+      const uint32_t dvo = (uint32_t)(((4 * q + (t & 3)) * Hv * VD + 16 * w + 4 * (t >> 2)) * 2);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const f32x4 bt = fac4(sBt, st), ve = rows4(sV, st);
@@ -356,9 +382,8 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
           dbL[st][e] = vb[st][e] * ve[e];
           o[e] = bt[e] * vb[st][e];
         }
-        const int r = 16 * st + 4 * q + (t & 3);   // after the transpose: row r, columns 16w + 4(t/4) ..
-        const uint2 u = pack4_bf16(quad_t(o));
-        if (r < len) *reinterpret_cast<uint2*>((T*)dvp + ((long)(t0 + r) * Hv + h) * VD + 16 * w + 4 * (t >> 2)) = u;
+        // after the transpose: row 16st + 4q + t%4, columns 16w + 4(t/4) ..
+        buf_store8(dvr, dvo + (uint32_t)(16 * st * Hv * VD * 2), pack4_bf16(quad_t(o)));
       }
       sDbP[w][16 * (t >> 2) + 4 * q + (t & 3)] += own_rows(dbL);
     }
@@ -376,7 +401,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 b = pass == 2 ? Df[ks] : Hf[ks];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc[tt] = mf(ra16(X, 16 * tt + t, ks), b, acc[tt]);
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = mf(ra16(X, tt, ks), b, acc[tt]);
         if (pass == 2) {
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
           struct Pairs { bf16x2 v[4]; };
@@ -397,7 +422,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
           }
         } else if (pass == 1) {   // dW rows
           const uint2 u = pack4_bf16(quad_t(-acc[tt]));
-          *reinterpret_cast<uint2*>(sW + t16(16 * tt + 4 * q + (t & 3), 16 * w + 4 * (t >> 2))) = u;
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(sW) + 4096 * tt + W16w) = u;
         } else {
           const f32x4 dc = fac4(sDec, tt), ke = rows4(sK, tt);
 #pragma unroll
@@ -423,13 +448,13 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     {  // dQ += dPD K;  dK += dPD^T Q
       bf16x8 bq[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) bq[ks] = rb16(sQ, ks, 16 * w);
+      for (int ks = 0; ks < 2; ++ks) bq[ks] = rb16w(sQ, ks);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          dq[tt] = mf(ra8(sPD, 16 * tt + t, ks), kt1[ks], dq[tt]);
-          dk[tt] = mf(rb8(sPD, ks, 16 * tt), bq[ks], dk[tt]);
+          dq[tt] = mf(ra8(sPD, tt, ks), kt1[ks], dq[tt]);
+          dk[tt] = mf(rb8(sPD, ks, tt), bq[ks], dk[tt]);
         }
     }
     lds_barrier();   // Q and dPD are no longer read
@@ -442,14 +467,14 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       f32x4 ta[2] = {zero4(), zero4()}, tb[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a1 = ra16(sW, 16 * ti + t, ks), a2 = ra16(sdVn, 16 * ti + t, ks);
-        const bf16x8 ak = ra16(sK, 16 * ti + t, ks);
+        const bf16x8 a1 = ra16(sW, ti, ks), a2 = ra16(sdVn, ti, ks);
+        const bf16x8 ak = ra16(sK, ti, ks);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const bf16x8 bk = ra16(sK, 16 * (tj0 + m) + t, ks);
+          const bf16x8 bk = ra16(sK, tj0 + m, ks);
           ta[m] = mf(a1, bk, ta[m]);
           Skk[m] = mf(ak, bk, Skk[m]);
-          tb[m] = mf(a2, ra16(sV, 16 * (tj0 + m) + t, ks), tb[m]);
+          tb[m] = mf(a2, ra16(sV, tj0 + m, ks), tb[m]);
         }
       }
 #pragma unroll
@@ -470,9 +495,9 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int st = 0; st < 4; ++st) kb[st] = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bw = rb16(sW, ks, 16 * w);
+        const bf16x8 bw = rb16w(sW, ks);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) kb[st] = mf(rb8(sA, ks, 16 * st), bw, kb[st]);
+        for (int st = 0; st < 4; ++st) kb[st] = mf(rb8(sA, ks, st), bw, kb[st]);
       }
       f32x4 rowK[4], dbL[4];
 #pragma unroll
@@ -503,9 +528,9 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       f32x4 m1[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = rb8(sA, ks, 16 * ti);
+        const bf16x8 a = rb8(sA, ks, ti);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) m1[m] = mf(a, rb8(sdA, ks, 16 * (tj0 + m)), m1[m]);
+        for (int m = 0; m < 2; ++m) m1[m] = mf(a, rb8(sdA, ks, tj0 + m), m1[m]);
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) st_tile8(sM1, ti, tj0 + m, m1[m]);
@@ -515,9 +540,9 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       f32x4 dl[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = ra8(sM1, 16 * ti + t, ks);
+        const bf16x8 a = ra8(sM1, ti, ks);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) dl[m] = mf(a, ra8(sA, 16 * (tj0 + m) + t, ks), dl[m]);
+        for (int m = 0; m < 2; ++m) dl[m] = mf(a, ra8(sA, tj0 + m, ks), dl[m]);
       }
       float rx[4] = {0.f, 0.f, 0.f, 0.f}, bs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -556,8 +581,8 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dk[tt] = mf(ra8(sE, 16 * tt + t, ks), kt1[ks], dk[tt]);
-        dk[tt] = mf(rb8(sE, ks, 16 * tt), kt2[ks], dk[tt]);
+        dk[tt] = mf(ra8(sE, tt, ks), kt1[ks], dk[tt]);
+        dk[tt] = mf(rb8(sE, ks, tt), kt2[ks], dk[tt]);
       }
     if (w == 0) {   // dgamma row sums, dg as its reverse cumulative sum, dbeta
       float dgm = 0.f, db = 0.f;
@@ -584,16 +609,14 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     }
     if (cu.gi == G - 1) {   // the group's dq and dk rows
       KArgs* pa = prm();
-      void *dqp = pa->dq, *dkp = pa->dk;
+      const long e0 = ((long)t0 * Hq + cu.hk) * KD, nb = (long)len * Hq * KD * 2;
+      const rsrc_t dqr = make_rsrc_u((const T*)pa->dq + e0, nb), dkr = make_rsrc_u((const T*)pa->dk + e0, nb);
+      const uint32_t o = (uint32_t)(((4 * q + (t & 3)) * Hq * KD + 16 * w + 4 * (t >> 2)) * 2);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int r = 16 * tt + 4 * q + (t & 3);
-        const uint2 uq = pack4_bf16(quad_t(dq[tt])), uk = pack4_bf16(quad_t(dk[tt]));
-        if (r < len) {
-          const long o = ((long)(t0 + r) * Hq + cu.hk) * KD + 16 * w + 4 * (t >> 2);
-          *reinterpret_cast<uint2*>((T*)dqp + o) = uq;
-          *reinterpret_cast<uint2*>((T*)dkp + o) = uk;
-        }
+      for (int tt = 0; tt < 4; ++tt) {   // row 16tt + 4q + t%4 (rows past the chunk are dropped)
+        const uint32_t ot = o + (uint32_t)(16 * tt * Hq * KD * 2);
+        buf_store8(dqr, ot, pack4_bf16(quad_t(dq[tt])));
+        buf_store8(dkr, ot, pack4_bf16(quad_t(dk[tt])));
       }
     }
     // the next unit's copies have landed; every wave is done with this unit
