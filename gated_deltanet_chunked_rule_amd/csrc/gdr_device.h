@@ -705,6 +705,20 @@ __device__ __forceinline__ float col_group_sum(float x) {
   return x;
 }
 
+// Four sums over the four lane groups at once: lane 16g + c receives the sum
+// over g' of x[g] held by lanes 16g' + c.  Two exchange steps with the
+// partners g ^ 1 and g ^ 2; at each a lane keeps the half of its values whose
+// index bit matches its own group bit and adds the partner's copy of it.
+__device__ __forceinline__ float group_sums4(const float (&x)[4]) {
+  const int g = lane_id() >> 4;
+  const bool b = (g & 1) != 0;
+  float y[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) y[j] = (b ? x[2 * j + 1] : x[2 * j]) + __shfl_xor(b ? x[2 * j] : x[2 * j + 1], 16, 64);
+  const bool c = (g & 2) != 0;
+  return (c ? y[1] : y[0]) + __shfl_xor(c ? y[0] : y[1], 32, 64);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);

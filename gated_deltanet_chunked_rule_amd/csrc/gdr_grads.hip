@@ -95,11 +95,13 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   // size (16 rows of a 128-wide tile: 4096 bytes, of a 64-wide one: 2048)
   // or XORs a contraction / column block into bits 5-7, which the root's
   // piece index occupies (the piece index of a block is the XOR of the
-  // block's and the lane's).  With rho = 4q + t/4 and rho' = 4q + t%4:
+  // block's and the lane's).  With rho = 4q + t/4:
   //   B16, B8: row 16i + t, contraction 32ks + 8q (A fragments)
   //   R16, R8: row 32ks + rho (+16), column 16m + 4(t&3) (transposing reads)
-  //   W16, W8: row 16i + rho', columns 16m + 4(t/4) .. +3 (8-byte tile writes)
-  uint32_t B16, B8, R8, R16w, W8, W16w;
+  //   V16, V8: row 16i + t, columns 16m + 4q .. +3 (8-byte reads and writes
+  //            of the four columns a transposed accumulator tile holds)
+  // (R16 and V16 only at this wave's column block m = w.)
+  uint32_t B16, B8, R8, R16w, V8, V16w;
   auto at = [](const T* X, uint32_t off) __attribute__((always_inline)) {
     return reinterpret_cast<const T*>(reinterpret_cast<const char*>(X) + off);
   };
@@ -125,30 +127,27 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     const int r = 32 * ks + 8 * q + (t >> 2), c = c0 + 4 * (t & 3);
     return cat4(trd(X + t16(r, c)), trd(X + t16(r + 4, c)));
   };
-  // X[16tt + 4q + i][dcol], i < 4 (the rows of this lane's accumulator entries)
-  auto rows4 = [&](const T* X, int tt) __attribute__((always_inline)) {
-    const i16x4 v = trd(at(X, 4096 * tt + R16w));
+  // Every product below is computed with its operands swapped (the A and B
+  // fragments have the same register layout), so that an accumulator tile
+  // holds the transposed block: lane (q, t) has row 16i + t and the four
+  // columns 16m + 4q + e, e < 4, which leave as one 8-byte store.
+  // X[16i + t][16w + 4q + e] of a 128-wide tile, as floats
+  auto row4 = [&](const T* X, int i) __attribute__((always_inline)) {
+    const uint2 u = *reinterpret_cast<const uint2*>(at(X, 4096 * i + V16w));
     f32x4 f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float((uint32_t)(uint16_t)v[i] << 16);
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xffff0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xffff0000u);
     return f;
   };
-  auto fac4 = [&](const float* F, int tt) __attribute__((always_inline)) {
-    return *reinterpret_cast<const f32x4*>(F + 16 * tt + 4 * q);
+  // F[16i + 4q + e], e < 4 (per-token factors at a tile's columns)
+  auto fac4 = [&](const float* F, int i) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(F + 16 * i + 4 * q);
   };
-  // Row sums of per-lane partials x[tt][e] (rows 16tt + 4q + e); lane t
-  // receives the sum for tt = t / 4, e = t % 4, i.e. row 16(t/4) + 4q + t%4.
-  auto own_rows = [&](const f32x4 (&x)[4]) __attribute__((always_inline)) {
-    float v[16];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * tt + e] = x[tt][e];
-    return row16_sums16(v);
-  };
-  // accumulator tile (row block rb, column block cb) of a 64 x 64 LDS matrix, 8-byte writes
-  auto st_tile8 = [&](T* X, int rb, int cb, f32x4 v) __attribute__((always_inline)) {
-    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(X) + 2048 * rb + (W8 ^ (32 * cb))) = pack4_bf16(quad_t(v));
+  // a transposed accumulator tile (row block i, column block m) into a 64 x 64 LDS matrix
+  auto st_t8 = [&](T* X, int i, int m, f32x4 v) __attribute__((always_inline)) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(X) + 2048 * i + (V8 ^ (32 * m))) = pack4_bf16(v);
   };
   auto mf = [](bf16x8 a, bf16x8 b, f32x4 c) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -272,13 +271,13 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     constexpr int ab = decltype(abc)::value;
     asm volatile("" : "+v"(q), "+v"(t), "+v"(dcol));
     {
-      const int rho = 4 * q + (t >> 2), rhp = 4 * q + (t & 3);
+      const int rho = 4 * q + (t >> 2);
       B16 = 256 * t + 16 * (q ^ stage_swz<16>(t));
       B8 = 128 * t + 16 * (q ^ stage_swz<8>(t));
       R8 = 128 * rho + 8 * (t & 1) + 16 * (((t >> 1) & 1) ^ stage_swz<8>(rho));
-      W8 = 128 * rhp + 8 * ((t >> 2) & 1) + 16 * ((t >> 3) ^ stage_swz<8>(rhp));
       R16w = (256 * rho + 8 * (t & 1) + 16 * (((t >> 1) & 1) ^ stage_swz<16>(rho))) ^ (32 * w);
-      W16w = (256 * rhp + 8 * ((t >> 2) & 1) + 16 * ((t >> 3) ^ stage_swz<16>(rhp))) ^ (32 * w);
+      V8 = 128 * t + 16 * ((q >> 1) ^ stage_swz<8>(t)) + 8 * (q & 1);
+      V16w = (256 * t + 16 * ((q >> 1) ^ stage_swz<16>(t)) + 8 * (q & 1)) ^ (32 * w);
     }
     wsc = w;
     asm volatile("" : "+s"(wsc));
@@ -323,41 +322,45 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 
     // ---- phase 1: dPD tiles; dO h^T, dVnew h^T, Vnew dh^T (column split)
     {
-      f32x4 dP[2] = {zero4(), zero4()}, Sqk[2] = {zero4(), zero4()};   // dO Vnew^T and raw Q K^T
+      // dO Vnew^T and raw Q K^T, transposed tiles: row 16ti + t, columns 16(tj0 + m) + 4q + e
+      f32x4 dP[2] = {zero4(), zero4()}, Sqk[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 a = ra16(sdO, ti, ks), aq = ra16(sQ, ti, ks);
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          dP[m] = mf(a, ra16(sVn, tj0 + m, ks), dP[m]);
-          Sqk[m] = mf(aq, ra16(sK, tj0 + m, ks), Sqk[m]);
+          dP[m] = mf(ra16(sVn, tj0 + m, ks), a, dP[m]);
+          Sqk[m] = mf(ra16(sK, tj0 + m, ks), aq, Sqk[m]);
         }
       }
-      float rx[4] = {0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * ti + t;
+      const float gr = sGam[r];
+      float rx = 0.f;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        float cx = 0.f;
-        const int c = 16 * (tj0 + m) + t;
+        const f32x4 gc = fac4(sGam, tj0 + m);
+        float cx[4];
         f32x4 pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * ti + 4 * q + e;
-          const float v = (r >= c && r < len) ? scale * __expf(sGam[r] - sGam[c]) * dP[m][e] : 0.f;
+          const int c = 16 * (tj0 + m) + 4 * q + e;
+          const float v = (r >= c && r < len) ? scale * __expf(gr - gc[e]) * dP[m][e] : 0.f;
           const float x = v * Sqk[m][e];
-          rx[e] += x;
-          cx += x;
+          rx += x;
+          cx[e] = x;
           pv[e] = v;
         }
-        st_tile8(sPD, ti, tj0 + m, pv);
-        cx = col_group_sum(cx);
-        if (q == 0) sColP[w][c] -= cx;
+        st_t8(sPD, ti, tj0 + m, pv);
+        const float cs = row16_sums4(cx);   // column 16(tj0 + m) + 4q + t/4
+        if ((t & 3) == 0) sColP[w][16 * (tj0 + m) + 4 * q + (t >> 2)] -= cs;
       }
-      const float own = row16_sums4(rx);   // the sum for row 16 ti + 4q + t/4
-      if ((t & 3) == 0) sRowP[w][16 * ti + 4 * q + (t >> 2)] += own;
+      rx = col_group_sum(rx);
+      if (q == 0) sRowP[w][r] += rx;
     }
     // Three passes over h and dh (rows 16w..16w+15 as B fragments), each
     // folded right away: s Gamma_t dO h^T into dq, -dVnew h^T (dW) into LDS
-    // rows, dec_t Vnew dh^T into dk; with the row sums they feed.
+    // rows, dec_t Vnew dh^T into dk; with the row sums they feed.  Rows of
+    // the 64 x 16 blocks below are tokens 16i + t, columns 16w + 4q + e.
     {  // dVb = A^T dVnew (needs neither h nor dh): dv and its dbeta terms
       f32x4 vb[4];
 #pragma unroll
@@ -366,31 +369,31 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 bd = rb16w(sdVn, ks);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) vb[st] = mf(rb8(sA, ks, st), bd, vb[st]);
+        for (int st = 0; st < 4; ++st) vb[st] = mf(bd, rb8(sA, ks, st), vb[st]);
       }
-      f32x4 dbL[4];
       // dv rows through a descriptor covering the chunk's rows (rows past
       // the chunk are dropped by the range check)
       const rsrc_t dvr = make_rsrc_u((const T*)prm()->dv + ((long)t0 * Hv + h) * VD, (long)len * Hv * VD * 2);
-      const uint32_t dvo = (uint32_t)(((4 * q + (t & 3)) * Hv * VD + 16 * w + 4 * (t >> 2)) * 2);
+      const uint32_t dvo = (uint32_t)((t * Hv * VD + 16 * w + 4 * q) * 2);
+      float dbL[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const f32x4 bt = fac4(sBt, st), ve = rows4(sV, st);
+        const float bt = sBt[16 * st + t];
+        const f32x4 ve = row4(sV, st);
+        float db = 0.f;
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          dbL[st][e] = vb[st][e] * ve[e];
-          o[e] = bt[e] * vb[st][e];
+          db += vb[st][e] * ve[e];
+          o[e] = bt * vb[st][e];
         }
-        // after the transpose: row 16st + 4q + t%4, columns 16w + 4(t/4) ..
-        buf_store8(dvr, dvo + (uint32_t)(16 * st * Hv * VD * 2), pack4_bf16(quad_t(o)));
+        dbL[st] = db;
+        buf_store8(dvr, dvo + (uint32_t)(16 * st * Hv * VD * 2), pack4_bf16(o));
       }
-      sDbP[w][16 * (t >> 2) + 4 * q + (t & 3)] += own_rows(dbL);
+      sDbP[w][16 * q + t] += group_sums4(dbL);
     }
     float hdp = 0.f, rsum = 0.f;
-    f32x4 rowL[4];   // per-lane row partials (rows 16tt + 4q + e)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) rowL[tt] = zero4();
+    float rowL[4] = {0.f, 0.f, 0.f, 0.f};   // per-lane row partials (rows 16tt + t)
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
       const T* X = pass == 0 ? sdO : pass == 1 ? sdVn : sVn;
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 b = pass == 2 ? Df[ks] : Hf[ks];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc[tt] = mf(ra16(X, tt, ks), b, acc[tt]);
+        for (int tt = 0; tt < 4; ++tt) acc[tt] = mf(b, ra16(X, tt, ks), acc[tt]);
         if (pass == 2) {
           typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
           struct Pairs { bf16x2 v[4]; };
@@ -413,30 +416,31 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         if (pass == 0) {
-          const f32x4 gm = fac4(sGm, tt), qe = rows4(sQ, tt);
+          const float gm = sGm[16 * tt + t];
+          const f32x4 qe = row4(sQ, tt);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float vq = scale * gm[e] * acc[tt][e];   // s Gamma_t (dO h^T)
+            const float vq = scale * gm * acc[tt][e];   // s Gamma_t (dO h^T)
             dq[tt][e] += vq;
-            rowL[tt][e] += vq * qe[e];
+            rowL[tt] += vq * qe[e];
           }
         } else if (pass == 1) {   // dW rows
-          const uint2 u = pack4_bf16(quad_t(-acc[tt]));
-          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(sW) + 4096 * tt + W16w) = u;
+          *reinterpret_cast<uint2*>(reinterpret_cast<char*>(sW) + 4096 * tt + V16w) = pack4_bf16(-acc[tt]);
         } else {
-          const f32x4 dc = fac4(sDec, tt), ke = rows4(sK, tt);
+          const float dc = sDec[16 * tt + t];
+          const f32x4 ke = row4(sK, tt);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float vk = dc[e] * acc[tt][e];             // dec_t (Vnew dh^T)
+            const float vk = dc * acc[tt][e];             // dec_t (Vnew dh^T)
             dk[tt][e] += vk;
             const float rk = vk * ke[e];
             rsum += rk;
-            rowL[tt][e] -= rk;
+            rowL[tt] -= rk;
           }
         }
       }
     }
-    sRowP[w][16 * (t >> 2) + 4 * q + (t & 3)] += own_rows(rowL);
+    sRowP[w][16 * q + t] += group_sums4(rowL);
     rsum = wave_sum(rsum);
     hdp = wave_sum(hdp);
     if (l == 0) { sRed[0][w] = rsum; sRed[1][w] = hdp; }
@@ -453,8 +457,8 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          dq[tt] = mf(ra8(sPD, tt, ks), kt1[ks], dq[tt]);
-          dk[tt] = mf(rb8(sPD, ks, tt), bq[ks], dk[tt]);
+          dq[tt] = mf(kt1[ks], ra8(sPD, tt, ks), dq[tt]);
+          dk[tt] = mf(bq[ks], rb8(sPD, ks, tt), dk[tt]);
         }
     }
     lds_barrier();   // Q and dPD are no longer read
@@ -462,7 +466,7 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 
     // ---- phase 2: dA tiles; dKb = A^T dW and dVb = A^T dVnew (column split)
     T* sdA = sPD;
-    f32x4 Skk[2] = {zero4(), zero4()};   // raw K K^T tiles (for phase 3)
+    f32x4 Skk[2] = {zero4(), zero4()};   // raw K K^T tiles (for phase 3), transposed like dA
     {
       f32x4 ta[2] = {zero4(), zero4()}, tb[2] = {zero4(), zero4()};
 #pragma unroll
@@ -472,21 +476,22 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           const bf16x8 bk = ra16(sK, tj0 + m, ks);
-          ta[m] = mf(a1, bk, ta[m]);
-          Skk[m] = mf(ak, bk, Skk[m]);
-          tb[m] = mf(a2, ra16(sV, tj0 + m, ks), tb[m]);
+          ta[m] = mf(bk, a1, ta[m]);
+          Skk[m] = mf(bk, ak, Skk[m]);
+          tb[m] = mf(ra16(sV, tj0 + m, ks), a2, tb[m]);
         }
       }
+      const int r = 16 * ti + t;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int c = 16 * (tj0 + m) + t;
+        const f32x4 btc = fac4(sBt, tj0 + m), gmc = fac4(sGm, tj0 + m);
         f32x4 av;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * ti + 4 * q + e;
-          av[e] = (r > c) ? sBt[c] * (sGm[c] * ta[m][e] + tb[m][e]) : 0.f;
+          const int c = 16 * (tj0 + m) + 4 * q + e;
+          av[e] = (r > c) ? btc[e] * (gmc[e] * ta[m][e] + tb[m][e]) : 0.f;
         }
-        st_tile8(sdA, ti, tj0 + m, av);
+        st_t8(sdA, ti, tj0 + m, av);
       }
     }
     {  // dKb = A^T dW, rows s of A^T in blocks st
@@ -497,23 +502,26 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 bw = rb16w(sW, ks);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) kb[st] = mf(rb8(sA, ks, st), bw, kb[st]);
+        for (int st = 0; st < 4; ++st) kb[st] = mf(bw, rb8(sA, ks, st), kb[st]);
       }
-      f32x4 rowK[4], dbL[4];
+      float rowK[4], dbL[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const f32x4 bt = fac4(sBt, st), gm = fac4(sGm, st), ke = rows4(sK, st);
+        const float bt = sBt[16 * st + t], gm = sGm[16 * st + t];
+        const f32x4 ke = row4(sK, st);
+        float rk = 0.f, db = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          dk[st][e] += bt[e] * gm[e] * kb[st][e];
+          dk[st][e] += bt * gm * kb[st][e];
           const float kk = kb[st][e] * ke[e];
-          rowK[st][e] = bt[e] * gm[e] * kk;
-          dbL[st][e] = gm[e] * kk;
+          rk += bt * gm * kk;
+          db += gm * kk;
         }
+        rowK[st] = rk;
+        dbL[st] = db;
       }
-      const int rown = 16 * (t >> 2) + 4 * q + (t & 3);
-      sRowP[w][rown] += own_rows(rowK);
-      sDbP[w][rown] += own_rows(dbL);
+      sRowP[w][16 * q + t] += group_sums4(rowK);
+      sDbP[w][16 * q + t] += group_sums4(dbL);
     }
     lds_barrier();   // dA complete; dW, dVnew, V and K are no longer read from LDS
     if (has_next) {
@@ -530,10 +538,10 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 a = rb8(sA, ks, ti);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) m1[m] = mf(a, rb8(sdA, ks, tj0 + m), m1[m]);
+        for (int m = 0; m < 2; ++m) m1[m] = mf(rb8(sdA, ks, tj0 + m), a, m1[m]);
       }
 #pragma unroll
-      for (int m = 0; m < 2; ++m) st_tile8(sM1, ti, tj0 + m, m1[m]);
+      for (int m = 0; m < 2; ++m) st_t8(sM1, ti, tj0 + m, m1[m]);
     }
     lds_barrier();
     {
@@ -542,38 +550,41 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 a = ra8(sM1, ti, ks);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) dl[m] = mf(a, ra8(sA, tj0 + m, ks), dl[m]);
+        for (int m = 0; m < 2; ++m) dl[m] = mf(ra8(sA, tj0 + m, ks), a, dl[m]);
       }
-      float rx[4] = {0.f, 0.f, 0.f, 0.f}, bs[4] = {0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * ti + t;
+      const float gr = sGam[r], btr = sBt[r];
+      float rx = 0.f, bs = 0.f;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int c = 16 * (tj0 + m) + t;
-        float cx = 0.f;
+        const f32x4 gc = fac4(sGam, tj0 + m);
+        float cx[4];
         f32x4 evv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * ti + 4 * q + e;
-          float ev = 0.f;
+          const int c = 16 * (tj0 + m) + 4 * q + e;
+          float ev = 0.f, x = 0.f;
           if (r > c) {
-            const float D = __expf(sGam[r] - sGam[c]);
+            const float D = __expf(gr - gc[e]);
             const float dlv = -dl[m][e];
             const float y = dlv * D * Skk[m][e];
-            bs[e] += y;
-            ev = dlv * sBt[r] * D;
-            const float x = sBt[r] * y;
-            rx[e] += x;
-            cx += x;
+            bs += y;
+            ev = dlv * btr * D;
+            x = btr * y;
+            rx += x;
           }
+          cx[e] = x;
           evv[e] = ev;
         }
-        st_tile8(sE, ti, tj0 + m, evv);
-        cx = col_group_sum(cx);
-        if (q == 0) sColP[w][c] -= cx;
+        st_t8(sE, ti, tj0 + m, evv);
+        const float cs = row16_sums4(cx);   // column 16(tj0 + m) + 4q + t/4
+        if ((t & 3) == 0) sColP[w][16 * (tj0 + m) + 4 * q + (t >> 2)] -= cs;
       }
-      const float orow = row16_sums4(rx), odb = row16_sums4(bs);   // row 16 ti + 4q + t/4
-      if ((t & 3) == 0) {
-        sRowP[w][16 * ti + 4 * q + (t >> 2)] += orow;
-        sDbP[w][16 * ti + 4 * q + (t >> 2)] += odb;
+      rx = col_group_sum(rx);
+      bs = col_group_sum(bs);
+      if (q == 0) {
+        sRowP[w][r] += rx;
+        sDbP[w][r] += bs;
       }
     }
     lds_barrier();   // E complete; every partial sum is in
@@ -581,8 +592,8 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dk[tt] = mf(ra8(sE, tt, ks), kt1[ks], dk[tt]);
-        dk[tt] = mf(rb8(sE, ks, tt), kt2[ks], dk[tt]);
+        dk[tt] = mf(kt1[ks], ra8(sE, tt, ks), dk[tt]);
+        dk[tt] = mf(kt2[ks], rb8(sE, ks, tt), dk[tt]);
       }
     if (w == 0) {   // dgamma row sums, dg as its reverse cumulative sum, dbeta
       float dgm = 0.f, db = 0.f;
@@ -611,12 +622,12 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       KArgs* pa = prm();
       const long e0 = ((long)t0 * Hq + cu.hk) * KD, nb = (long)len * Hq * KD * 2;
       const rsrc_t dqr = make_rsrc_u((const T*)pa->dq + e0, nb), dkr = make_rsrc_u((const T*)pa->dk + e0, nb);
-      const uint32_t o = (uint32_t)(((4 * q + (t & 3)) * Hq * KD + 16 * w + 4 * (t >> 2)) * 2);
+      const uint32_t o = (uint32_t)((t * Hq * KD + 16 * w + 4 * q) * 2);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {   // row 16tt + 4q + t%4 (rows past the chunk are dropped)
+      for (int tt = 0; tt < 4; ++tt) {   // row 16tt + t (rows past the chunk are dropped)
         const uint32_t ot = o + (uint32_t)(16 * tt * Hq * KD * 2);
-        buf_store8(dqr, ot, pack4_bf16(quad_t(dq[tt])));
-        buf_store8(dkr, ot, pack4_bf16(quad_t(dk[tt])));
+        buf_store8(dqr, ot, pack4_bf16(dq[tt]));
+        buf_store8(dkr, ot, pack4_bf16(dk[tt]));
       }
     }
     // the next unit's copies have landed; every wave is done with this unit
