@@ -80,7 +80,17 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   // the unit loop (and spill them).
   int q = l >> 4, t = l & 15;
   int dcol = 16 * w + t;                       // this wave's feature column
-  const int ti = w >> 1, tj0 = 2 * (w & 1);    // this wave's 64 x 64 tiles (ti, tj0), (ti, tj0 + 1)
+  // The 64 x 64 token-by-token products (dPD, dA, M1, dL) are needed on
+  // their ten lower 16 x 16 tiles only.  Waves 0 and 1 take two tiles of one
+  // row block, (ti, tj0) and (ti, tj0 + 1), waves 2..7 one, so that the two
+  // waves of each SIMD (w and w + 4) hold 3, 3, 2 and 2 tiles:
+  //   w0 (3,0) (3,1)  w1 (2,0) (2,1)  w2 (3,2)  w3 (3,3)
+  //   w4 (2,2)        w5 (1,0)        w6 (1,1)  w7 (0,0)
+  // Waves 2..7 also keep the six upper tiles zero where a product's
+  // operand region is shared: upper tile w - 2 of M1 and of E (every unit),
+  // and of the dPD / dA area (once).
+  const int ti = (0x01123323 >> (4 * w)) & 15, tj0 = (0x01023200 >> (4 * w)) & 15, nt = w < 2 ? 2 : 1;
+  const int zu = 4 * ((w + 6) & 7), zi = (0x211000 >> zu) & 15, zj = (0x332321 >> zu) & 15;   // upper tile w - 2 (w >= 2)
 
   // staged-tile element offsets: 128-wide (16 pieces a row) and 64-wide (8)
   auto t16 = [](int r, int c) __attribute__((always_inline)) { return (r * 16 + ((c >> 3) ^ stage_swz<16>(r))) * 8 + (c & 7); };
@@ -258,11 +268,19 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
   copy_dO_Vn(cu);
   copy_dVn_V(cu);
   copy_A_gates(cu, ic<0>());
+  if (w >= 2) {
+    const int r = 16 * zi + t, c = 16 * zj + 4 * q;
+    *reinterpret_cast<uint2*>(sPD + (r * 8 + ((c >> 3) ^ stage_swz<8>(r))) * 8 + (c & 7)) = make_uint2(0u, 0u);
+  }
   // the first unit's copies have landed (later units wait at the end of the previous one)
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   f32x4 dq[4], dk[4];
+  // raw Q K^T and K K^T tiles of this wave, transposed like the products
+  // they scale; they depend on q and k only, so they are formed at the
+  // first unit of an item and kept for its other value heads
+  f32x4 Sqk[2], Skk[2];
   bf16x8 kt1[2], kt2[2];   // K fragments at column block w: rt (for dPD K, E K) and rb (for E^T K)
 
   // One unit with its A and gate buffers ab (a compile-time index: the loop
@@ -322,22 +340,32 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 
     // ---- phase 1: dPD tiles; dO h^T, dVnew h^T, Vnew dh^T (column split)
     {
-      // dO Vnew^T and raw Q K^T, transposed tiles: row 16ti + t, columns 16(tj0 + m) + 4q + e
-      f32x4 dP[2] = {zero4(), zero4()}, Sqk[2] = {zero4(), zero4()};
+      // dO Vnew^T, transposed tiles: row 16ti + t, columns 16(tj0 + m) + 4q + e
+      if (new_item) {
+        Sqk[0] = zero4();
+        Sqk[1] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 aq = ra16(sQ, ti, ks);
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            if (m < nt) Sqk[m] = mf(ra16(sK, tj0 + m, ks), aq, Sqk[m]);
+        }
+      }
+      f32x4 dP[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = ra16(sdO, ti, ks), aq = ra16(sQ, ti, ks);
+        const bf16x8 a = ra16(sdO, ti, ks);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          dP[m] = mf(ra16(sVn, tj0 + m, ks), a, dP[m]);
-          Sqk[m] = mf(ra16(sK, tj0 + m, ks), aq, Sqk[m]);
-        }
+        for (int m = 0; m < 2; ++m)
+          if (m < nt) dP[m] = mf(ra16(sVn, tj0 + m, ks), a, dP[m]);
       }
       const int r = 16 * ti + t;
       const float gr = sGam[r];
       float rx = 0.f;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
+        if (m >= nt) break;
         const f32x4 gc = fac4(sGam, tj0 + m);
         float cx[4];
         f32x4 pv;
@@ -466,24 +494,33 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
 
     // ---- phase 2: dA tiles; dKb = A^T dW and dVb = A^T dVnew (column split)
     T* sdA = sPD;
-    f32x4 Skk[2] = {zero4(), zero4()};   // raw K K^T tiles (for phase 3), transposed like dA
     {
+      if (new_item) {
+        Skk[0] = zero4();
+        Skk[1] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 ak = ra16(sK, ti, ks);
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            if (m < nt) Skk[m] = mf(ra16(sK, tj0 + m, ks), ak, Skk[m]);
+        }
+      }
       f32x4 ta[2] = {zero4(), zero4()}, tb[2] = {zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 a1 = ra16(sW, ti, ks), a2 = ra16(sdVn, ti, ks);
-        const bf16x8 ak = ra16(sK, ti, ks);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 bk = ra16(sK, tj0 + m, ks);
-          ta[m] = mf(bk, a1, ta[m]);
-          Skk[m] = mf(bk, ak, Skk[m]);
-          tb[m] = mf(ra16(sV, tj0 + m, ks), a2, tb[m]);
-        }
+        for (int m = 0; m < 2; ++m)
+          if (m < nt) {
+            ta[m] = mf(ra16(sK, tj0 + m, ks), a1, ta[m]);
+            tb[m] = mf(ra16(sV, tj0 + m, ks), a2, tb[m]);
+          }
       }
       const int r = 16 * ti + t;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
+        if (m >= nt) break;
         const f32x4 btc = fac4(sBt, tj0 + m), gmc = fac4(sGm, tj0 + m);
         f32x4 av;
 #pragma unroll
@@ -538,10 +575,16 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 a = rb8(sA, ks, ti);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) m1[m] = mf(rb8(sdA, ks, tj0 + m), a, m1[m]);
+        for (int m = 0; m < 2; ++m)
+          if (m < nt) m1[m] = mf(rb8(sdA, ks, tj0 + m), a, m1[m]);
       }
 #pragma unroll
-      for (int m = 0; m < 2; ++m) st_t8(sM1, ti, tj0 + m, m1[m]);
+      for (int m = 0; m < 2; ++m)
+        if (m < nt) st_t8(sM1, ti, tj0 + m, m1[m]);
+      if (w >= 2) {   // upper tiles of M1 and E: the dW rows were there
+        st_t8(sM1, zi, zj, zero4());
+        st_t8(sE, zi, zj, zero4());
+      }
     }
     lds_barrier();
     {
@@ -550,13 +593,15 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 a = ra8(sM1, ti, ks);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) dl[m] = mf(ra8(sA, tj0 + m, ks), a, dl[m]);
+        for (int m = 0; m < 2; ++m)
+          if (m < nt) dl[m] = mf(ra8(sA, tj0 + m, ks), a, dl[m]);
       }
       const int r = 16 * ti + t;
       const float gr = sGam[r], btr = sBt[r];
       float rx = 0.f, bs = 0.f;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
+        if (m >= nt) break;
         const f32x4 gc = fac4(sGam, tj0 + m);
         float cx[4];
         f32x4 evv;
