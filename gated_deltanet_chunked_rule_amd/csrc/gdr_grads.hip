@@ -457,14 +457,15 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
         } else {
           const float dc = sDec[16 * tt + t];
           const f32x4 ke = row4(sK, tt);
+          float rk = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float vk = dc * acc[tt][e];             // dec_t (Vnew dh^T)
             dk[tt][e] += vk;
-            const float rk = vk * ke[e];
-            rsum += rk;
-            rowL[tt] -= rk;
+            rk += vk * ke[e];
           }
+          rsum += rk;
+          rowL[tt] -= rk;
         }
       }
     }
@@ -544,18 +545,16 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       float rowK[4], dbL[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const float bt = sBt[16 * st + t], gm = sGm[16 * st + t];
+        const float gm = sGm[16 * st + t], bg = sBt[16 * st + t] * gm;
         const f32x4 ke = row4(sK, st);
-        float rk = 0.f, db = 0.f;
+        float kk = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          dk[st][e] += bt * gm * kb[st][e];
-          const float kk = kb[st][e] * ke[e];
-          rk += bt * gm * kk;
-          db += gm * kk;
+          dk[st][e] += bg * kb[st][e];
+          kk += kb[st][e] * ke[e];
         }
-        rowK[st] = rk;
-        dbL[st] = db;
+        rowK[st] = bg * kk;
+        dbL[st] = gm * kk;
       }
       sRowP[w][16 * q + t] += group_sums4(rowK);
       sDbP[w][16 * q + t] += group_sums4(dbL);
@@ -640,13 +639,12 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
         dk[tt] = mf(kt1[ks], ra8(sE, tt, ks), dk[tt]);
         dk[tt] = mf(kt2[ks], rb8(sE, ks, tt), dk[tt]);
       }
-    if (w == 0) {   // dgamma row sums, dg as its reverse cumulative sum, dbeta
-      float dgm = 0.f, db = 0.f;
+    // dgamma row sums and dg as their reverse cumulative sum on wave 3,
+    // dbeta on wave 2 (both on the SIMDs with fewer 64 x 64 tiles)
+    if (w == 3) {
+      float dgm = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < FNW; ++ww) {
-        dgm += sRowP[ww][l] + sColP[ww][l];
-        db += sDbP[ww][l];
-      }
+      for (int ww = 0; ww < FNW; ++ww) dgm += sRowP[ww][l] + sColP[ww][l];
       if (l == len - 1) {
         float r0 = 0.f, r1 = 0.f;
 #pragma unroll
@@ -657,11 +655,12 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
       const float rev = __shfl(dgm, 63 - l, 64);
       const float sc = wave_inclusive_scan(rev);
       const float dgv = __shfl(sc, 63 - l, 64);
-      if (l < len) {
-        KArgs* pa = prm();
-        pa->dg[(long)(t0 + l) * Hv + h] = dgv;
-        pa->dbeta[(long)(t0 + l) * Hv + h] = db;
-      }
+      if (l < len) prm()->dg[(long)(t0 + l) * Hv + h] = dgv;
+    } else if (w == 2) {
+      float db = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < FNW; ++ww) db += sDbP[ww][l];
+      if (l < len) prm()->dbeta[(long)(t0 + l) * Hv + h] = db;
     }
     if (cu.gi == G - 1) {   // the group's dq and dk rows
       KArgs* pa = prm();
