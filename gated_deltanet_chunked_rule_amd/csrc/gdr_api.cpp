@@ -53,7 +53,7 @@ struct Problem {
 
 struct Layout {
   size_t cu = 0, chunk_off = 0, seg_off = 0, gcum = 0, cert = 0, W = 0, U = 0, vnew = 0, hbuf = 0;
-  size_t A = 0, dhbuf = 0, dvn = 0, segtr = 0, hstart = 0, Au = 0, seg_order = 0, total = 0;
+  size_t A = 0, dhbuf = 0, dvn = 0, segtr = 0, hstart = 0, Au = 0, seg_order = 0, hflag = 0, total = 0;
 };
 
 // bf16 stages A diag(beta) per chunk and V, and forms Vnew (and, in the
@@ -205,6 +205,7 @@ Layout layout(const Problem& P, bool bwd) {
   Lo.seg_order = take(kMaxOrderedSegs * 4);
   Lo.gcum = take(hv * tt * 4);
   Lo.cert = take(hv * nt * 4);
+  Lo.hflag = take(nn * hv * 4);
   if (apath(P)) {
     Lo.Au = take(hv * tt * kChunk * 2);
   } else {
@@ -315,10 +316,14 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
     fp.split_vnew = (!bwd && P.precise_vnew) ? 1 : 0;
     fp.hbuf = bwd ? ws + Lo.hbuf : nullptr;
     fp.vnew = bwd ? ws + Lo.vnew : nullptr;
+    fp.hflag = nullptr;
     if (exact_cp(P, L)) {
-      // transitions (M, b) of the uncertified heads' segments, then their exact start states
+      // transitions (M, b) of the uncertified heads' segments, then their
+      // exact start states; the transition pass records each head's
+      // certificate decision for the scan and the output pass
       gdr::FusedParams tp = fp;
       tp.trans = 1;
+      tp.hflag = reinterpret_cast<int*>(ws + Lo.hflag);
       tp.segtr = reinterpret_cast<float*>(ws + Lo.segtr);
       if ((e = gdr::launch_fused(P.dt, P.K, tp, segs, st)) != hipSuccess) return hip_fail(e, "transition launch");
       gdr::ScanParams sc;
@@ -326,8 +331,10 @@ gdr_status run_forward_chain(const Problem& P, const Layout& Lo, char* ws, const
       sc.hstart = reinterpret_cast<float*>(ws + Lo.hstart);
       sc.Hv = P.Hv; sc.seg_chunks = L; sc.warmup = P.W; sc.total_segs = segs; sc.log_eps = P.log_eps;
       sc.rev = 0; sc.rev_cert = fp.rev_cert;
+      sc.hflag = tp.hflag;
       if ((e = gdr::launch_segscan(P.K, sc, P.N * P.Hv, st)) != hipSuccess) return hip_fail(e, "scan launch");
       fp.hstart = sc.hstart;
+      fp.hflag = tp.hflag;
     }
     if ((e = gdr::launch_fused(P.dt, P.K, fp, segs, st)) != hipSuccess) return hip_fail(e, "fused launch");
   } else {
@@ -519,8 +526,11 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
     dp.dht = dht; dp.dh0 = dh0; dp.dhbuf = ws + Lo.dhbuf; dp.dvn = ws + Lo.dvn;
     dp.Hq = P.Hq; dp.Hv = P.Hv; dp.seg_chunks = L; dp.warmup = P.W; dp.total_segs = P.total_segs;
     dp.log_eps = P.log_eps; dp.scale = scale;
-    dp.trans = 0; dp.segtr = nullptr; dp.dhstart = nullptr;
+    dp.trans = 0; dp.segtr = nullptr; dp.dhstart = nullptr; dp.hflag = nullptr;
     if (exact_cp(P, L)) {
+      // the certificate decisions (reverse windows included) that the
+      // forward-direction transition pass of this call recorded
+      dp.hflag = reinterpret_cast<const int*>(ws + Lo.hflag);
       // reverse offsets d_s (into segtr part 1, whose b_s are spent), then
       // the exact end gradients (into hstart, whose start states are spent)
       gdr::DFusedParams tp = dp;
@@ -533,6 +543,7 @@ gdr_status gdr_chunk_bwd(const gdr_shape* shape, const gdr_options* opts, const 
       sc.hstart = reinterpret_cast<float*>(ws + Lo.hstart);
       sc.Hv = P.Hv; sc.seg_chunks = L; sc.warmup = P.W; sc.total_segs = P.total_segs;
       sc.log_eps = P.log_eps; sc.rev = 1; sc.rev_cert = 1;
+      sc.hflag = dp.hflag;
       if ((e = gdr::launch_segscan(P.K, sc, P.N * P.Hv, hs)) != hipSuccess) return hip_fail(e, "reverse scan launch");
       dp.dhstart = sc.hstart;
     }

@@ -270,7 +270,8 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
   const float* hcert = p.cert + (long)h * s.NTtot + c0;
   const int send = min(pseg * L + L, nch);   // the segment's end chunk
   const float wpre = TRANS ? 0.f : warmup_first(hcert, send, 1, nch - send, p.warmup);
-  const bool certified = head_certified(hcert, nseg, nch, L, p.warmup, p.log_eps, true);
+  const bool certified = p.hflag ? p.hflag[(long)n * p.Hv + h] != 0
+                                 : head_certified(hcert, nseg, nch, L, p.warmup, p.log_eps, true);
   const int gseg = s.seg_at(n) + pseg;
   const long hbase = ((long)n * p.Hv + h) * KD * VD;
   // chunks crs down to cbeg; those below cend are the segment's own

@@ -1063,7 +1063,15 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 
   const float* hcert = p.cert + (long)h * s.NTtot + c0;
   const float wpre = TRANS ? 0.f : warmup_first(hcert, pseg * L - 1, -1, pseg * L, p.warmup);
-  const bool certified = head_certified(hcert, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0);
+  // The head's certificate: the transition pass evaluates it and records
+  // the decision for the later passes of the same call, which read it.
+  bool certified;
+  if (!TRANS && p.hflag) {
+    certified = p.hflag[(long)n * p.Hv + h] != 0;
+  } else {
+    certified = head_certified(hcert, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0);
+    if (TRANS && p.hflag && pseg == 0 && part == 0 && threadIdx.x == 0) p.hflag[(long)n * p.Hv + h] = certified ? 1 : 0;
+  }
   const int gseg = s.seg_at(n) + pseg;          // global segment index
   const bool exact = !certified && p.hstart != nullptr;
   int cstart, cbeg, cend;
@@ -1655,7 +1663,8 @@ __global__ __launch_bounds__(KD * 4) void k_segscan(ScanParams p, int total_item
   const int L = p.seg_chunks;
   if (nseg <= 1 || c0 < 0) return;
   const int nch = s.chunk_at(n + 1) - c0;
-  if (head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0))
+  if (p.hflag ? p.hflag[(long)n * p.Hv + h] != 0
+              : head_certified(p.cert + (long)h * s.NTtot + c0, nseg, nch, L, p.warmup, p.log_eps, p.rev_cert != 0))
     return;   // certified: the warmup path needs no start states
   const int w = wave_id(), l = lane_id(), q = l >> 4, t = l & 15;
   const int col = 16 * cb + t, row0 = 16 * w + 4 * q;

@@ -114,6 +114,8 @@ struct FusedParams {         // forward state recurrence fused with the output
   int split_vnew;            // 1: bf16 output pass with Vnew as two bf16 terms (MODE 4)
   void* hbuf;                // non-null (backward recompute): store each chunk's entry state
   void* vnew;                //   and Vnew instead of the output
+  int* hflag;                // nullable [N][Hv]: each head's certificate decision; the
+                             //   transition pass writes it, the later passes of the call read it
 };
 
 struct DFusedParams {        // reverse state pass with CP segments (backward)
@@ -130,6 +132,8 @@ struct DFusedParams {        // reverse state pass with CP segments (backward)
   int trans;                 // 1: reverse segment offsets d_s into segtr part 1
   float* segtr;
   const float* dhstart;      // nullable: exact state gradients at the segment ends [Hv][total_segs][K][V]
+  const int* hflag;          // nullable [N][Hv]: certificate decisions (reverse windows included)
+                             //   of the forward-direction transition pass of the same call
 };
 
 struct ScanParams {          // exact segment start states from the segment transitions
@@ -140,6 +144,7 @@ struct ScanParams {          // exact segment start states from the segment tran
   float log_eps;
   int rev;                   // 1: reverse scan g_{s-1} = M_s^T g_s + d_s (state gradients)
   int rev_cert;
+  const int* hflag;          // nullable [N][Hv]: certificate decisions of the transition pass
 };
 
 struct DStateParams {        // reverse state pass
