@@ -329,9 +329,9 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
     const int len = min(CH, seq1 - t0);
     const long rbytes = (long)len * KD * (long)sizeof(T);
     if (piece == 0)
-      lds_copy_tile<1, 8, FNW, 8>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, apack_bytes(len)), off_a, w);
+      lds_copy_tile<1, 8, FNW, 8, true>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, apack_bytes(len)), off_a, w);
     if (piece == 1)
-      lds_copy_tile<NCP, NCH, FNW, VEC>(bf.O, rsrc_words((const T*)p.d_o + ((long)t0 * p.Hv + h) * VD, rbytes * p.Hv), off_o, w);
+      lds_copy_tile<NCP, NCH, FNW, VEC, true>(bf.O, rsrc_words((const T*)p.d_o + ((long)t0 * p.Hv + h) * VD, rbytes * p.Hv), off_o, w);
     if (piece == 2)
       lds_copy_tile<NCP, NCH, FNW, VEC>(bf.K, rsrc_words((const T*)p.k + ((long)t0 * p.Hq + hk) * KD, rbytes * p.Hq), off_qk, w);
     if (piece == 3) {

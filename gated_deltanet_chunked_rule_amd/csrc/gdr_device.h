@@ -98,10 +98,12 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
   __builtin_memcpy(&u, &v, 16);
   return u;
 }
+// NT: the non-temporal hint, for data that no later kernel of the call reads
+template <bool NT = false>
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 u) {
   decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)) v;
   __builtin_memcpy(&v, &u, 16);
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, NT ? 2 : 0);
 }
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
@@ -533,8 +535,14 @@ __device__ __forceinline__ i32x4v rsrc_words(const void* base, long bytes) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
 }
+// NT: the non-temporal hint, for tiles read once (no other workgroup of the
+// launch reads them), so that they do not displace tiles that others reuse
+template <bool NT = false>
 __device__ __forceinline__ void lds_copy16(i32x4v rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
 }
 __device__ __forceinline__ void lds_copy4(i32x4v rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds) : "memory");
@@ -543,12 +551,12 @@ __device__ __forceinline__ void lds_copy4(i32x4v rsrc, uint32_t voff, uint32_t l
 // One wave's share of copying a staged tile from global memory into LDS:
 // instruction j fills the 1 KB block w + 8j of the tile; off[j] is this
 // lane's byte offset in the source (rows past the descriptor range read 0).
-template <int NCP, int NCH, int FNWV, int VEC, typename T>
+template <int NCP, int NCH, int FNWV, int VEC, bool NT = false, typename T>
 __device__ __forceinline__ void lds_copy_tile(T* dst, i32x4v rv, const uint32_t* off, int w) {
 #pragma unroll
   for (int j = 0; j < NCP; ++j) {
     const int i = w + FNWV * j;
-    if (NCH % FNWV == 0 || i < NCH) lds_copy16(rv, off[j], lds_addr(dst + 64 * i * VEC));
+    if (NCH % FNWV == 0 || i < NCH) lds_copy16<NT>(rv, off[j], lds_addr(dst + 64 * i * VEC));
   }
 }
 

@@ -1164,9 +1164,9 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     const long wbytes = (long)len * KD * (long)sizeof(T), qbytes = wbytes * p.Hq;
     if constexpr (AP) {
       if (piece == 0)
-        lds_copy_tile<1, 8, FNW, 8>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, apack_bytes(len)), off_a, w);
+        lds_copy_tile<1, 8, FNW, 8, true>(bf.W, rsrc_words((const T*)p.Au + ((long)h * s.Ttot + t0) * CH, apack_bytes(len)), off_a, w);
       if (piece == 1 && !no_u)
-        lds_copy_tile<NCP, NCH, FNW, VEC>(bf.U, rsrc_words((const T*)p.v + ((long)t0 * p.Hv + h) * VD, wbytes * p.Hv), off_v, w);
+        lds_copy_tile<NCP, NCH, FNW, VEC, true>(bf.U, rsrc_words((const T*)p.v + ((long)t0 * p.Hv + h) * VD, wbytes * p.Hv), off_v, w);
     } else {
       if (piece == 0)
         lds_copy_tile<NCP, NCH, FNW, VEC>(bf.W, rsrc_words((const T*)p.W + ((long)h * s.Ttot + t0) * KD, wbytes), off_wu, w);
@@ -1214,8 +1214,8 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 #pragma unroll
       for (int i = threadIdx.x; i < CH * NCH; i += FNT) {
         const int r = i / NCH, c = i % NCH;
-        buf_store16(rr, (uint32_t)r * rs + (uint32_t)c * 16u,
-                    *reinterpret_cast<const uint4*>(sO + (r * NCH + (c ^ stage_swz<NCH>(r))) * VEC));
+        buf_store16<true>(rr, (uint32_t)r * rs + (uint32_t)c * 16u,
+                          *reinterpret_cast<const uint4*>(sO + (r * NCH + (c ^ stage_swz<NCH>(r))) * VEC));
       }
     }
   };

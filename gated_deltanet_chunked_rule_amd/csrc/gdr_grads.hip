@@ -212,30 +212,31 @@ __global__ __launch_bounds__(FNT) void k_gradsf(GradParams p, int total_items, i
     }
   };
   int wsc = w;   // the wave id in a scalar register, made opaque at every unit (see body)
-  auto tile = [&](T* dst, const void* base, long elem0, long row_elems, int len, const uint32_t* off)
+  // (nt: tiles that only this unit reads; q and k serve the group's value heads)
+  auto tile = [&](T* dst, const void* base, long elem0, long row_elems, int len, const uint32_t* off, auto ntc)
       __attribute__((always_inline)) {
-    lds_copy_tile<2, 16, FNW, 8>(dst, rsrc_words((const T*)base + elem0, (long)len * row_elems * 2), off, wsc);
+    lds_copy_tile<2, 16, FNW, 8, decltype(ntc)::value != 0>(dst, rsrc_words((const T*)base + elem0, (long)len * row_elems * 2), off, wsc);
   };
   auto copy_dO_Vn = [&](const Unit& u) __attribute__((always_inline)) {
     KArgs* pa = prm();
-    tile(sdO, pa->d_o, ((long)u.t0 * Hv + u.h) * VD, (long)Hv * VD, u.len, off_hv);
-    tile(sVn, pa->vnew, ((long)u.h * Ttot + u.t0) * VD, VD, u.len, off_ws);
+    tile(sdO, pa->d_o, ((long)u.t0 * Hv + u.h) * VD, (long)Hv * VD, u.len, off_hv, ic<1>());
+    tile(sVn, pa->vnew, ((long)u.h * Ttot + u.t0) * VD, VD, u.len, off_ws, ic<1>());
   };
   auto copy_Q = [&](const Unit& u) __attribute__((always_inline)) {
-    tile(sQ, prm()->q, ((long)u.t0 * Hq + u.hk) * KD, (long)Hq * KD, u.len, off_qk);
+    tile(sQ, prm()->q, ((long)u.t0 * Hq + u.hk) * KD, (long)Hq * KD, u.len, off_qk, ic<0>());
   };
   auto copy_K = [&](const Unit& u) __attribute__((always_inline)) {
-    tile(sK, prm()->k, ((long)u.t0 * Hq + u.hk) * KD, (long)Hq * KD, u.len, off_qk);
+    tile(sK, prm()->k, ((long)u.t0 * Hq + u.hk) * KD, (long)Hq * KD, u.len, off_qk, ic<0>());
   };
   auto copy_dVn_V = [&](const Unit& u) __attribute__((always_inline)) {
     KArgs* pa = prm();
-    tile(sdVn, pa->dvn, ((long)u.h * Ttot + u.t0) * VD, VD, u.len, off_ws);
-    tile(sV, pa->v, ((long)u.t0 * Hv + u.h) * VD, (long)Hv * VD, u.len, off_hv);
+    tile(sdVn, pa->dvn, ((long)u.h * Ttot + u.t0) * VD, VD, u.len, off_ws, ic<1>());
+    tile(sV, pa->v, ((long)u.t0 * Hv + u.h) * VD, (long)Hv * VD, u.len, off_hv, ic<1>());
   };
   auto copy_A_gates = [&](const Unit& u, auto abc) __attribute__((always_inline)) {   // into buffer ab
     constexpr int ab = decltype(abc)::value;
     KArgs* pa = prm();
-    lds_copy_tile<1, 8, FNW, 8>(&sA2[ab][0],
+    lds_copy_tile<1, 8, FNW, 8, true>(&sA2[ab][0],
                                 rsrc_words((const T*)pa->A_bf + ((long)u.h * Ttot + u.t0) * CH, (long)u.len * CH * 2),
                                 off_a, wsc);
     if (w == 0) {
