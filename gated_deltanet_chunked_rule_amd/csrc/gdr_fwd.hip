@@ -1528,19 +1528,21 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     if (prev_out) store_o(prev_t0, prev_len);
     lds_barrier();  // P complete; the previous chunk's output rows are out of LDS
     if (!F32 && keep) {   // the staged entry state and Vnew rows, 16-byte pieces
+      // (non-temporal: the gradient kernel reads them only after the reverse pass)
+      typedef unsigned u32x4nt __attribute__((ext_vector_type(4)));
       T* hb = (T*)p.hbuf + ((long)h * s.NTtot + c0 + jc) * KD * VD;
 #pragma unroll
       for (int i = threadIdx.x; i < KD * NCH; i += FNT) {
         const int r = i / NCH, c = i % NCH;
         const T* src = (r < CH ? sQ0 : sQ1) + ((r & (CH - 1)) * NCH + (c ^ stage_swz<NCH>(r))) * VEC;
-        *reinterpret_cast<uint4*>(hb + (long)r * VD + c * VEC) = *reinterpret_cast<const uint4*>(src);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4nt*>(src), reinterpret_cast<u32x4nt*>(hb + (long)r * VD + c * VEC));
       }
       const rsrc_t vr = make_rsrc((T*)p.vnew + ((long)h * s.Ttot + t0) * VD, (long)len * VD * (long)sizeof(T));
 #pragma unroll
       for (int i = threadIdx.x; i < CH * NCH; i += FNT) {
         const int r = i / NCH, c = i % NCH;
-        buf_store16(vr, (uint32_t)(r * VD + c * VEC) * (uint32_t)sizeof(T),
-                    *reinterpret_cast<const uint4*>(sO + (r * NCH + (c ^ stage_swz<NCH>(r))) * VEC));
+        buf_store16<true>(vr, (uint32_t)(r * VD + c * VEC) * (uint32_t)sizeof(T),
+                          *reinterpret_cast<const uint4*>(sO + (r * NCH + (c ^ stage_swz<NCH>(r))) * VEC));
       }
     }
 
