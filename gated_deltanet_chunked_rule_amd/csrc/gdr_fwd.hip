@@ -1287,16 +1287,27 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     }
 
     if (!warm && pcnt > 0) {  // P tiles of this wave
-      // Masked scaled decays first (they do not depend on the products); the
-      // gate cumsums of the lane's four rows are one 16-byte read.
+      // Masked scaled decays first (they do not depend on the products).
+      // bf16: the products are formed with swapped operands, so a lane holds
+      // row 16i + t over the four columns 16j + 4q + e (one 8-byte store, no
+      // in-quad transpose); fp32: rows 16i + 4q + e of column 16j + t.  Either
+      // way the gate cumsums of the lane's four entries are one 16-byte read.
       f32x4 dec[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(sG + r0);
-        const float gc = sG[c];
+        if constexpr (F32) {
+          const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
+          const f32x4 gr = *reinterpret_cast<const f32x4*>(sG + r0);
+          const float gc = sG[c];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dec[m][e] = (r0 + e >= c && r0 + e < len) ? p.scale * __expf(gr[e] - gc) : 0.f;
+          for (int e = 0; e < 4; ++e) dec[m][e] = (r0 + e >= c && r0 + e < len) ? p.scale * __expf(gr[e] - gc) : 0.f;
+        } else {
+          const int r = 16 * pti[m] + t, c0 = 16 * ptj[m] + 4 * q;
+          const float gr = sG[r];
+          const f32x4 gc = *reinterpret_cast<const f32x4*>(sG + c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dec[m][e] = (r >= c0 + e && r < len) ? p.scale * __expf(gr - gc[e]) : 0.f;
+        }
       }
       f32x4 pa[2] = {zero4(), zero4()};
       if constexpr (F32) {
@@ -1316,31 +1327,30 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
             fb[m] = *reinterpret_cast<const bf16x8*>(sK + tix(16 * ptj[m] + t, k0 + 8 * q));
           }
 #pragma unroll
-          for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[m], fb[m], pa[m], 0, 0, 0);
+          for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[m], fa[m], pa[m], 0, 0, 0);
         }
       } else {   // one tile
 #pragma unroll
         for (int k0 = 0; k0 < KD; k0 += 32) {
           const bf16x8 fa = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * pti[0] + t, k0 + 8 * q));
           const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sK + tix(16 * ptj[0] + t, k0 + 8 * q));
-          pa[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, pa[0], 0, 0, 0);
+          pa[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, pa[0], 0, 0, 0);
         }
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (m < pcnt) {
-          const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
           const f32x4 pv = dec[m] * pa[m];
           if constexpr (F32) {
+            const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
 #pragma unroll
             for (int e = 0; e < 4; ++e) sP[(r0 + e) * PP + c] = pv[e];
           } else {
-            // Quad transpose: a lane gets one row over four consecutive
-            // columns, which the column permutation keeps adjacent (one
-            // 8-byte store).
-            const int rr = r0 + (t & 3), cc = 16 * ptj[m] + 4 * (t >> 2);
+            // row 16i + t, columns 16j + 4q .. +3, which the column
+            // permutation keeps adjacent (one 8-byte store)
+            const int rr = 16 * pti[m] + t, cc = 16 * ptj[m] + 4 * q;
             const int pc = (cc & ~31) + 8 * ((cc >> 2) & 3) + 4 * ((cc >> 4) & 1);
-            *reinterpret_cast<uint2*>(sP + tix8(rr, pc)) = pack4_bf16(quad_t(pv));
+            *reinterpret_cast<uint2*>(sP + tix8(rr, pc)) = pack4_bf16(pv);
           }
         }
       }
