@@ -439,13 +439,16 @@ __global__ __launch_bounds__(FNT) void k_dfused(DFusedParams p, int total_items)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (m < cnt) {
+          // a lane's four rows r0 + e land in four consecutive columns of
+          // the stored row c (the permutation keeps r & 3): one 8-byte store
+          const int r0 = 16 * ti[m] + 4 * q, c = 16 * tj[m] + t;
+          const f32x4 gr = *reinterpret_cast<const f32x4*>(sG + r0);
+          const float gc = sG[c];
+          f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * ti[m] + acc_row(e), c = 16 * tj[m] + acc_col();
-            const float v = (r >= c && r < len) ? p.scale * __expf(sG[r] - sG[c]) * pa[m][e] : 0.f;
-            const int pr = (r & ~31) + 8 * ((r >> 2) & 3) + 4 * ((r >> 4) & 1) + (r & 3);
-            sP[tix8(c, pr)] = from_f<T>(v);
-          }
+          for (int e = 0; e < 4; ++e) v[e] = (r0 + e >= c && r0 + e < len) ? p.scale * __expf(gr[e] - gc) * pa[m][e] : 0.f;
+          const int pr = (r0 & ~31) + 8 * ((r0 >> 2) & 3) + 4 * ((r0 >> 4) & 1);
+          *reinterpret_cast<uint2*>(sP + tix8(c, pr)) = pack4_bf16(v);
         }
       }
     }
