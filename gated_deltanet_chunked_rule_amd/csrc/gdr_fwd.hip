@@ -1398,6 +1398,10 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
             for (int cb = 0; cb < CBW; ++cb) vn[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[tt], hb[cb], vn[tt][cb], 0, 0, 0);
         }
         if (!warm) {   // Q h after K h: its products fill the K h -> Vnew latency
+          // The output products take swapped operands (the A and B fragments
+          // have the same register layout), so that oa holds transposed
+          // blocks: lane (q, t) has token row 16tt + t over the four value
+          // columns 16w + 4q + e, staged as one 8-byte write per tile.
 #pragma unroll
           for (int ks = 0; ks < KD / 32; ++ks) {
             bf16x8 aq[4];
@@ -1405,7 +1409,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) aq[tt] = *reinterpret_cast<const bf16x8*>(sQ + tix(16 * tt + t, 32 * ks + 8 * q));
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) oa[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[tt], hb, oa[tt][0], 0, 0, 0);
+            for (int tt = 0; tt < 4; ++tt) oa[tt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hb, aq[tt], oa[tt][0], 0, 0, 0);
           }
         }
       }
@@ -1457,12 +1461,13 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
       f32x4 vd[4][CBW];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < 4; ++tt) {
+        const float gmt = sM[16 * tt + t];   // bf16: oa's row is 16tt + t
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * tt + acc_row(e);
           const float d = sD[r];
-          const float gm = sM[r];
+          const float gm = F32 ? sM[r] : gmt;
 #pragma unroll
           for (int cb = 0; cb < CBW; ++cb) {
             if constexpr (!AP) vn[tt][cb][e] = uv[tt][e][cb] - vn[tt][cb][e];
@@ -1470,6 +1475,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
             oa[tt][cb][e] *= gm;
           }
         }
+      }
       if (keep) {   // Vnew token rows
         T* vb = (T*)p.vnew + ((long)h * s.Ttot + t0) * VD;
         if constexpr (F32) {
@@ -1594,29 +1600,19 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 #pragma unroll
           for (int tt = 2 * ks; tt < 4; ++tt)
 #pragma unroll
-            for (int cb = 0; cb < CBW; ++cb) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[ks][tt], vb[cb], oa[tt][cb], 0, 0, 0);
+            for (int cb = 0; cb < CBW; ++cb) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[cb], ap[ks][tt], oa[tt][cb], 0, 0, 0);
           if constexpr (SPLITV) {
 #pragma unroll
             for (int cb = 0; cb < CBW; ++cb) {
               const bf16x8 vl = pack_b_lo(vn[2 * ks][cb], vn[2 * ks + 1][cb], vb[cb]);
 #pragma unroll
-              for (int tt = 2 * ks; tt < 4; ++tt) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[ks][tt], vl, oa[tt][cb], 0, 0, 0);
+              for (int tt = 2 * ks; tt < 4; ++tt) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, ap[ks][tt], oa[tt][cb], 0, 0, 0);
             }
           }
         }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * tt + acc_row(e);
-            if constexpr (CBW == 2) {
-              bf16 lo = from_f<T>(oa[tt][0][e]), hi = from_f<T>(oa[tt][1][e]);
-              *reinterpret_cast<uint32_t*>(sO + tix(r, 32 * w + 2 * t)) =
-                  (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-            } else {
-              sO[tix(r, vcol(0))] = from_f<T>(oa[tt][0][e]);
-            }
-          }
+        for (int tt = 0; tt < 4; ++tt)   // row 16tt + t, columns 16w + 4q .. +3
+          *reinterpret_cast<uint2*>(sO + tix(16 * tt + t, 16 * w + 4 * q)) = pack4_bf16(oa[tt][0]);
       }
     }
     wait_copies(jc + 1, ic<1 - b>());   // the next chunk's tiles have landed; the output rows are staged
