@@ -1542,7 +1542,12 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
       }
     }
     if (prev_out) store_o(prev_t0, prev_len);
-    lds_barrier();  // P complete; the previous chunk's output rows are out of LDS
+    // P complete; the previous chunk's output rows are out of LDS; the staged
+    // entry state is in.  A warm step that stores no state writes none of
+    // these (its copies go to the other buffer, which the end-of-step barrier
+    // publishes), so it skips this barrier: the output pass's warmup and
+    // every transition step.
+    if (!warm || keep) lds_barrier();
     if (!F32 && keep) {   // the staged entry state and Vnew rows, 16-byte pieces
       // (non-temporal: the gradient kernel reads them only after the reverse pass)
       typedef unsigned u32x4nt __attribute__((ext_vector_type(4)));
