@@ -1288,35 +1288,36 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 
     if (!warm && pcnt > 0) {  // P tiles of this wave
       // Masked scaled decays first (they do not depend on the products).
-      // bf16: the products are formed with swapped operands, so a lane holds
-      // row 16i + t over the four columns 16j + 4q + e (one 8-byte store, no
-      // in-quad transpose); fp32: rows 16i + 4q + e of column 16j + t.  Either
-      // way the gate cumsums of the lane's four entries are one 16-byte read.
+      // The products are formed with swapped operands, so a lane holds row
+      // 16i + t over the four columns 16j + 4q + e (one store, no in-quad
+      // transpose), whose gate cumsums are one 16-byte read.
       f32x4 dec[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        if constexpr (F32) {
-          const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
-          const f32x4 gr = *reinterpret_cast<const f32x4*>(sG + r0);
-          const float gc = sG[c];
+        const int r = 16 * pti[m] + t, c0 = 16 * ptj[m] + 4 * q;
+        const float gr = sG[r];
+        const f32x4 gc = *reinterpret_cast<const f32x4*>(sG + c0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dec[m][e] = (r0 + e >= c && r0 + e < len) ? p.scale * __expf(gr[e] - gc) : 0.f;
-        } else {
-          const int r = 16 * pti[m] + t, c0 = 16 * ptj[m] + 4 * q;
-          const float gr = sG[r];
-          const f32x4 gc = *reinterpret_cast<const f32x4*>(sG + c0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dec[m][e] = (r >= c0 + e && r < len) ? p.scale * __expf(gr - gc[e]) : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) dec[m][e] = (r >= c0 + e && r < len) ? p.scale * __expf(gr - gc[e]) : 0.f;
       }
       f32x4 pa[2] = {zero4(), zero4()};
       if constexpr (F32) {
+        // Lane quarter q takes the four consecutive K columns 16s + 4q.. of
+        // each 16-column slice as one 16-byte read of Q and of K; step e of
+        // the slice contracts over column 16s + 4q + e.
 #pragma unroll
-        for (int k0 = 0; k0 < KD; k0 += 4)
+        for (int k0 = 0; k0 < KD; k0 += 16) {
+          f32x4 fa[2], fb[2];
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
-            pa[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[tix(16 * pti[m] + t, k0 + q)], sK[tix(16 * ptj[m] + t, k0 + q)],
-                                                         pa[m], 0, 0, 0);
+          for (int m = 0; m < 2; ++m) {
+            fa[m] = *reinterpret_cast<const f32x4*>(sQ + tix(16 * pti[m] + t, k0 + 4 * q));
+            fb[m] = *reinterpret_cast<const f32x4*>(sK + tix(16 * ptj[m] + t, k0 + 4 * q));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) pa[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[m][e], fa[m][e], pa[m], 0, 0, 0);
+        }
       } else if (pcnt > 1) {
 #pragma unroll
         for (int k0 = 0; k0 < KD; k0 += 32) {
@@ -1342,9 +1343,7 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
         if (m < pcnt) {
           const f32x4 pv = dec[m] * pa[m];
           if constexpr (F32) {
-            const int r0 = 16 * pti[m] + 4 * q, c = 16 * ptj[m] + t;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sP[(r0 + e) * PP + c] = pv[e];
+            *reinterpret_cast<f32x4*>(sP + (16 * pti[m] + t) * PP + 16 * ptj[m] + 4 * q) = pv;
           } else {
             // row 16i + t, columns 16j + 4q .. +3, which the column
             // permutation keeps adjacent (one 8-byte store)
@@ -1368,22 +1367,31 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
     if (owner) {
       // Vnew = U - W h and Q h.
       if constexpr (F32) {
+        // step st of row block rb contracts over K row 16rb + 4q + st, which
+        // is where the state accumulator keeps it; the W and Q entries of
+        // the four steps are one 16-byte read per token tile
 #pragma unroll
-        for (int rb = 0; rb < NKB; ++rb)
+        for (int rb = 0; rb < NKB; ++rb) {
+          f32x4 aw[4], aq[4];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            aw[tt] = *reinterpret_cast<const f32x4*>(sW + tix(16 * tt + t, 16 * rb + 4 * q));
+            if (!warm) aq[tt] = *reinterpret_cast<const f32x4*>(sQ + tix(16 * tt + t, 16 * rb + 4 * q));
+          }
 #pragma unroll
           for (int st = 0; st < 4; ++st)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-              const int col = 16 * rb + 4 * q + st;
-              const float aw = sW[tix(16 * tt + t, col)];
 #pragma unroll
-              for (int cb = 0; cb < CBW; ++cb) vn[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw, hs[rb][cb][st], vn[tt][cb], 0, 0, 0);
+              for (int cb = 0; cb < CBW; ++cb)
+                vn[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[tt][st], hs[rb][cb][st], vn[tt][cb], 0, 0, 0);
               if (!warm) {
-                const float aq = sQ[tix(16 * tt + t, col)];
 #pragma unroll
-                for (int cb = 0; cb < CBW; ++cb) oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, hs[rb][cb][st], oa[tt][cb], 0, 0, 0);
+                for (int cb = 0; cb < CBW; ++cb)
+                  oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[tt][st], hs[rb][cb][st], oa[tt][cb], 0, 0, 0);
               }
             }
+        }
       } else {
 #pragma unroll
         for (int ks = 0; ks < KD / 32; ++ks) {
@@ -1569,17 +1577,21 @@ __global__ __launch_bounds__(FNT) void k_fused(FusedParams p, int total_items) {
 
     if (!warm && owner) {  // O += P Vnew
       if constexpr (F32) {
+        // step st of token tile tp contracts over token 16tp + 4q + st, as
+        // Vnew's accumulator holds it; P's four entries are one 16-byte read
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tp = 0; tp < 4; ++tp) {
+          f32x4 ap[4];
 #pragma unroll
-          for (int tp = 0; tp <= tt; ++tp)
+          for (int tt = tp; tt < 4; ++tt) ap[tt] = *reinterpret_cast<const f32x4*>(sP + (16 * tt + t) * PP + 16 * tp + 4 * q);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-              const float ap = sP[(16 * tt + t) * PP + 16 * tp + 4 * q + st];
+          for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int tt = tp; tt < 4; ++tt)
 #pragma unroll
               for (int cb = 0; cb < CBW; ++cb)
-                oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ap, vn[tp][cb][st], oa[tt][cb], 0, 0, 0);
-            }
+                oa[tt][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ap[tt][st], vn[tp][cb][st], oa[tt][cb], 0, 0, 0);
+        }
         // fp32 output straight from the accumulators (16 lanes cover 64 contiguous bytes)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
